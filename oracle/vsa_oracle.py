@@ -1,0 +1,377 @@
+"""Plain fp64 CPU oracle of the two-branch video sparse attention forward.
+
+TEST INFRASTRUCTURE.  Only tests/, ``__graft_entry__.smoke()`` and the
+cpu_baseline leg of ``bench.py`` may import this module.  It shares no code
+with the HIP path (no kernel, header, table or helper); the two read the same
+seeded arrays from ``workloads.synth`` and nothing else.
+
+Every step is written straight from its definition, in float64, with numpy
+matmul as the only library primitive.  No blocking, fusion or reordering
+beyond what a step's definition states.
+
+Pages cited (title; site):
+  [R2V-fr]  "Ref2VA VSA : noeud d'attention sparse pour le Ref2VA H3"
+            (comfyui-wiki.com, French news item)
+  [R2V-en]  "ComfyUI-Ref2VA-VSA: Ultra-Fast Character Video Generation
+            (72s on RTX 4090)" (upstar.dev README)
+  [FH3]     "BSAI FastH3 Native VSA (recipe)" (comfy.icu node page)
+  [BSA-es]  "ComfyUI Agrega Nodo Central de Atencion Dispersa y Compilador
+            Comfy" (comfyui-wiki.com, Spanish news item)
+  [SPK-es]  "Spark-H3: atencion dispersa por bloques acelera MiniMax-H3 en
+            ComfyUI" (comfyui-wiki.com, Spanish news item)
+
+Method, in the pages' order:
+  1. geometry mapper: video span -> 4x4x4 tiles of 64 tokens; text,
+     reference-image and reference-audio segments -> segment-pure tiles
+     ([R2V-fr] "Le correctif d'attention a deux niveaux" item 1; [R2V-en]
+     "Technical Architecture" and "The Solution"; [FH3] "The mechanism").
+  2. coarse branch: mean-pooled Q/K/V per tile, scores of query tiles
+     against video key tiles, softmax, attend ([BSA-es] "tres backends",
+     VSA item; [SPK-es] "Que cambia Spark-Attn").
+  3. optional log-mass bias on the pooled logits, anchored at the mean video
+     query ([SPK-es] "Que cambia Spark-Attn", Spark-Reweight item, and the
+     figure caption on exp(E[x]) vs E[exp(x)]).
+  4. selection: top-k video key tiles per query tile at a keep fraction
+     ([FH3] "The mechanism"; [BSA-es] top-k item), or a per-head threshold
+     mean + tau * std ([BSA-es] Sol-Attn item); prefix tiles never pruned
+     ([R2V-fr] items 1-2; [R2V-en] "The Solution").
+  5. fine branch: exact attention over the listed tiles ([BSA-es] first
+     paragraph; [SPK-es] "Que cambia Spark-Attn"); conditioning query rows
+     run dense under exact_kv_and_rows ([FH3] "The inputs that matter",
+     sink_conditioning).
+  6. gated combine O = O_fine + G * O_coarse with G the to_gate_compress
+     output ([R2V-fr] item 3; [R2V-en] "Technical Architecture"; [BSA-es]
+     VSA item).
+
+Readings taken where the pages are silent or loose (each one also listed in
+the design notes):
+  * video tokens are packed raster (t, h, w) with w fastest; video tiles are
+    numbered raster (tt, th, tw); tokens inside a tile raster (dt, dh, dw);
+  * tile numbering: all prefix tiles first, in packed order, then video tiles;
+    the video key index used for ties is the raster rank j in [0, Vt);
+  * a prefix segment becomes ceil(len/64) tiles of consecutive tokens; the
+    last one may be partial and its missing rows are padding, which takes
+    no part in pooling, softmax or output;
+  * softmax scale 1/sqrt(128) in both branches;
+  * k = ceil(keep * Vt / 100 - 1e-9) clamped to [1, Vt];
+  * the coarse branch scores and attends over every video key tile; prefix
+    key tiles are always exact and are not in the coarse branch;
+  * exact_kv: prefix query tiles are ordinary sparse rows;
+    exact_kv_and_rows: prefix query tiles are dense rows with no coarse term;
+  * G has the output's shape; no gate means no coarse term in the output
+    (the coarse scores still drive the selection); O_coarse of a query tile
+    is broadcast to each of its tokens;
+  * ranking uses the logit S (scale and bias included), ties go to the
+    lowest video tile index;
+  * tau statistics: per (batch, head), population mean and std (two-pass)
+    over every (sparse query tile, video key tile) logit; keep S > thr;
+  * log-mass bias b_j = log(mean_t exp(l_t - p_j)) with l_t = s q_a . k_t,
+    p_j = s q_a . kbar_j and q_a the mean of all video queries.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TILE_EDGE = 4
+TILE_TOKENS = TILE_EDGE ** 3       # 64
+HEAD_DIM = 128
+
+SEG_TEXT, SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_OTHER_PREFIX, SEG_VIDEO = 0, 1, 2, 3, 4
+SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 1, 2
+SELECT_TOPK, SELECT_TAU = 0, 1
+COARSE_MEAN, COARSE_MEAN_LOGMASS = 0, 1
+
+
+def softmax_scale(head_dim: int = HEAD_DIM) -> float:
+    """1/sqrt(d): the plain attention scale (pages silent; reading above)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+# --------------------------------------------------------------------------
+# 1. geometry mapper
+# --------------------------------------------------------------------------
+@dataclass
+class Geometry:
+    n_tokens: int
+    tiles: list            # tile id -> int64 array of packed token indices (valid tokens only)
+    tile_kind: list        # tile id -> segment kind
+    n_prefix: int          # P
+    n_video: int           # Vt
+    grid: tuple            # (T, H, W)
+    video_start: int
+
+    @property
+    def n_tiles(self) -> int:
+        return self.n_prefix + self.n_video
+
+
+def map_geometry(segments, T: int, H: int, W: int) -> Geometry:
+    """Cut the packed sequence into segment-pure tiles.
+
+    [R2V-fr] "Le correctif..." item 1 and [R2V-en] "The Solution": the mapper
+    isolates text / reference-image / reference-audio tokens in tiles of
+    their own.  [R2V-en] "Technical Architecture" and [FH3] "The mechanism":
+    video tokens are grouped in 4x4x4 spatio-temporal tiles of 64 tokens.
+    """
+    segs = sorted((int(s), int(n), int(kd)) for s, n, kd in segments)
+    pos = 0
+    for s, n, _ in segs:
+        if s != pos or n <= 0:
+            raise ValueError("segments must partition [0, N) with positive lengths")
+        pos += n
+    n_tokens = pos
+    videos = [sg for sg in segs if sg[2] == SEG_VIDEO]
+    if len(videos) != 1:
+        raise ValueError("exactly one video segment is required")
+    vstart, vlen, _ = videos[0]
+    if vlen != T * H * W or T % TILE_EDGE or H % TILE_EDGE or W % TILE_EDGE:
+        raise ValueError("video span must be T*H*W tokens with T, H, W multiples of 4")
+
+    tiles, kinds = [], []
+    for s, n, kd in segs:                      # prefix tiles, packed order
+        if kd == SEG_VIDEO:
+            continue
+        for off in range(0, n, TILE_TOKENS):
+            tiles.append(np.arange(s + off, s + min(off + TILE_TOKENS, n), dtype=np.int64))
+            kinds.append(kd)
+    n_prefix = len(tiles)
+    for tt in range(T // TILE_EDGE):           # video tiles, raster (tt, th, tw)
+        for th in range(H // TILE_EDGE):
+            for tw in range(W // TILE_EDGE):
+                toks = []
+                for dt in range(TILE_EDGE):    # tokens raster (dt, dh, dw)
+                    for dh in range(TILE_EDGE):
+                        for dw in range(TILE_EDGE):
+                            t = TILE_EDGE * tt + dt
+                            h = TILE_EDGE * th + dh
+                            w = TILE_EDGE * tw + dw
+                            toks.append(vstart + (t * H + h) * W + w)
+                tiles.append(np.asarray(toks, dtype=np.int64))
+                kinds.append(SEG_VIDEO)
+    n_video = len(tiles) - n_prefix
+    return Geometry(n_tokens, tiles, kinds, n_prefix, n_video, (T, H, W), vstart)
+
+
+def keep_count(keep_percent: float, n_video: int) -> int:
+    """Number k of video key tiles kept per query tile at a keep percent.
+
+    [FH3] "The inputs that matter": video_keep_percent; the plain reading of
+    a percent of Vt that is not an integer is to round up.
+    """
+    k = math.ceil(keep_percent * n_video / 100.0 - 1e-9)
+    return max(1, min(n_video, k))
+
+
+def row_classes(geom: Geometry, sink: int):
+    """(sparse query tiles, dense query tiles).
+
+    [FH3] "The inputs that matter", sink_conditioning: exact_kv keeps the
+    conditioning keys exact for every query; exact_kv_and_rows also runs the
+    conditioning queries dense.
+    """
+    prefix = list(range(geom.n_prefix))
+    video = list(range(geom.n_prefix, geom.n_tiles))
+    if sink == SINK_EXACT_KV:
+        return prefix + video, []
+    if sink == SINK_EXACT_KV_AND_ROWS:
+        return video, prefix
+    raise ValueError("unsupported sink mode")
+
+
+# --------------------------------------------------------------------------
+# 2. coarse branch summaries
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact bfloat16 -> float64 (a bf16 is the top 16 bits of a float32)."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def pool_tiles(X: np.ndarray, tiles) -> np.ndarray:
+    """Mean of the valid tokens of each tile ([SPK-es]: the compressed branch's
+    summary is a mean pool).  X is [N, D] for one (batch, head)."""
+    return np.stack([X[t].mean(axis=0) for t in tiles])
+
+
+def logmass_bias(Q: np.ndarray, K: np.ndarray, geom: Geometry, scale: float):
+    """Per video key tile log-mass bias, anchored at the mean video query.
+
+    [SPK-es] "Que cambia Spark-Attn", Spark-Reweight: mean pooling puts
+    exp(E[x]) in place of E[exp(x)]; a bias restores the missing mass, and the
+    score uses the mean of the video queries as a per-head anchor.
+      q_a = mean of Q over all valid video tokens
+      l_t = s q_a . k_t,  p_j = s q_a . kbar_j
+      b_j = log( mean_{t in j} exp(l_t - p_j) )
+    Returns (b [Vt], q_a [D]).
+    """
+    vt = geom.tiles[geom.n_prefix:]
+    video_tokens = np.concatenate(vt)
+    q_a = Q[video_tokens].mean(axis=0)
+    b = np.empty(len(vt))
+    for j, toks in enumerate(vt):
+        kbar = K[toks].mean(axis=0)
+        p = scale * (q_a @ kbar)
+        ell = scale * (K[toks] @ q_a)
+        b[j] = math.log(np.mean(np.exp(ell - p)))
+    return b, q_a
+
+
+def coarse_branch(Qbar: np.ndarray, Kbar: np.ndarray, Vbar: np.ndarray,
+                  bias: np.ndarray, scale: float):
+    """Coarse scores, softmax and output for a set of query tiles.
+
+    S_ij = s qbar_i . kbar_j + b_j over video key tiles j; P = row softmax;
+    O_c,i = sum_j P_ij vbar_j.  Returns (S, O_c).
+    """
+    S = scale * (Qbar @ Kbar.T) + bias[None, :]
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    P = E / E.sum(axis=1, keepdims=True)
+    return S, P @ Vbar
+
+
+# --------------------------------------------------------------------------
+# 4. selection
+# --------------------------------------------------------------------------
+def select_topk(S_row: np.ndarray, k: int) -> np.ndarray:
+    """The k largest logits; equal logits go to the lowest tile index.
+    Returns the kept video tile indices in ascending order."""
+    order = sorted(range(len(S_row)), key=lambda j: (-S_row[j], j))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def tau_threshold(S: np.ndarray, tau: float) -> float:
+    """mu + tau * sigma over every logit of one (batch, head), population
+    moments in two passes ([BSA-es] Sol-Attn: a per-head threshold in sigmas
+    of the score distribution)."""
+    vals = S.ravel()
+    n = vals.size
+    mu = float(np.sum(vals)) / n
+    var = float(np.sum((vals - mu) ** 2)) / n
+    return mu + tau * math.sqrt(var)
+
+
+def select_tau(S_row: np.ndarray, thr: float) -> np.ndarray:
+    return np.nonzero(S_row > thr)[0].astype(np.int64)
+
+
+def row_list(geom: Geometry, video_sel) -> np.ndarray:
+    """Key tiles of one sparse row: every prefix tile (never pruned) then the
+    kept video tiles, both ascending, as tile ids."""
+    return np.concatenate([np.arange(geom.n_prefix, dtype=np.int64),
+                           geom.n_prefix + np.asarray(video_sel, dtype=np.int64)])
+
+
+# --------------------------------------------------------------------------
+# 5. fine branch
+# --------------------------------------------------------------------------
+def fine_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry,
+             qtile: int, key_tiles, scale: float) -> np.ndarray:
+    """Exact softmax attention of the valid queries of one query tile over the
+    valid tokens of the listed key tiles.  Returns [n_valid, D]."""
+    rows = geom.tiles[qtile]
+    keys = np.concatenate([geom.tiles[t] for t in key_tiles])
+    z = scale * (Q[rows] @ K[keys].T)
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e @ V[keys]) / e.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# whole forward for one (batch, head)
+# --------------------------------------------------------------------------
+def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
+                 select: int, coarse: int, tau: float, rows=None,
+                 list_override=None, want_intermediates=False):
+    """Run the method for one (batch, head).
+
+    Q, K, V, G: float64 [N, D] (G may be None).  rows: query tile ids to
+    produce (None = all).  list_override: {query tile id: tile id array} to
+    replace the selection of some sparse rows (used when several selections
+    are correct).  Returns (O [N, D] with NaN outside the produced rows,
+    intermediates dict or None).
+    """
+    scale = softmax_scale(Q.shape[1])
+    sparse, dense = row_classes(geom, sink)
+    if rows is None:
+        rows = list(range(geom.n_tiles))
+    rows_set = set(int(r) for r in rows)
+    vt = geom.tiles[geom.n_prefix:]
+    Kbar = pool_tiles(K, vt)
+    Vbar = pool_tiles(V, vt)
+    if coarse == COARSE_MEAN_LOGMASS:
+        bias, q_a = logmass_bias(Q, K, geom, scale)
+    elif coarse == COARSE_MEAN:
+        bias, q_a = np.zeros(len(vt)), None
+    else:
+        raise ValueError("unsupported coarse mode")
+
+    # the tau threshold needs every sparse row's logits; top-k only the rows asked for
+    need = sparse if select == SELECT_TAU else [i for i in sparse if i in rows_set]
+    need_idx = {i: n for n, i in enumerate(need)}
+    Qbar = pool_tiles(Q, [geom.tiles[i] for i in need]) if need else np.zeros((0, Q.shape[1]))
+    S, Oc = coarse_branch(Qbar, Kbar, Vbar, bias, scale) if need else (np.zeros((0, len(vt))), None)
+    thr = tau_threshold(S, tau) if select == SELECT_TAU else None
+    k = keep_count(keep_percent, geom.n_video) if select == SELECT_TOPK else None
+
+    O = np.full_like(Q, np.nan)
+    lists = {}
+    dense_set = set(dense)
+    all_tiles = np.arange(geom.n_tiles, dtype=np.int64)
+    for i in sorted(rows_set):
+        toks = geom.tiles[i]
+        if i in dense_set:
+            lst = all_tiles
+        else:
+            srow = S[need_idx[i]]
+            if select == SELECT_TOPK:
+                sel = select_topk(srow, k)
+            else:
+                sel = select_tau(srow, thr)
+            lst = row_list(geom, sel)
+            if list_override is not None and i in list_override:
+                lst = np.asarray(list_override[i], dtype=np.int64)
+        lists[i] = lst
+        of = fine_row(Q, K, V, geom, i, lst, scale)
+        if i not in dense_set and G is not None:
+            of = of + G[toks] * Oc[need_idx[i]][None, :]
+        O[toks] = of
+    inter = None
+    if want_intermediates:
+        inter = dict(Kbar=Kbar, Vbar=Vbar, bias=bias, anchor=q_a, sparse_rows=need,
+                     Qbar=Qbar, S=S, Oc=Oc, thr=thr, k=k, lists=lists)
+    return O, inter
+
+
+def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
+            select: int = SELECT_TOPK, coarse: int = COARSE_MEAN, tau: float = 0.0,
+            heads=None, rows=None, list_override=None, want_intermediates=False):
+    """Oracle forward on bf16 bit arrays q, k, v, g ([B, N, H, D] uint16; g
+    may be None).  Returns (O float64 [B, N, H, D] (NaN where not produced),
+    {(b, h): intermediates}).  heads: iterable of (b, h) to run (None = all).
+    list_override: {(b, h): {query tile: tile ids}}."""
+    q, k, v, g = inputs["q"], inputs["k"], inputs["v"], inputs.get("g")
+    B, N, H, D = q.shape
+    T, Hh, W = grid
+    geom = map_geometry(segments, T, Hh, W)
+    if geom.n_tokens != N:
+        raise ValueError("segments do not cover the token axis")
+    O = np.full((B, N, H, D), np.nan)
+    inter = {}
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        Qh = bf16_bits_to_f64(q[b, :, h, :])
+        Kh = bf16_bits_to_f64(k[b, :, h, :])
+        Vh = bf16_bits_to_f64(v[b, :, h, :])
+        Gh = bf16_bits_to_f64(g[b, :, h, :]) if g is not None else None
+        for arr in (Qh, Kh, Vh) + ((Gh,) if Gh is not None else ()):
+            if not np.all(np.isfinite(arr)):
+                raise ValueError("inputs must be finite")
+        lo = None if list_override is None else list_override.get((b, h))
+        O[b, :, h, :], it = forward_head(Qh, Kh, Vh, Gh, geom, keep_percent, sink, select,
+                                         coarse, tau, rows=rows, list_override=lo,
+                                         want_intermediates=want_intermediates)
+        inter[(b, h)] = it
+    return O, inter

@@ -1,0 +1,444 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with an
+independent statement of what it must compute: a library routine (torch's
+scaled_dot_product_attention in float64, Python's exact ``statistics``
+module), an independent formulation (the video grid sliced into 4x4x4 cubes
+with numpy reshapes), brute force on tiny inputs, closed forms (log cosh),
+invariants and metamorphic relations.  ``test_oracle_pins.py`` runs them on
+the real oracle; ``test_oracle_mutations.py`` plants plausible mistakes in
+the oracle and checks that some pin fails.
+
+Pages are cited by the short tags defined in the oracle's header.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import statistics
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import torch
+
+from oracle import vsa_oracle as O
+from workloads.synth import (Workload, make_inputs, f32_to_bf16_bits, SEG_TEXT,
+                             SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_VIDEO, SINK_EXACT_KV,
+                             SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, SELECT_TAU,
+                             COARSE_MEAN, COARSE_MEAN_LOGMASS)
+
+GOLDEN = json.loads((Path(__file__).parent / "golden" / "page_numbers.json").read_text())
+D = 128
+
+# small shapes: several tiles, partial prefix tiles, both segment orders
+SMALL = Workload("small", 2, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 64), (SEG_REF_AUDIO, 30)),
+                 (4, 8, 12), 25.0, SINK_EXACT_KV, seed=7, recipe="iid")
+SMALL_VIDEO_FIRST = Workload("small_vf", 1, ((SEG_TEXT, 70), (SEG_REF_AUDIO, 64)), (8, 4, 8),
+                             30.0, SINK_EXACT_KV, seed=8, recipe="scaled", video_first=True)
+# every video axis holds more than one tile
+GEOM_3D = Workload("geom3d", 1, ((SEG_REF_IMAGE, 200),), (8, 12, 16), 25.0, SINK_EXACT_KV, seed=6)
+
+
+def as_f64(bits):
+    return O.bf16_bits_to_f64(bits)
+
+
+def torch_sdpa(q, k, v, mask=None):
+    """Textbook softmax(q k^T / sqrt(d) + mask) v in float64 via torch."""
+    tq = torch.from_numpy(np.ascontiguousarray(q))[None, None]
+    tk = torch.from_numpy(np.ascontiguousarray(k))[None, None]
+    tv = torch.from_numpy(np.ascontiguousarray(v))[None, None]
+    tm = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask))[None, None]
+    with torch.no_grad():
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm)
+    return out[0, 0].numpy()
+
+
+def video_cube_tokens(w: Workload):
+    """Token ids of every 4x4x4 video cube, from a reshape of the packed grid.
+
+    Independent of the oracle's index arithmetic: the video span is viewed as
+    a (T, H, W) array of token ids (raster, w fastest) and sliced."""
+    T, H, W = w.grid
+    vstart = [s for s, n, kd in w.segments() if kd == SEG_VIDEO][0]
+    ids = vstart + np.arange(T * H * W).reshape(T, H, W)
+    cubes = ids.reshape(T // 4, 4, H // 4, 4, W // 4, 4).transpose(0, 2, 4, 1, 3, 5)
+    return cubes.reshape(-1, 64)
+
+
+def prefix_chunks(w: Workload):
+    """Token ids of each 64-token run of every prefix segment, packed order."""
+    out = []
+    for s, n, kd in sorted(w.segments()):
+        if kd == SEG_VIDEO:
+            continue
+        for off in range(0, n, 64):
+            out.append(np.arange(s + off, s + min(off + 64, n)))
+    return out
+
+
+def independent_pool(X, w: Workload):
+    """Per-tile means: prefix chunks by slicing, video cubes by reshape+mean."""
+    T, H, W = w.grid
+    vstart = [s for s, n, kd in w.segments() if kd == SEG_VIDEO][0]
+    pre = np.stack([X[c].mean(axis=0) for c in prefix_chunks(w)])
+    vid = X[vstart:vstart + T * H * W].reshape(T // 4, 4, H // 4, 4, W // 4, 4, X.shape[1])
+    vid = vid.mean(axis=(1, 3, 5)).reshape(-1, X.shape[1])
+    return pre, vid
+
+
+def geom_of(w: Workload):
+    return O.map_geometry(w.segments(), *w.grid)
+
+
+# ---------------------------------------------------------------- P-4 geometry
+def check_geometry(w: Workload):
+    geom = geom_of(w)
+    cubes = video_cube_tokens(w)
+    chunks = prefix_chunks(w)
+    assert geom.n_prefix == len(chunks)
+    assert geom.n_video == len(cubes)
+    for i, c in enumerate(chunks):
+        assert np.array_equal(geom.tiles[i], c), f"prefix tile {i}"
+    for j, c in enumerate(cubes):
+        assert np.array_equal(geom.tiles[geom.n_prefix + j], c), f"video tile {j}"
+    # partition of the valid tokens
+    allt = np.concatenate(geom.tiles)
+    assert np.array_equal(np.sort(allt), np.arange(w.n_tokens))
+    # segment purity and cube shape
+    kind_of = np.empty(w.n_tokens, dtype=np.int64)
+    for s, n, kd in w.segments():
+        kind_of[s:s + n] = kd
+    for t, toks in enumerate(geom.tiles):
+        assert len(set(kind_of[toks].tolist())) == 1, f"tile {t} mixes segments"
+        assert 1 <= len(toks) <= GOLDEN["tile_tokens"]["value"]
+    T, H, W = w.grid
+    vstart = geom.video_start
+    e = GOLDEN["tile_edge"]["value"]
+    for toks in geom.tiles[geom.n_prefix:]:
+        r = toks - vstart
+        t, h, ww = r // (H * W), (r // W) % H, r % W
+        for ax in (t, h, ww):
+            assert ax.max() - ax.min() == e - 1 and ax.min() % e == 0
+            assert len(set(ax.tolist())) == e
+    # gather then scatter is the identity, bitwise
+    X = np.random.default_rng(3).standard_normal((w.n_tokens, 5))
+    gathered = [X[toks] for toks in geom.tiles]
+    Y = np.full_like(X, np.nan)
+    for toks, g in zip(geom.tiles, gathered):
+        Y[toks] = g
+    assert np.array_equal(X, Y)
+
+
+def check_keep_counts():
+    """k from a keep percent at the pages' operating points and the workloads' grids."""
+    assert O.keep_count(10.0, 528) == 53
+    assert O.keep_count(20.0, 528) == 106
+    assert O.keep_count(25.0, 264) == 66
+    assert O.keep_count(25.0, 16) == 4
+    assert O.keep_count(100.0, 528) == 528
+    assert O.keep_count(0.01, 528) == 1
+    for p in GOLDEN["keep_operating_points_percent"]["value"]:
+        k = O.keep_count(float(p), 528)
+        assert k - 1 < p * 528 / 100 <= k
+
+
+# ---------------------------------------------------------------- P-1 fine branch
+def check_dense_equivalence(w: Workload):
+    """keep 100%, no gate: every list holds every tile, so the output is plain
+    dense softmax attention over all tokens ([BSA-es]/[SPK-es]: sparse results
+    are judged against the dense run)."""
+    x = make_inputs(w, with_gate=False)
+    out, _ = O.forward(x, w.segments(), w.grid, 100.0, w.sink)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            ref = torch_sdpa(as_f64(x["q"][b, :, h]), as_f64(x["k"][b, :, h]), as_f64(x["v"][b, :, h]))
+            err = np.abs(out[b, :, h] - ref).max()
+            assert err < 1e-12, f"dense equivalence b{b} h{h}: {err}"
+
+
+def check_dense_rows_and_gate(w: Workload):
+    """exact_kv_and_rows at keep 100% with a gate: prefix rows are dense with no
+    coarse term; video rows are dense plus G * O_coarse of their tile."""
+    x = make_inputs(w, with_gate=True)
+    out, _ = O.forward(x, w.segments(), w.grid, 100.0, SINK_EXACT_KV_AND_ROWS)
+    cubes = video_cube_tokens(w)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            Q, K, V, G = (as_f64(x[n][b, :, h]) for n in "qkvg")
+            dense = torch_sdpa(Q, K, V)
+            _, qv = independent_pool(Q, w)
+            _, kv = independent_pool(K, w)
+            _, vv = independent_pool(V, w)
+            oc = torch_sdpa(qv, kv, vv)                    # [Vt, D]
+            ref = dense.copy()
+            for j, toks in enumerate(cubes):
+                ref[toks] += G[toks] * oc[j][None, :]
+            err = np.abs(out[b, :, h] - ref).max()
+            assert err < 1e-12, f"dense rows + gate b{b} h{h}: {err}"
+
+
+# ---------------------------------------------------------------- P-2 coarse
+def check_pooling(w: Workload):
+    x = make_inputs(w)
+    geom = geom_of(w)
+    for h in range(w.heads):
+        X = as_f64(x["q"][0, :, h])
+        pre, vid = independent_pool(X, w)
+        got = O.pool_tiles(X, geom.tiles)
+        assert np.abs(got[:geom.n_prefix] - pre).max() < 1e-13
+        assert np.abs(got[geom.n_prefix:] - vid).max() < 1e-13
+
+
+def check_coarse(w: Workload, coarse=COARSE_MEAN):
+    """O_coarse is dense attention on the pooled summaries (plus the bias as an
+    additive mask in log-mass mode); prefix key tiles are not in it."""
+    x = make_inputs(w)
+    geom = geom_of(w)
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, SINK_EXACT_KV, coarse=coarse,
+                         want_intermediates=True)
+    for h in range(w.heads):
+        Q, K, V = (as_f64(x[n][0, :, h]) for n in "qkv")
+        qp, qv = independent_pool(Q, w)
+        _, kv = independent_pool(K, w)
+        _, vv = independent_pool(V, w)
+        it = inter[(0, h)]
+        assert it["sparse_rows"] == list(range(geom.n_tiles))
+        qall = np.concatenate([qp, qv])
+        mask = np.broadcast_to(it["bias"][None, :], (qall.shape[0], kv.shape[0]))
+        ref = torch_sdpa(qall, kv, vv, mask=mask)
+        assert np.abs(it["Oc"] - ref).max() < 1e-12
+        S_ref = qall @ kv.T / math.sqrt(D) + mask
+        assert np.abs(it["S"] - S_ref).max() < 1e-12
+        if coarse == COARSE_MEAN:
+            assert np.all(it["bias"] == 0.0)
+
+
+# ---------------------------------------------------------------- P-3 prefix exemption
+def check_prefix_exempt(w: Workload):
+    x = make_inputs(w)
+    geom = geom_of(w)
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, want_intermediates=True)
+    k = O.keep_count(w.keep, geom.n_video)
+    sparse, dense = O.row_classes(geom, w.sink)
+    for it in inter.values():
+        for i, lst in it["lists"].items():
+            lst = list(lst)
+            assert lst == sorted(lst)
+            assert set(range(geom.n_prefix)) <= set(lst), f"row {i} lost a prefix tile"
+            if i in dense:
+                assert lst == list(range(geom.n_tiles))
+            else:
+                assert len(lst) == geom.n_prefix + k
+                assert all(t >= geom.n_prefix for t in lst[geom.n_prefix:])
+
+
+# ---------------------------------------------------------------- P-5 top-k
+def brute_topk(s, k):
+    """All k-subsets; keep those with the largest sorted value profile, then the
+    lexicographically smallest index set (ties -> lowest indices)."""
+    best = None
+    for comb in itertools.combinations(range(len(s)), k):
+        key = (sorted((s[j] for j in comb), reverse=True), [-j for j in comb])
+        # compare value profile first (larger better), then prefer smaller indices
+        if best is None or key[0] > best[0][0] or (key[0] == best[0][0] and list(comb) < best[1]):
+            best = (key, list(comb))
+    return best[1]
+
+
+def check_topk_bruteforce():
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        n = int(rng.integers(3, 9))
+        k = int(rng.integers(1, n + 1))
+        vals = rng.integers(0, 4, size=n).astype(np.float64) if trial % 2 else rng.standard_normal(n)
+        got = list(O.select_topk(vals, k))
+        assert got == brute_topk(list(vals), k), (vals, k, got)
+
+
+def check_topk_ties_in_forward():
+    """Every video key tile a copy of video tile 0: all coarse logits of a row
+    tie, so each sparse row must keep video tiles 0..k-1."""
+    w = Workload("ties", 1, ((SEG_TEXT, 64),), (4, 8, 8), 25.0, SINK_EXACT_KV, seed=5)
+    x = make_inputs(w)
+    geom = geom_of(w)
+    k = x["k"].copy()
+    first = geom.tiles[geom.n_prefix]
+    for toks in geom.tiles[geom.n_prefix:]:
+        k[0, toks] = x["k"][0, first]
+    x["k"] = k
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, want_intermediates=True)
+    kk = O.keep_count(w.keep, geom.n_video)
+    for lst in inter[(0, 0)]["lists"].values():
+        assert list(lst) == list(range(geom.n_prefix)) + [geom.n_prefix + j for j in range(kk)]
+
+
+# ---------------------------------------------------------------- P-6 tau
+def check_tau_threshold():
+    rng = np.random.default_rng(21)
+    S = rng.standard_normal((7, 11)) * 0.3 + 0.1
+    vals = [Fraction(float(v)) for v in S.ravel()]
+    mu = statistics.fmean(S.ravel())
+    sd = statistics.pstdev(S.ravel().tolist())
+    for tau in (1.0, 1.5, 2.0, -0.5):
+        thr = O.tau_threshold(S, tau)
+        assert abs(thr - (mu + tau * sd)) < 1e-12
+    assert len(vals) == 77
+
+
+def check_tau_limits(w: Workload):
+    x = make_inputs(w)
+    geom = geom_of(w)
+    for tau, expect_video in ((1e6, 0), (-1e6, geom.n_video)):
+        _, inter = O.forward(x, w.segments(), w.grid, 0.0, SINK_EXACT_KV, select=SELECT_TAU,
+                             tau=tau, want_intermediates=True)
+        for lst in inter[(0, 0)]["lists"].values():
+            assert len(lst) == geom.n_prefix + expect_video
+
+
+def check_tau_fractions():
+    """On near-Gaussian pooled logits the kept share of video tiles follows the
+    pages' tau -> share table (statistical sanity, loose bound)."""
+    w = Workload("taufrac", 2, ((SEG_TEXT, 128),), (16, 16, 16), 0.0, SINK_EXACT_KV, seed=31)
+    x = make_inputs(w, with_gate=False)
+    geom = geom_of(w)
+    for tau_s, page in GOLDEN["tau_kept_fraction"]["value"].items():
+        tau = float(tau_s)
+        _, inter = O.forward(x, w.segments(), w.grid, 0.0, SINK_EXACT_KV, select=SELECT_TAU,
+                             tau=tau, rows=[], want_intermediates=True)
+        kept = 0
+        total = 0
+        for it in inter.values():
+            kept += int((it["S"] > it["thr"]).sum())
+            total += it["S"].size
+        frac = kept / total
+        assert abs(frac - page) <= max(0.01, 0.2 * page), (tau, frac, page)
+
+
+# ---------------------------------------------------------------- P-7 log-mass
+def check_logmass():
+    """Jensen (b >= 0), constant tiles (b = 0) and a closed form: when the
+    anchored token logits of a tile are +d and -d in equal numbers,
+    b = log cosh d ([SPK-es] Spark-Reweight and its figure: the biased pooled
+    logit's exponential equals the mean exponential)."""
+    w = Workload("lm", 1, ((SEG_TEXT, 64),), (4, 8, 8), 25.0, SINK_EXACT_KV, seed=41)
+    x = make_inputs(w)
+    geom = geom_of(w)
+    q = np.zeros((1, w.n_tokens, 1, D), np.float32)
+    k = np.zeros_like(q)
+    u = np.zeros(D, np.float32)
+    u[3] = 1.5
+    vs = geom.video_start
+    q[0, :, 0] = np.asarray(O.bf16_bits_to_f64(x["q"][0, :, 0]), np.float32)
+    q[0, vs:, 0] = u                                  # every video query equals u
+    rng = np.random.default_rng(42)
+    tiles = geom.tiles[geom.n_prefix:]
+    amp = {}
+    for j, toks in enumerate(tiles):
+        base = rng.integers(-8, 8, size=D).astype(np.float32) / 4
+        if j % 3 == 0:                                # constant tile -> b = 0
+            k[0, toks, 0] = base
+            amp[j] = 0.0
+        elif j % 3 == 1:                              # +/- a along e3 -> log cosh
+            a = float(j % 5 + 1) / 2
+            sgn = np.where(np.arange(len(toks)) % 2 == 0, 1.0, -1.0).astype(np.float32)
+            k[0, toks, 0] = base
+            k[0, toks, 0, 3] += sgn * a
+            amp[j] = 1.5 * a / math.sqrt(D)
+        else:                                         # random tile: Jensen only
+            k[0, toks, 0] = rng.standard_normal((len(toks), D)).astype(np.float32)
+    Qh = O.bf16_bits_to_f64(f32_to_bf16_bits(q)[0, :, 0])
+    Kh = O.bf16_bits_to_f64(f32_to_bf16_bits(k)[0, :, 0])
+    b, q_a = O.logmass_bias(Qh, Kh, geom, 1.0 / math.sqrt(D))
+    assert np.allclose(q_a, u, atol=0, rtol=0)
+    assert np.all(b >= -1e-15)
+    for j, d in amp.items():
+        assert abs(b[j] - math.log(math.cosh(d))) < 1e-12, (j, b[j], d)
+    # the biased pooled logit's exponential equals the mean token exponential
+    for j, toks in enumerate(tiles):
+        s = 1.0 / math.sqrt(D)
+        lhs = math.exp(s * float(u.astype(np.float64) @ Kh[toks].mean(axis=0)) + b[j])
+        rhs = float(np.mean([math.exp(s * float(u.astype(np.float64) @ Kh[t])) for t in toks]))
+        assert abs(lhs - rhs) <= 1e-12 * rhs
+
+
+# ---------------------------------------------------------------- P-8 combine
+def check_combine(w: Workload):
+    x = make_inputs(w, with_gate=True)
+    segs = w.segments()
+    o1, _ = O.forward(x, segs, w.grid, w.keep, w.sink)
+    x0 = dict(x, g=None)
+    o0, _ = O.forward(x0, segs, w.grid, w.keep, w.sink)
+    xz = dict(x, g=np.zeros_like(x["g"]))
+    oz, _ = O.forward(xz, segs, w.grid, w.keep, w.sink)
+    assert np.array_equal(o0, oz)
+    # linear in G: doubling G (exact in bf16) doubles O - O(G=0)
+    g2 = f32_to_bf16_bits(2 * O.bf16_bits_to_f64(x["g"]).astype(np.float32))
+    o2, _ = O.forward(dict(x, g=g2), segs, w.grid, w.keep, w.sink)
+    assert np.abs((o2 - o0) - 2 * (o1 - o0)).max() < 1e-12
+    assert np.abs(o1 - o0).max() > 1e-3
+
+
+# ---------------------------------------------------------------- P-9 metamorphic
+def check_metamorphic(w: Workload):
+    x = make_inputs(w, with_gate=True)
+    geom = geom_of(w)
+    rng = np.random.default_rng(51)
+    for h in range(w.heads):
+        Q, K, V, G = (as_f64(x[n][0, :, h]) for n in "qkvg")
+        for coarse in (COARSE_MEAN, COARSE_MEAN_LOGMASS):
+            args = (geom, w.keep, w.sink, SELECT_TOPK, coarse, 0.0)
+            o, it = O.forward_head(Q, K, V, G, *args, want_intermediates=True)
+            c = rng.standard_normal(D)
+            o2, it2 = O.forward_head(Q, K + c[None, :], V, G, *args, want_intermediates=True)
+            for i in it["lists"]:
+                assert np.array_equal(it["lists"][i], it2["lists"][i])
+            assert np.abs(o - o2).max() < 1e-9
+            assert np.abs(it["bias"] - it2["bias"]).max() < 1e-9
+            o3, _ = O.forward_head(Q, K, 3.0 * V, G, *args)
+            assert np.abs(o3 - 3.0 * o).max() < 1e-9
+
+
+def check_prefix_permutation():
+    """Reordering the conditioning segments permutes the outputs of their
+    tokens and leaves every video token's output unchanged."""
+    pre = ((SEG_TEXT, 64), (SEG_REF_IMAGE, 128), (SEG_REF_AUDIO, 64))
+    w = Workload("perm", 1, pre, (4, 8, 8), 25.0, SINK_EXACT_KV, seed=61)
+    x = make_inputs(w)
+    perm_pre = (pre[2], pre[0], pre[1])
+    w2 = Workload("perm2", 1, perm_pre, (4, 8, 8), 25.0, SINK_EXACT_KV, seed=61)
+    # token map: new position -> old position
+    old_start = {kd: s for s, n, kd in w.segments()}
+    idx = []
+    for s, n, kd in sorted(w2.segments()):
+        idx.extend(range(old_start[kd], old_start[kd] + n))
+    idx = np.asarray(idx)
+    x2 = {n: x[n][:, idx] for n in "qkvg"}
+    o, _ = O.forward(x, w.segments(), w.grid, w.keep, w.sink)
+    o2, _ = O.forward(x2, w2.segments(), w2.grid, w2.keep, w2.sink)
+    assert np.abs(o2 - o[:, idx]).max() < 1e-12
+
+
+ALL_CHECKS = [
+    ("geometry", lambda: (check_geometry(SMALL), check_geometry(SMALL_VIDEO_FIRST),
+                          check_geometry(GEOM_3D))),
+    ("keep_counts", check_keep_counts),
+    ("dense_equivalence", lambda: (check_dense_equivalence(SMALL), check_dense_equivalence(SMALL_VIDEO_FIRST))),
+    ("dense_rows_and_gate", lambda: check_dense_rows_and_gate(SMALL)),
+    ("pooling", lambda: check_pooling(SMALL)),
+    ("coarse_mean", lambda: check_coarse(SMALL, COARSE_MEAN)),
+    ("coarse_logmass", lambda: check_coarse(SMALL_VIDEO_FIRST, COARSE_MEAN_LOGMASS)),
+    ("prefix_exempt", lambda: (check_prefix_exempt(SMALL), check_prefix_exempt(
+        Workload("pe", 1, SMALL.prefix, SMALL.grid, 10.0, SINK_EXACT_KV_AND_ROWS, seed=9)))),
+    ("topk_bruteforce", check_topk_bruteforce),
+    ("topk_ties", check_topk_ties_in_forward),
+    ("tau_threshold", check_tau_threshold),
+    ("tau_limits", lambda: check_tau_limits(SMALL)),
+    ("tau_fractions", check_tau_fractions),
+    ("logmass", check_logmass),
+    ("combine", lambda: check_combine(SMALL)),
+    ("metamorphic", lambda: check_metamorphic(SMALL_VIDEO_FIRST)),
+    ("prefix_permutation", check_prefix_permutation),
+]

@@ -1,0 +1,105 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin fails.
+
+Each mutation replaces one oracle function with a wrong variant; the named
+pin must then raise.  This shows the pins can tell a right oracle from a
+plausibly wrong one, so agreement with them means something.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import vsa_oracle as O
+
+_orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
+                                      "logmass_bias", "coarse_branch", "tau_threshold",
+                                      "keep_count", "pool_tiles", "fine_row")}
+
+
+def _geom_swapped_axes(segments, T, H, W):
+    g = _orig["map_geometry"](segments, T, H, W)
+    # video tiles enumerated (th, tt, tw) instead of (tt, th, tw)
+    nt, nh, nw = T // 4, H // 4, W // 4
+    vid = g.tiles[g.n_prefix:]
+    order = [tt * nh * nw + th * nw + tw for th in range(nh) for tt in range(nt) for tw in range(nw)]
+    g.tiles = g.tiles[:g.n_prefix] + [vid[o] for o in order]
+    return g
+
+
+def _geom_token_order(segments, T, H, W):
+    g = _orig["map_geometry"](segments, T, H, W)
+    # tokens inside a video tile in (dw, dh, dt) order
+    perm = np.arange(64).reshape(4, 4, 4).transpose(2, 1, 0).ravel()
+    g.tiles = g.tiles[:g.n_prefix] + [t[perm] for t in g.tiles[g.n_prefix:]]
+    return g
+
+
+def _topk_high_ties(S_row, k):
+    order = sorted(range(len(S_row)), key=lambda j: (-S_row[j], -j))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def _topk_smallest(S_row, k):
+    order = sorted(range(len(S_row)), key=lambda j: (S_row[j], j))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+def _bias_flipped(Q, K, geom, scale):
+    b, qa = _orig["logmass_bias"](Q, K, geom, scale)
+    return -b, qa
+
+
+def _bias_no_anchor(Q, K, geom, scale):
+    return np.zeros(geom.n_video), np.zeros(Q.shape[1])
+
+
+def _coarse_no_bias(Qbar, Kbar, Vbar, bias, scale):
+    return _orig["coarse_branch"](Qbar, Kbar, Vbar, np.zeros_like(bias), scale)
+
+
+def _tau_variance(S, tau):
+    vals = S.ravel()
+    mu = float(np.mean(vals))
+    return mu + tau * float(np.mean((vals - mu) ** 2))
+
+
+def _fine_k_for_v(Q, K, V, geom, qtile, key_tiles, scale):
+    return _orig["fine_row"](Q, K, K, geom, qtile, key_tiles, scale)
+
+
+MUTATIONS = [
+    ("scale_1_over_d", "softmax_scale", lambda d=128: 1.0 / d, "dense_equivalence"),
+    ("tile_axes_swapped", "map_geometry", _geom_swapped_axes, "geometry"),
+    ("tile_token_order", "map_geometry", _geom_token_order, "geometry"),
+    ("ties_to_highest", "select_topk", _topk_high_ties, "topk_ties"),
+    ("topk_smallest", "select_topk", _topk_smallest, "topk_bruteforce"),
+    ("prefix_dropped", "row_list", lambda geom, sel: geom.n_prefix + np.asarray(sel, dtype=np.int64),
+     "prefix_exempt"),
+    ("bias_sign", "logmass_bias", _bias_flipped, "logmass"),
+    ("bias_no_anchor", "logmass_bias", _bias_no_anchor, "logmass"),
+    ("coarse_ignores_bias", "coarse_branch", _coarse_no_bias, "coarse_logmass"),
+    ("tau_uses_variance", "tau_threshold", _tau_variance, "tau_threshold"),
+    ("keep_floor", "keep_count", lambda p, n: max(1, min(n, math.floor(p * n / 100.0))), "keep_counts"),
+    ("pool_sum", "pool_tiles", lambda X, tiles: np.stack([X[t].sum(axis=0) for t in tiles]), "pooling"),
+    ("fine_k_as_v", "fine_row", _fine_k_for_v, "dense_equivalence"),
+]
+
+
+@pytest.mark.parametrize("name,attr,bad,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, attr, bad, pin):
+    monkeypatch.setattr(O, attr, bad)
+    check = dict(P.ALL_CHECKS)[pin]
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_combine_sign_is_caught(monkeypatch):
+    """O_fine - G*O_coarse instead of +: the dense-rows-with-gate pin fails."""
+    orig = O.forward_head
+
+    def bad(Q, K, V, G, *a, **kw):
+        return orig(Q, K, V, None if G is None else -G, *a, **kw)
+    monkeypatch.setattr(O, "forward_head", bad)
+    with pytest.raises(AssertionError):
+        P.check_dense_rows_and_gate(P.SMALL)
