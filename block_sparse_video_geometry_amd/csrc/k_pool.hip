@@ -1,0 +1,174 @@
+// Geometry gather + mean pooling, and the log-mass anchor and bias.
+//
+// Pooling: the compressed branch summarises each tile by the mean of its
+// tokens ("Spark-H3: atencion dispersa por bloques acelera MiniMax-H3 en
+// ComfyUI", "Que cambia Spark-Attn"; "ComfyUI Agrega Nodo Central de Atencion
+// Dispersa...", VSA item: cubic tiling plus a coarse compression branch).
+// Log-mass bias: same Spark page, Spark-Reweight item: mean pooling stands
+// exp(E[x]) in for E[exp(x)]; a bias per tile, scored with the mean video
+// query as the anchor, restores the missing mass.
+//
+// HBM-bound: each (tile, head) slice of Q, K, V is read once; one wave per
+// (tile, head), 16 lanes per token (16 x 16 B = one 256-byte head row), four
+// tokens per load instruction, all 16 loads of a tile in flight.
+#include "vsa_device.h"
+#include "vsa_kernels.h"
+
+namespace {
+
+// Sum of this wave's 64 tile rows of one head: lane group grp = lane/16 owns
+// rows 4p + grp, lane chunk c = lane%16 owns dims 8c..8c+7.  Result reduced
+// over the four groups (every lane holds its chunk's sums).
+__device__ __forceinline__ void tile_sum(const VsaGeom& g, const u32x4* __restrict__ X, int b,
+                                         int h, int t, int grp, int c, float acc[8]) {
+  u32x4 buf[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int tok = tile_token(g, t, 4 * p + grp);
+    if (tok >= 0)
+      buf[p] = X[row_offset(g, b, tok, h) / 8 + c];
+    else
+      buf[p] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w] += bf16lo(buf[p][w]);
+      acc[2 * w + 1] += bf16hi(buf[p][w]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] += __shfl_xor(acc[i], 16);
+    acc[i] += __shfl_xor(acc[i], 32);
+  }
+}
+
+__device__ __forceinline__ void store8(float* dst, const float v[8], float mul) {
+  f32x4* d4 = reinterpret_cast<f32x4*>(dst);
+  d4[0] = f32x4{v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul};
+  d4[1] = f32x4{v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul};
+}
+
+__global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* __restrict__ q,
+                                                       const u32x4* __restrict__ k,
+                                                       const u32x4* __restrict__ v,
+                                                       float* __restrict__ qbar,
+                                                       float* __restrict__ kbar,
+                                                       float* __restrict__ vbar,
+                                                       float* __restrict__ bias) {
+  const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;
+  const int b = blockIdx.z;
+  if (h >= g.heads) return;
+  const int grp = lane >> 4, c = lane & 15;
+  const size_t bh = (size_t)b * g.heads + h;
+  const float inv = 1.0f / (float)tile_valid(g, t);
+  float acc[8];
+  tile_sum(g, q, b, h, t, grp, c, acc);
+  if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  if (t < g.P) return;
+  const int j = t - g.P;
+  tile_sum(g, k, b, h, t, grp, c, acc);
+  if (grp == 0) store8(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  tile_sum(g, v, b, h, t, grp, c, acc);
+  if (grp == 0) store8(vbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  if (g.coarse == VSA_COARSE_MEAN && lane == 0) bias[bh * g.Vt + j] = 0.0f;
+}
+
+// q_a = mean of the video tiles' qbar (every video tile holds 64 tokens, so
+// this is the mean of all video queries).  Fixed-order reduction.
+__global__ __launch_bounds__(1024) void vsa_anchor_kernel(VsaGeom g, const float* __restrict__ qbar,
+                                                          float* __restrict__ anchor) {
+  __shared__ float part[8][VSA_HEAD_DIM];
+  const int d = threadIdx.x & 127, slice = threadIdx.x >> 7;
+  const size_t bh = (size_t)blockIdx.y * g.heads + blockIdx.x;
+  const float* base = qbar + (bh * g.Tq + g.P) * VSA_HEAD_DIM + d;
+  float s = 0.f;
+  for (int j = slice; j < g.Vt; j += 8) s += base[(size_t)j * VSA_HEAD_DIM];
+  part[slice][d] = s;
+  __syncthreads();
+  if (slice == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot += part[i][d];
+    anchor[bh * VSA_HEAD_DIM + d] = tot / (float)g.Vt;
+  }
+}
+
+// b_j = log(mean_t exp(s q_a . (k_t - kbar_j))), max-shifted.  One wave per
+// (video tile, head).
+__global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4* __restrict__ k,
+                                                          const float* __restrict__ kbar,
+                                                          const float* __restrict__ anchor,
+                                                          float* __restrict__ bias) {
+  const int j = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;
+  const int b = blockIdx.z;
+  if (h >= g.heads) return;
+  const int grp = lane >> 4, c = lane & 15;
+  const size_t bh = (size_t)b * g.heads + h;
+  const int t = g.P + j;
+  float qa[8], kb[8];
+  const f32x4* a4 = reinterpret_cast<const f32x4*>(anchor + bh * VSA_HEAD_DIM + 8 * c);
+  const f32x4* k4 = reinterpret_cast<const f32x4*>(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qa[i] = a4[0][i];
+    qa[4 + i] = a4[1][i];
+    kb[i] = k4[0][i];
+    kb[4 + i] = k4[1][i];
+  }
+  u32x4 buf[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) buf[p] = k[row_offset(g, b, tile_token(g, t, 4 * p + grp), h) / 8 + c];
+  float ell[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s += qa[2 * w] * (bf16lo(buf[p][w]) - kb[2 * w]);
+      s += qa[2 * w + 1] * (bf16hi(buf[p][w]) - kb[2 * w + 1]);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) s += __shfl_xor(s, m);
+    ell[p] = s * g.scale;
+  }
+  float mx = ell[0];
+#pragma unroll
+  for (int p = 1; p < 16; ++p) mx = fmaxf(mx, ell[p]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float se = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) se += expf(ell[p] - mx);
+  se += __shfl_xor(se, 16);
+  se += __shfl_xor(se, 32);
+  if (lane == 0) bias[bh * g.Vt + j] = mx + logf(se * (1.0f / VSA_TILE_TOKENS));
+}
+
+}  // namespace
+
+void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void* v, float* qbar,
+                     float* kbar, float* vbar, float* bias, hipStream_t st) {
+  dim3 grid(g.Tq, (g.heads + 3) / 4, g.batch);
+  hipLaunchKernelGGL(vsa_pool_kernel, grid, dim3(256), 0, st, g, (const u32x4*)q, (const u32x4*)k,
+                     (const u32x4*)v, qbar, kbar, vbar, bias);
+}
+
+void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipStream_t st) {
+  hipLaunchKernelGGL(vsa_anchor_kernel, dim3(g.heads, g.batch), dim3(1024), 0, st, g, qbar, anchor);
+}
+
+void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
+                        float* bias, hipStream_t st) {
+  dim3 grid(g.Vt, (g.heads + 3) / 4, g.batch);
+  hipLaunchKernelGGL(vsa_logmass_kernel, grid, dim3(256), 0, st, g, (const u32x4*)k, kbar, anchor,
+                     bias);
+}

@@ -1,0 +1,272 @@
+// vsa_forward: argument checks and the launch sequence on the caller's stream;
+// stats read-back and the per-kernel event timer.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "vsa_internal.h"
+#include "vsa_kernels.h"
+
+namespace {
+
+bool log_enabled() {
+  static const int on = [] {
+    const char* e = std::getenv("VSA_LOG");
+    return (e != nullptr && e[0] == '1') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+// 1 = gfx950, -1 = other, 0 = not yet checked (per device ordinal)
+int g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VSA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return VSA_ERR_UNSUPPORTED;
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VSA_ERR_HIP;
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_arch_ok[dev] == 1 ? VSA_OK : VSA_ERR_UNSUPPORTED;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr) return false;
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+struct vsa_timer {
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;          // recorded since the last read
+  std::vector<hipEvent_t> pool;   // free events
+  std::vector<std::string> names;
+  std::vector<double> total_ms;
+  std::vector<int> launches;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  int stage_id(const char* name) {
+    for (size_t i = 0; i < names.size(); ++i)
+      if (names[i] == name) return (int)i;
+    names.emplace_back(name);
+    total_ms.push_back(0.0);
+    launches.push_back(0);
+    return (int)names.size() - 1;
+  }
+};
+
+namespace {
+
+// Runs `launch` between two events when a timer is given.
+template <class F>
+int timed(vsa_timer* tm, const char* name, hipStream_t st, F&& launch) {
+  if (tm == nullptr) {
+    launch();
+    return VSA_OK;
+  }
+  vsa_timer::Rec r{tm->stage_id(name), tm->get(), tm->get()};
+  if (r.a == nullptr || r.b == nullptr) return VSA_ERR_HIP;
+  if (hipEventRecord(r.a, st) != hipSuccess) return VSA_ERR_HIP;
+  launch();
+  if (hipEventRecord(r.b, st) != hipSuccess) return VSA_ERR_HIP;
+  tm->recs.push_back(r);
+  return VSA_OK;
+}
+
+}  // namespace
+
+int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                       const void* g, void* o, void* workspace, void* stream, vsa_timer* tm) {
+  const VsaGeom& G = plan->g;
+  const VsaLayout& L = plan->ws;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qbar = reinterpret_cast<float*>(ws + L.qbar);
+  float* kbar = reinterpret_cast<float*>(ws + L.kbar);
+  float* vbar = reinterpret_cast<float*>(ws + L.vbar);
+  float* bias = reinterpret_cast<float*>(ws + L.bias);
+  float* anchor = reinterpret_cast<float*>(ws + L.anchor);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  float* ocoarse = reinterpret_cast<float*>(ws + L.ocoarse);
+  float* thr = reinterpret_cast<float*>(ws + L.thr);
+  int* lists = reinterpret_cast<int*>(ws + L.lists);
+  int* counts = reinterpret_cast<int*>(ws + L.counts);
+  double* statp = reinterpret_cast<double*>(ws + L.statp);
+
+  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+  int rc = VSA_OK;
+#define VSA_STEP(name, call)                                  \
+  do {                                                        \
+    rc = timed(tm, name, st, [&] { call; });                  \
+    if (rc != VSA_OK) return rc;                              \
+    if (hipGetLastError() != hipSuccess) return VSA_ERR_HIP;  \
+  } while (0)
+
+  VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
+  if (G.coarse == VSA_COARSE_MEAN_LOGMASS) {
+    VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
+    VSA_STEP("logmass", vsa_launch_logmass(G, k, kbar, anchor, bias, st));
+  }
+  VSA_STEP("scores", vsa_launch_scores(G, qbar, kbar, bias, scores, statp, st));
+  VSA_STEP("coarse_out", vsa_launch_coarse_out(G, scores, vbar, ocoarse, st));
+  if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
+  VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
+  VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, st));
+#undef VSA_STEP
+  return VSA_OK;
+}
+
+namespace {
+
+int forward_common(const vsa_plan* plan, const void* q, const void* k, const void* v, const void* g,
+                   void* o, void* workspace, size_t workspace_bytes, void* stream, vsa_timer* tm) {
+  if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return VSA_ERR_INVALID_ARGUMENT;
+  if (workspace == nullptr || workspace_bytes < plan->ws.total) return VSA_ERR_WORKSPACE;
+  const void* bufs[5] = {q, k, v, g, o};
+  for (const void* p : bufs)
+    if (p != nullptr && !aligned(p, 16)) return VSA_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256)) return VSA_ERR_INVALID_ARGUMENT;
+  const size_t tbytes = (size_t)plan->g.batch * plan->n_tokens * plan->g.heads * VSA_HEAD_DIM * 2;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(o, tbytes, bufs[i], tbytes)) return VSA_ERR_INVALID_ARGUMENT;
+  if (overlaps(o, tbytes, workspace, plan->ws.total)) return VSA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(workspace, plan->ws.total, bufs[i], tbytes)) return VSA_ERR_INVALID_ARGUMENT;
+  const int dev = check_device();
+  if (dev != VSA_OK) return dev;
+  const int rc = vsa_launch_forward(plan, q, k, v, g, o, workspace, stream, tm);
+  if (log_enabled()) {
+    const VsaGeom& G = plan->g;
+    std::fprintf(stderr,
+                 "[vsa] forward B=%d N=%d heads=%d P=%d Vt=%d k=%d sink=%d select=%d coarse=%d "
+                 "tau=%g gate=%d status=%d\n",
+                 G.batch, G.N, G.heads, G.P, G.Vt, G.k, G.sink, G.select, G.coarse, (double)G.tau,
+                 g != nullptr, rc);
+  }
+  return rc;
+}
+
+}  // namespace
+
+extern "C" int vsa_forward(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                           const void* g, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return forward_common(plan, q, k, v, g, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int vsa_forward_timed(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                                 const void* g, void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream, vsa_timer* timer) {
+  if (timer == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  return forward_common(plan, q, k, v, g, o, workspace, workspace_bytes, stream, timer);
+}
+
+extern "C" int vsa_read_stats(const vsa_plan* plan, const void* workspace, void* stream,
+                              vsa_stats* out) {
+  if (plan == nullptr || workspace == nullptr || out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  const VsaGeom& G = plan->g;
+  const size_t n = (size_t)G.batch * G.heads * G.Qs;
+  std::vector<int> cnt(n);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n > 0) {
+    const char* ws = static_cast<const char*>(workspace);
+    if (hipMemcpyAsync(cnt.data(), ws + plan->ws.counts, n * sizeof(int), hipMemcpyDeviceToHost,
+                       st) != hipSuccess)
+      return VSA_ERR_HIP;
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return VSA_ERR_HIP;
+  const int64_t BH = (int64_t)G.batch * G.heads;
+  int64_t pairs = BH * G.n_dense * (int64_t)G.Tq, kept = 0;
+  for (size_t i = 0; i < n; ++i) {
+    pairs += cnt[i];
+    kept += cnt[i] - G.P;
+  }
+  out->executed_pairs = pairs;
+  out->dense_pairs = BH * (int64_t)G.Tq * G.Tq;
+  out->sparse_rows = BH * G.Qs;
+  out->dense_rows = BH * G.n_dense;
+  out->kept_video_tiles = kept;
+  out->k = G.k;
+  out->reserved = 0;
+  return VSA_OK;
+}
+
+extern "C" int vsa_timer_create(vsa_timer** out) {
+  if (out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  *out = new (std::nothrow) vsa_timer();
+  return *out == nullptr ? VSA_ERR_NO_MEMORY : VSA_OK;
+}
+
+extern "C" int vsa_timer_destroy(vsa_timer* t) {
+  if (t == nullptr) return VSA_OK;
+  for (auto& r : t->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto e : t->pool) (void)hipEventDestroy(e);
+  delete t;
+  return VSA_OK;
+}
+
+namespace {
+int drain(vsa_timer* t) {
+  for (auto& r : t->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return VSA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return VSA_ERR_HIP;
+    t->total_ms[r.stage] += ms;
+    t->launches[r.stage] += 1;
+    t->pool.push_back(r.a);
+    t->pool.push_back(r.b);
+  }
+  t->recs.clear();
+  return VSA_OK;
+}
+}  // namespace
+
+extern "C" int vsa_timer_reset(vsa_timer* t) {
+  if (t == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  const int rc = drain(t);
+  for (auto& x : t->total_ms) x = 0.0;
+  for (auto& x : t->launches) x = 0;
+  return rc;
+}
+
+extern "C" int vsa_timer_read(vsa_timer* t, vsa_kernel_time* out, int max, int* n) {
+  if (t == nullptr || n == nullptr || (out == nullptr && max > 0)) return VSA_ERR_INVALID_ARGUMENT;
+  const int rc = drain(t);
+  if (rc != VSA_OK) return rc;
+  const int m = (int)t->names.size();
+  for (int i = 0; i < m && i < max; ++i) {
+    std::memset(out[i].name, 0, sizeof(out[i].name));
+    std::strncpy(out[i].name, t->names[i].c_str(), sizeof(out[i].name) - 1);
+    out[i].launches = t->launches[i];
+    out[i].total_ms = t->total_ms[i];
+  }
+  *n = m;
+  return VSA_OK;
+}

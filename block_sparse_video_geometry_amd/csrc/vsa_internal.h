@@ -1,0 +1,53 @@
+// Internal definitions shared by the host plan and the gfx950 kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "vsa.h"
+
+#define VSA_MAX_PREFIX_SEGS 16
+#define VSA_MAX_VIDEO_TILES 4096
+#define VSA_HEAD_DIM 128
+#define VSA_TILE_TOKENS 64
+#define VSA_COARSE_ROWS 32   // sparse rows per workgroup of the coarse-score kernel
+
+// Geometry and options of one plan, passed to every kernel by value.  Tile ids:
+// prefix tiles [0, P) in packed order, video tiles [P, P + Vt) raster (tt, th, tw).
+struct VsaGeom {
+  int32_t n_pre_segs;
+  int32_t pre_start[VSA_MAX_PREFIX_SEGS];  // packed start token of each prefix segment
+  int32_t pre_len[VSA_MAX_PREFIX_SEGS];
+  int32_t pre_tile0[VSA_MAX_PREFIX_SEGS + 1];  // first tile id of each prefix segment; [n] = P
+  int32_t vstart;                          // packed start of the video span
+  int32_t T, H, W;                         // video latent grid
+  int32_t tw_n, th_n;                      // W/4, H/4
+  int32_t P, Vt, Tq;
+  int32_t N, heads, batch;
+  int32_t n_dense;                         // dense query tiles per (batch, head): 0 or P
+  int32_t Qs;                              // sparse query tiles per (batch, head): Tq - n_dense
+  int32_t cap;                             // list capacity per sparse row
+  int32_t k;                               // TOPK keep count
+  int32_t sink, select, coarse;
+  float tau;
+  float scale;                             // softmax scale 1/sqrt(128)
+  int32_t coarse_blocks;                   // workgroups per (batch, head) of the score kernel
+};
+
+struct VsaLayout {        // byte offsets into the workspace
+  size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
+  size_t total;
+};
+
+struct vsa_plan {
+  VsaGeom g;
+  VsaLayout ws;
+  vsa_options opts;
+  float keep;
+  int64_t n_tokens;
+};
+
+// kernel launch sequence (defined in vsa_forward.hip)
+struct vsa_timer;
+int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                       const void* g, void* o, void* workspace, void* stream, vsa_timer* timer);

@@ -1,0 +1,39 @@
+// Host launchers of the gfx950 kernels (one translation unit per step).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "vsa_internal.h"
+
+// Geometry gather + mean pooling: qbar for every tile, kbar/vbar for video
+// tiles; writes bias = 0 when the coarse mode has no log-mass bias.
+void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void* v, float* qbar,
+                     float* kbar, float* vbar, float* bias, hipStream_t st);
+
+// Mean video query per (batch, head) (log-mass anchor).
+void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipStream_t st);
+
+// Log-mass bias per video key tile.
+void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
+                        float* bias, hipStream_t st);
+
+// Coarse logits S = s qbar kbar^T + bias of the sparse rows, and per-workgroup
+// (sum, sum of squares) partials for the tau statistics.
+void vsa_launch_scores(const VsaGeom& g, const float* qbar, const float* kbar, const float* bias,
+                       float* scores, double* statp, hipStream_t st);
+
+// Row softmax of S and O_coarse = P vbar.
+void vsa_launch_coarse_out(const VsaGeom& g, const float* scores, const float* vbar, float* ocoarse,
+                           hipStream_t st);
+
+// tau threshold mean + tau * std per (batch, head) from the partials.
+void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream_t st);
+
+// Per sparse row list of key tiles: prefix tiles, then selected video tiles.
+void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, int* lists,
+                       int* counts, hipStream_t st);
+
+// Block-sparse fine attention + gated combine, output in packed order.
+void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
+                     const float* ocoarse, const int* lists, const int* counts, void* o,
+                     hipStream_t st);

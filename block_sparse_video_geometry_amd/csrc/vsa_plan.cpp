@@ -1,0 +1,218 @@
+// Host-side plan: validates the packed layout and builds the tile geometry.
+//
+// Geometry mapper ("Ref2VA VSA : noeud d'attention sparse pour le Ref2VA H3",
+// "Le correctif d'attention a deux niveaux", item 1; "ComfyUI-Ref2VA-VSA",
+// "The Solution"): every conditioning segment (text, reference image,
+// reference audio) is cut into tiles of 64 consecutive tokens that hold no
+// other segment; the video span is cut into 4x4x4 tiles ("ComfyUI-Ref2VA-VSA",
+// "Technical Architecture").  The plan is a few scalars and at most 16
+// segments, so kernels take it by value; the library never allocates device
+// memory.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "vsa_internal.h"
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Seg {
+  int64_t start, length;
+  int32_t kind;
+};
+
+}  // namespace
+
+extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch, int video_T,
+                                 int video_H, int video_W, int heads, int head_dim,
+                                 float keep_percent, const vsa_options* opts, vsa_plan** out) {
+  if (out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (segs == nullptr || n_segs <= 0 || batch <= 0 || heads <= 0 || video_T <= 0 ||
+      video_H <= 0 || video_W <= 0 || head_dim <= 0)
+    return VSA_ERR_INVALID_ARGUMENT;
+  if (head_dim != VSA_HEAD_DIM) return VSA_ERR_UNSUPPORTED;
+  if (video_T % 4 || video_H % 4 || video_W % 4) return VSA_ERR_UNSUPPORTED;
+
+  vsa_options o{VSA_SINK_EXACT_KV, VSA_SELECT_TOPK, VSA_COARSE_MEAN, 0.0f};
+  if (opts != nullptr) o = *opts;
+  if (o.sink != VSA_SINK_EXACT_KV && o.sink != VSA_SINK_EXACT_KV_AND_ROWS)
+    return VSA_ERR_UNSUPPORTED;
+  if (o.select != VSA_SELECT_TOPK && o.select != VSA_SELECT_TAU) return VSA_ERR_UNSUPPORTED;
+  if (o.coarse != VSA_COARSE_MEAN && o.coarse != VSA_COARSE_MEAN_LOGMASS)
+    return VSA_ERR_UNSUPPORTED;
+  if (o.select == VSA_SELECT_TOPK && !(keep_percent > 0.0f && keep_percent <= 100.0f))
+    return VSA_ERR_UNSUPPORTED;
+  if (o.select == VSA_SELECT_TAU && !std::isfinite(o.tau)) return VSA_ERR_UNSUPPORTED;
+
+  // spans: sort by start, must partition [0, N)
+  std::vector<Seg> s;
+  s.reserve(n_segs);
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].start < 0 || segs[i].length <= 0) return VSA_ERR_INVALID_ARGUMENT;
+    if (segs[i].kind < VSA_SEG_TEXT || segs[i].kind > VSA_SEG_VIDEO)
+      return VSA_ERR_INVALID_ARGUMENT;
+    s.push_back({segs[i].start, segs[i].length, segs[i].kind});
+  }
+  std::sort(s.begin(), s.end(), [](const Seg& a, const Seg& b) { return a.start < b.start; });
+  int64_t pos = 0;
+  int n_video = 0, n_prefix = 0;
+  for (const Seg& x : s) {
+    if (x.start != pos) return VSA_ERR_INVALID_ARGUMENT;  // gap or overlap
+    pos += x.length;
+    if (x.kind == VSA_SEG_VIDEO) ++n_video; else ++n_prefix;
+  }
+  const int64_t N = pos;
+  if (n_video != 1) return VSA_ERR_UNSUPPORTED;
+  if (n_prefix > VSA_MAX_PREFIX_SEGS) return VSA_ERR_UNSUPPORTED;
+  // 32-bit token and element indexing inside the kernels
+  if (N * (int64_t)heads * VSA_HEAD_DIM >= ((int64_t)1 << 31)) return VSA_ERR_UNSUPPORTED;
+
+  vsa_plan* p = new (std::nothrow) vsa_plan();
+  if (p == nullptr) return VSA_ERR_NO_MEMORY;
+  VsaGeom& g = p->g;
+  std::memset(&g, 0, sizeof(g));
+  int tile = 0;
+  for (const Seg& x : s) {
+    if (x.kind == VSA_SEG_VIDEO) {
+      if (x.length != (int64_t)video_T * video_H * video_W) {
+        delete p;
+        return VSA_ERR_INVALID_ARGUMENT;
+      }
+      g.vstart = (int32_t)x.start;
+      continue;
+    }
+    g.pre_start[g.n_pre_segs] = (int32_t)x.start;
+    g.pre_len[g.n_pre_segs] = (int32_t)x.length;
+    g.pre_tile0[g.n_pre_segs] = tile;
+    tile += (int)((x.length + VSA_TILE_TOKENS - 1) / VSA_TILE_TOKENS);
+    ++g.n_pre_segs;
+  }
+  g.pre_tile0[g.n_pre_segs] = tile;
+  for (int i = g.n_pre_segs + 1; i <= VSA_MAX_PREFIX_SEGS; ++i) g.pre_tile0[i] = tile;
+  g.T = video_T;
+  g.H = video_H;
+  g.W = video_W;
+  g.tw_n = video_W / 4;
+  g.th_n = video_H / 4;
+  g.P = tile;
+  g.Vt = (video_T / 4) * (video_H / 4) * (video_W / 4);
+  if (g.Vt > VSA_MAX_VIDEO_TILES) {
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
+  g.Tq = g.P + g.Vt;
+  g.N = (int32_t)N;
+  g.heads = heads;
+  g.batch = batch;
+  g.n_dense = (o.sink == VSA_SINK_EXACT_KV_AND_ROWS) ? g.P : 0;
+  g.Qs = g.Tq - g.n_dense;
+  // k = ceil(keep * Vt / 100), clamped to [1, Vt]
+  if (o.select == VSA_SELECT_TOPK) {
+    int k = (int)std::ceil((double)keep_percent * g.Vt / 100.0 - 1e-9);
+    g.k = std::max(1, std::min(g.Vt, k));
+    g.cap = g.P + g.k;
+  } else {
+    g.k = 0;
+    g.cap = g.P + g.Vt;
+  }
+  g.sink = o.sink;
+  g.select = o.select;
+  g.coarse = o.coarse;
+  g.tau = o.tau;
+  g.scale = (float)(1.0 / std::sqrt((double)VSA_HEAD_DIM));
+  g.coarse_blocks = (g.Qs + VSA_COARSE_ROWS - 1) / VSA_COARSE_ROWS;
+
+  // workspace layout
+  const size_t BH = (size_t)batch * heads;
+  const size_t A = 256;
+  VsaLayout& L = p->ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), A);
+    return at;
+  };
+  L.qbar = take(BH * g.Tq * VSA_HEAD_DIM * 4);
+  L.kbar = take(BH * g.Vt * VSA_HEAD_DIM * 4);
+  L.vbar = take(BH * g.Vt * VSA_HEAD_DIM * 4);
+  L.bias = take(BH * g.Vt * 4);
+  L.anchor = take(BH * VSA_HEAD_DIM * 4);
+  L.scores = take(BH * (size_t)g.Qs * g.Vt * 4);
+  L.ocoarse = take(BH * (size_t)g.Qs * VSA_HEAD_DIM * 4);
+  L.thr = take(BH * 4);
+  L.lists = take(BH * (size_t)g.Qs * g.cap * 4);
+  L.counts = take(BH * (size_t)g.Qs * 4);
+  L.statp = take(BH * (size_t)g.coarse_blocks * 2 * 8);
+  L.total = off;
+
+  p->opts = o;
+  p->keep = keep_percent;
+  p->n_tokens = N;
+  *out = p;
+  return VSA_OK;
+}
+
+extern "C" int vsa_plan_workspace_bytes(const vsa_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  *bytes = plan->ws.total;
+  return VSA_OK;
+}
+
+extern "C" int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out) {
+  if (plan == nullptr || out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  const VsaGeom& g = plan->g;
+  out->batch = g.batch;
+  out->heads = g.heads;
+  out->head_dim = VSA_HEAD_DIM;
+  out->n_tokens = plan->n_tokens;
+  out->n_prefix_tiles = g.P;
+  out->n_video_tiles = g.Vt;
+  out->n_tiles = g.Tq;
+  out->k = g.k;
+  out->n_dense_rows = g.n_dense;
+  out->n_sparse_rows = g.Qs;
+  out->list_capacity = g.cap;
+  out->options = plan->opts;
+  out->keep_percent = plan->keep;
+  return VSA_OK;
+}
+
+extern "C" int vsa_debug_views(const vsa_plan* plan, vsa_debug* out) {
+  if (plan == nullptr || out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
+  const VsaLayout& L = plan->ws;
+  out->qbar = L.qbar;
+  out->kbar = L.kbar;
+  out->vbar = L.vbar;
+  out->bias = L.bias;
+  out->anchor = L.anchor;
+  out->scores = L.scores;
+  out->ocoarse = L.ocoarse;
+  out->thr = L.thr;
+  out->lists = L.lists;
+  out->counts = L.counts;
+  out->total_bytes = L.total;
+  return VSA_OK;
+}
+
+extern "C" int vsa_plan_destroy(vsa_plan* plan) {
+  delete plan;
+  return VSA_OK;
+}
+
+extern "C" const char* vsa_status_string(int status) {
+  switch (status) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_INVALID_ARGUMENT: return "VSA_ERR_INVALID_ARGUMENT";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+    case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
+    case VSA_ERR_HIP: return "VSA_ERR_HIP";
+    case VSA_ERR_NO_MEMORY: return "VSA_ERR_NO_MEMORY";
+    default: return "VSA_ERR_UNKNOWN";
+  }
+}

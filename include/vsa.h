@@ -1,0 +1,231 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) two-branch video sparse attention
+ * forward over a packed "conditioning prefix + video" token sequence.
+ *
+ * What the calls compute (pages cited by title and section):
+ *  - "Ref2VA VSA : noeud d'attention sparse pour le Ref2VA H3", section
+ *    "Le correctif d'attention a deux niveaux", items 1-3: a geometry mapper
+ *    puts text, reference-image and reference-audio tokens in tiles of their
+ *    own that top-k never prunes; top-k prunes only video key tiles; a gate
+ *    (to_gate_compress) scales the compressed branch.
+ *  - "ComfyUI-Ref2VA-VSA: Ultra-Fast Character Video Generation", sections
+ *    "Technical Architecture" and "The Solution": 4x4x4 spatio-temporal video
+ *    tiles; segment-pure prefix tiles that stay dense.
+ *  - "BSAI FastH3 Native VSA (recipe)", sections "The mechanism, briefly" and
+ *    "The inputs that matter": 64-token video blocks are scored and only the
+ *    top share runs exact attention; BF16 with head_dim 128; the patch needs
+ *    the packed segment layout; sink_conditioning exact_kv /
+ *    exact_kv_and_rows; ambiguous cases must not silently run dense.
+ *  - "ComfyUI Agrega Nodo Central de Atencion Dispersa y Compilador Comfy",
+ *    section "Atencion dispersa por bloques: un nodo, tres backends": each
+ *    query block goes to a chosen subset of key blocks; top-k at a fixed keep
+ *    share; Sol-Attn per-head threshold in sigmas of the score distribution;
+ *    VSA = cubic tiling plus a coarse compression branch.
+ *  - "Spark-H3: atencion dispersa por bloques acelera MiniMax-H3 en ComfyUI",
+ *    section "Que cambia Spark-Attn": an exact branch over the top-ranked
+ *    blocks and a compressed branch over mean-pooled summaries; a log-mass
+ *    bias anchored at the mean video query restores the mass that mean
+ *    pooling loses.
+ *
+ * Conventions for every call:
+ *  - Every function returns an int status: VSA_OK (0) or a negative
+ *    vsa_status.  Nothing aborts, throws or prints (unless the environment
+ *    variable VSA_LOG=1, which writes one line per forward to stderr).
+ *  - Device pointers are HIP device addresses on the current device.  The
+ *    caller owns every device buffer (inputs, output, workspace) and the
+ *    stream.  The library owns only the host-side plan.
+ *  - Streams are passed as void* holding a hipStream_t (NULL = null stream).
+ *
+ * Tensor layout (q, k, v, g, o): bf16, [batch, N, heads, 128] contiguous in
+ * packed token order, heads interleaved; 16-byte aligned.
+ *
+ * Tile numbering used by every output of the library: the P prefix tiles
+ * first (segments in packed order, 64 consecutive tokens per tile, the last
+ * tile of a segment possibly partial), then the Vt video tiles in raster
+ * order (tt, th, tw) over the (T/4, H/4, W/4) tile grid.  Inside a video tile
+ * the 64 tokens are raster (dt, dh, dw).  Video tokens are packed raster
+ * (t, h, w), w fastest.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad spans, negative sizes, aliasing */
+  VSA_ERR_UNSUPPORTED = -2,      /* outside what the kernels implement: head_dim != 128,
+                                    grid dims not multiples of 4, not exactly one video span,
+                                    keep outside (0, 100], > 4096 video tiles, > 16 prefix
+                                    segments, unknown mode, device not gfx950.  The caller
+                                    decides explicitly what to run instead. */
+  VSA_ERR_WORKSPACE = -3,        /* workspace pointer null or smaller than required */
+  VSA_ERR_HIP = -4,              /* a HIP runtime call or kernel launch failed */
+  VSA_ERR_NO_MEMORY = -5         /* host allocation of the plan failed */
+} vsa_status;
+
+typedef enum {
+  VSA_SEG_TEXT = 0,
+  VSA_SEG_REF_IMAGE = 1,
+  VSA_SEG_REF_AUDIO = 2,
+  VSA_SEG_OTHER_PREFIX = 3,
+  VSA_SEG_VIDEO = 4
+} vsa_seg_kind;
+
+/* One span of the packed token axis, [start, start + length). */
+typedef struct {
+  int64_t start;
+  int64_t length;
+  int32_t kind;    /* vsa_seg_kind */
+  int32_t reserved;
+} vsa_segment;
+
+/* sink_conditioning ("BSAI FastH3 Native VSA (recipe)", "The inputs that
+ * matter"): EXACT_KV keeps every prefix key tile in every query tile's list;
+ * EXACT_KV_AND_ROWS also runs prefix query tiles dense (all key tiles, no
+ * coarse term). */
+typedef enum { VSA_SINK_EXACT_KV = 1, VSA_SINK_EXACT_KV_AND_ROWS = 2 } vsa_sink;
+
+/* Video key tile selection: TOPK keeps the k = ceil(keep * Vt / 100) largest
+ * coarse logits of each sparse query tile (ties to the lowest video tile
+ * index); TAU keeps every video tile whose logit exceeds mean + tau * std of
+ * all the (sparse query tile, video key tile) logits of its (batch, head)
+ * (Sol-Attn, "un nodo, tres backends"). */
+typedef enum { VSA_SELECT_TOPK = 0, VSA_SELECT_TAU = 1 } vsa_select;
+
+/* Coarse logits: MEAN is s * qbar . kbar; MEAN_LOGMASS adds the per video
+ * tile bias b_j = log(mean_{t in j} exp(s q_a . (k_t - kbar_j))) with q_a the
+ * mean video query of the (batch, head) ("Que cambia Spark-Attn",
+ * Spark-Reweight).  s = 1/sqrt(128). */
+typedef enum { VSA_COARSE_MEAN = 0, VSA_COARSE_MEAN_LOGMASS = 1 } vsa_coarse;
+
+typedef struct {
+  int32_t sink;    /* vsa_sink */
+  int32_t select;  /* vsa_select */
+  int32_t coarse;  /* vsa_coarse */
+  float tau;       /* TAU mode threshold in standard deviations */
+} vsa_options;
+
+typedef struct vsa_plan vsa_plan; /* opaque, host-only, immutable after creation */
+
+/* Shape facts of a plan. */
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int64_t n_tokens;        /* N */
+  int32_t n_prefix_tiles;  /* P */
+  int32_t n_video_tiles;   /* Vt */
+  int32_t n_tiles;         /* Tq = P + Vt */
+  int32_t k;               /* video tiles kept per sparse row (TOPK); 0 in TAU mode */
+  int32_t n_dense_rows;    /* query tiles per (batch, head) that run dense */
+  int32_t n_sparse_rows;   /* query tiles per (batch, head) that select (Qs) */
+  int32_t list_capacity;   /* entries reserved per sparse row in the list buffer */
+  vsa_options options;
+  float keep_percent;
+} vsa_plan_desc;
+
+/* Counters of one forward ("BSAI FastH3 Native VSA (recipe)", "Where it goes
+ * wrong": read the stats and check sparse work is above zero). */
+typedef struct {
+  int64_t executed_pairs;   /* (query tile, key tile) pairs run by the fine branch, all (batch, head) */
+  int64_t dense_pairs;      /* pairs a dense run would execute: batch * heads * Tq * Tq */
+  int64_t sparse_rows;      /* sparse query tiles, all (batch, head) */
+  int64_t dense_rows;       /* dense query tiles, all (batch, head) */
+  int64_t kept_video_tiles; /* video key tiles kept over all sparse rows */
+  int32_t k;                /* as in vsa_plan_desc */
+  int32_t reserved;
+} vsa_stats;
+
+/* Byte offsets into the workspace of the intermediates of the last forward
+ * that used it (all row-major, fp32 unless noted):
+ *   qbar  [batch, heads, Tq, 128]   mean of the valid Q tokens of each tile
+ *   kbar  [batch, heads, Vt, 128]   mean K of each video tile
+ *   vbar  [batch, heads, Vt, 128]   mean V of each video tile
+ *   bias  [batch, heads, Vt]        log-mass bias (zeros in MEAN mode)
+ *   anchor[batch, heads, 128]       mean video query (LOGMASS mode only)
+ *   scores[batch, heads, Qs, Vt]    coarse logits of the sparse rows
+ *   ocoarse[batch, heads, Qs, 128]  coarse output of the sparse rows
+ *   thr   [batch, heads]            TAU threshold (TAU mode only)
+ *   lists [batch, heads, Qs, list_capacity] int32 tile ids (prefix ascending, then video ascending)
+ *   counts[batch, heads, Qs]        int32 valid entries of each list
+ * Sparse row s of a (batch, head) is query tile s + n_dense_rows. */
+typedef struct {
+  size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts;
+  size_t total_bytes;
+} vsa_debug;
+
+/* Build the plan for one packed layout ("BSAI FastH3 Native VSA (recipe)",
+ * "The mechanism, briefly": the patch reads where the video span starts and
+ * ends).  segs: n_segs spans that must partition [0, N) (any order; sorted by
+ * start inside), exactly one of kind VSA_SEG_VIDEO with length
+ * video_T * video_H * video_W, each dim a multiple of 4, at most 16 prefix
+ * spans.  keep_percent in (0, 100] is used in TOPK mode.  opts may be NULL
+ * ({EXACT_KV, TOPK, MEAN}).  On success *out owns a new plan (free with
+ * vsa_plan_destroy); on error *out is NULL.  Host only, no device work. */
+int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch, int video_T, int video_H,
+                      int video_W, int heads, int head_dim, float keep_percent,
+                      const vsa_options* opts, vsa_plan** out);
+
+/* Bytes of device workspace vsa_forward needs for this plan. */
+int vsa_plan_workspace_bytes(const vsa_plan* plan, size_t* bytes);
+
+/* Shape facts of the plan. */
+int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out);
+
+/* Enqueue the whole forward on `stream`: geometry gather + mean pooling,
+ * [anchor + log-mass bias], coarse logits, coarse softmax + O_coarse,
+ * [tau statistics], selection, block-sparse fine attention with the gated
+ * combine O = O_fine + G * O_coarse written in packed order.
+ * q, k, v, o: [batch, N, heads, 128] bf16 device buffers; g: same shape or
+ * NULL (no coarse term in O).  o must not overlap q, k, v, g or the
+ * workspace.  workspace: >= vsa_plan_workspace_bytes, 256-byte aligned,
+ * device memory the call may overwrite.  Arguments are checked before
+ * anything is enqueued; the call returns without waiting for the GPU.
+ * Deterministic: the same inputs give bitwise the same o. */
+int vsa_forward(const vsa_plan* plan, const void* q, const void* k, const void* v, const void* g,
+                void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Counters of the last forward that used `workspace` (reads the list counts
+ * back; synchronises `stream`). */
+int vsa_read_stats(const vsa_plan* plan, const void* workspace, void* stream, vsa_stats* out);
+
+/* Offsets of the intermediates inside the workspace (host only). */
+int vsa_debug_views(const vsa_plan* plan, vsa_debug* out);
+
+int vsa_plan_destroy(vsa_plan* plan);
+
+/* Static string for a status code (never NULL). */
+const char* vsa_status_string(int status);
+
+/* ---- kernel timing for measurement -------------------------------------
+ * A timer records a HIP event pair around every kernel that
+ * vsa_forward_timed enqueues, on the same stream, and sums the elapsed times
+ * per kernel.  Not thread-safe; one timer per stream. */
+typedef struct vsa_timer vsa_timer;
+
+typedef struct {
+  char name[32];       /* kernel name */
+  int32_t launches;    /* launches recorded since the last reset */
+  double total_ms;     /* summed event-to-event time */
+} vsa_kernel_time;
+
+int vsa_timer_create(vsa_timer** out);
+int vsa_timer_destroy(vsa_timer* timer);
+int vsa_timer_reset(vsa_timer* timer);
+/* Same as vsa_forward, plus event records around each kernel. */
+int vsa_forward_timed(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                      const void* g, void* o, void* workspace, size_t workspace_bytes,
+                      void* stream, vsa_timer* timer);
+/* Waits for the recorded events, then fills up to `max` entries (one per
+ * kernel name) and sets *n to their number. */
+int vsa_timer_read(vsa_timer* timer, vsa_kernel_time* out, int max, int* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

@@ -64,7 +64,8 @@ the design notes):
   * ranking uses the logit S (scale and bias included), ties go to the
     lowest video tile index;
   * tau statistics: per (batch, head), population mean and std (two-pass)
-    over every (sparse query tile, video key tile) logit; keep S > thr;
+    over every (sparse query tile, video key tile) logit; keep S > thr; a
+    row whose list ends up empty has a zero fine output;
   * log-mass bias b_j = log(mean_t exp(l_t - p_j)) with l_t = s q_a . k_t,
     p_j = s q_a . kbar_j and q_a the mean of all video queries.
 """
@@ -270,8 +271,12 @@ def row_list(geom: Geometry, video_sel) -> np.ndarray:
 def fine_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry,
              qtile: int, key_tiles, scale: float) -> np.ndarray:
     """Exact softmax attention of the valid queries of one query tile over the
-    valid tokens of the listed key tiles.  Returns [n_valid, D]."""
+    valid tokens of the listed key tiles.  Returns [n_valid, D].  An empty
+    list (possible only with no prefix and nothing above the tau threshold)
+    attends to nothing and gives zeros."""
     rows = geom.tiles[qtile]
+    if len(key_tiles) == 0:
+        return np.zeros((len(rows), Q.shape[1]))
     keys = np.concatenate([geom.tiles[t] for t in key_tiles])
     z = scale * (Q[rows] @ K[keys].T)
     z = z - z.max(axis=1, keepdims=True)

@@ -1,0 +1,150 @@
+"""Compare the HIP path's results with the fp64 oracle.
+
+Selections: per (batch, head, sparse query tile) let S(k) and S(k+1) be the
+oracle's k-th and (k+1)-th largest coarse logits.  Where S(k) - S(k+1) > GAP
+the GPU list must equal the oracle's.  Elsewhere the GPU list must be a
+valid top-k within GAP (size P + k, every prefix tile, every kept logit
+>= S(k) - GAP, every dropped logit <= S(k+1) + GAP); the oracle then adopts
+the GPU's list for that row before the outputs are compared.  Tau mode: the
+GPU must agree wherever |S - thr| > GAP and its choice is adopted elsewhere.
+
+Outputs, over every valid element produced: max |O_gpu - O_ref| <= 2e-2 and
+||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2 (bf16 inputs, fp32 accumulation,
+bf16 output).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import vsa_oracle as O
+
+GAP = 1e-4
+TOL_ABS = 2e-2
+TOL_REL = 1e-2
+
+
+def bits_to_f64(b):
+    return O.bf16_bits_to_f64(b)
+
+
+def gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar", "vbar",
+                                              "bias", "ocoarse", "thr", "anchor")):
+    """Copy the output and the workspace intermediates to host numpy arrays."""
+    import torch
+    from block_sparse_video_geometry_amd import debug_tensor
+    res = {"o": o.view(torch.int16).cpu().numpy().view(np.uint16)}
+    for f in fields:
+        res[f] = debug_tensor(plan, ws, f).cpu().numpy()
+    return res
+
+
+def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol_rel=TOL_REL,
+                 check_intermediates=True):
+    """Raise AssertionError on a mismatch; return a report dict.
+
+    w: workload, x: input bit arrays, gpu: dict from gpu_results_to_numpy.
+    heads: (b, h) pairs to check (None = all); rows: query tile ids (None = all)."""
+    geom = O.map_geometry(w.segments(), *w.grid)
+    sparse, dense = O.row_classes(geom, w.sink)
+    n_dense = len(dense)
+    P = geom.n_prefix
+    B, N, H, D = x["q"].shape
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    rep = dict(rows=0, exact_rows=0, adopted_rows=0, max_abs=0.0, err2=0.0, ref2=0.0,
+               max_s_err=0.0, max_pool_err=0.0, max_oc_err=0.0, max_bias_err=0.0, s_mag=1.0,
+               bias_mag=1.0)
+    g_all = x.get("g")
+    for b, h in heads:
+        Q, K, V = (bits_to_f64(x[n][b, :, h]) for n in "qkv")
+        G = bits_to_f64(g_all[b, :, h]) if g_all is not None else None
+        _, it = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                               rows=rows, want_intermediates=True)
+        need = it["sparse_rows"]
+        S_ref = it["S"]
+        if S_ref.size:
+            rep["s_mag"] = max(rep["s_mag"], float(np.abs(S_ref).max()))
+        rep["bias_mag"] = max(rep["bias_mag"], float(np.abs(it["bias"]).max()))
+        if check_intermediates:
+            kb = gpu["kbar"][b, h].astype(np.float64)
+            vb = gpu["vbar"][b, h].astype(np.float64)
+            rep["max_pool_err"] = max(rep["max_pool_err"], np.abs(kb - it["Kbar"]).max(),
+                                      np.abs(vb - it["Vbar"]).max())
+            if need:
+                qb = gpu["qbar"][b, h][np.asarray(need)].astype(np.float64)
+                rep["max_pool_err"] = max(rep["max_pool_err"], np.abs(qb - it["Qbar"]).max())
+                oc = gpu["ocoarse"][b, h][np.asarray(need) - n_dense].astype(np.float64)
+                rep["max_oc_err"] = max(rep["max_oc_err"], np.abs(oc - it["Oc"]).max())
+            rep["max_bias_err"] = max(rep["max_bias_err"],
+                                      np.abs(gpu["bias"][b, h].astype(np.float64) - it["bias"]).max())
+        override = {}
+        for n_i, i in enumerate(need):
+            if rows is not None and i not in set(rows):
+                continue
+            s = i - n_dense
+            srow_ref = S_ref[n_i]
+            srow_gpu = gpu["scores"][b, h, s].astype(np.float64)
+            rep["max_s_err"] = max(rep["max_s_err"], np.abs(srow_gpu - srow_ref).max())
+            cnt = int(gpu["counts"][b, h, s])
+            glist = gpu["lists"][b, h, s, :cnt].astype(np.int64)
+            olist = it["lists"][i]
+            assert list(glist[:P]) == list(range(P)), f"(b{b},h{h},tile {i}) prefix tiles missing"
+            gvid = glist[P:] - P
+            assert np.all(np.diff(gvid) > 0), f"(b{b},h{h},tile {i}) list not ascending"
+            assert gvid.size == 0 or (gvid.min() >= 0 and gvid.max() < geom.n_video)
+            if w.select == O.SELECT_TOPK:
+                k = it["k"]
+                assert cnt == P + k, f"(b{b},h{h},tile {i}) count {cnt} != {P + k}"
+                srt = np.sort(srow_ref)[::-1]
+                sk = srt[k - 1]
+                sk1 = srt[k] if k < len(srt) else -np.inf
+                if sk - sk1 > gap:
+                    assert np.array_equal(glist, olist), \
+                        f"(b{b},h{h},tile {i}) selection differs at gap {sk - sk1:.3g}"
+                    rep["exact_rows"] += 1
+                else:
+                    sel = np.zeros(geom.n_video, bool)
+                    sel[gvid] = True
+                    assert np.all(srow_ref[sel] >= sk - gap), f"(b{b},h{h},tile {i}) weak pick"
+                    assert np.all(srow_ref[~sel] <= sk1 + gap), f"(b{b},h{h},tile {i}) weak drop"
+                    override[i] = glist
+                    rep["adopted_rows"] += 1
+            else:
+                thr = it["thr"]
+                sel = np.zeros(geom.n_video, bool)
+                sel[gvid] = True
+                clear = np.abs(srow_ref - thr) > gap
+                assert np.array_equal(sel[clear], (srow_ref > thr)[clear]), \
+                    f"(b{b},h{h},tile {i}) tau selection differs away from the threshold"
+                if np.array_equal(glist, olist):
+                    rep["exact_rows"] += 1
+                else:
+                    override[i] = glist
+                    rep["adopted_rows"] += 1
+        if override:
+            Oref, _ = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                                     rows=rows, list_override=override)
+        else:
+            Oref, _ = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                                     rows=rows)
+        row_ids = range(geom.n_tiles) if rows is None else rows
+        toks = np.concatenate([geom.tiles[i] for i in row_ids])
+        og = bits_to_f64(gpu["o"][b, toks, h])
+        orf = Oref[toks]
+        assert np.all(np.isfinite(og)), f"(b{b},h{h}) non-finite GPU output"
+        diff = og - orf
+        rep["max_abs"] = max(rep["max_abs"], float(np.abs(diff).max()))
+        rep["err2"] += float((diff ** 2).sum())
+        rep["ref2"] += float((orf ** 2).sum())
+        rep["rows"] += len(list(row_ids))
+    rep["rel_l2"] = (rep["err2"] / rep["ref2"]) ** 0.5 if rep["ref2"] > 0 else 0.0
+    assert rep["max_abs"] <= tol_abs, f"max abs error {rep['max_abs']:.3g} > {tol_abs}"
+    assert rep["rel_l2"] <= tol_rel, f"relative L2 error {rep['rel_l2']:.3g} > {tol_rel}"
+    if check_intermediates:
+        # fp32 dot products of length 128 on pooled values: ~1e-6 relative to the logit size
+        assert rep["max_s_err"] < 1e-5 * rep["s_mag"], f"coarse logits differ by {rep['max_s_err']:.3g}"
+        assert rep["max_pool_err"] < 1e-5, f"pooled means differ by {rep['max_pool_err']:.3g}"
+        assert rep["max_oc_err"] < 1e-4, f"O_coarse differs by {rep['max_oc_err']:.3g}"
+        assert rep["max_bias_err"] < 1e-5 * rep["bias_mag"], \
+            f"log-mass bias differs by {rep['max_bias_err']:.3g}"
+    return rep

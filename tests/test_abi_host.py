@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, plan validation
+status codes, plan shapes against the oracle's geometry, workspace layout."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import block_sparse_video_geometry_amd as V
+from block_sparse_video_geometry_amd import vsa as VB
+from oracle import vsa_oracle as O
+from workloads.synth import WORKLOADS
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "vsa.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(VB._LIB_PATH))
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in vsa.h but not exported"
+    assert set(names) == set(VB.EXPORTS)
+
+
+def test_status_strings():
+    for code, name in [(0, "VSA_OK"), (-1, "VSA_ERR_INVALID_ARGUMENT"), (-2, "VSA_ERR_UNSUPPORTED"),
+                       (-3, "VSA_ERR_WORKSPACE"), (-4, "VSA_ERR_HIP"), (-5, "VSA_ERR_NO_MEMORY")]:
+        assert V.vsa_status_string(code) == name
+    assert V.vsa_status_string(7) == "VSA_ERR_UNKNOWN"
+
+
+GOOD = [(0, 64, 0), (64, 64, 1), (128, 1024, 4)]
+
+
+def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw):
+    try:
+        V.vsa_plan_geometry(segs, batch, T, H, W, heads, hd, keep, **kw)
+        return 0
+    except V.VsaError as e:
+        return e.status
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(segs=GOOD), 0),
+    (dict(segs=list(reversed(GOOD))), 0),                            # any order
+    (dict(segs=[(0, 64, 0), (70, 58, 1), (128, 1024, 4)]), -1),       # gap
+    (dict(segs=[(0, 70, 0), (64, 64, 1), (128, 1024, 4)]), -1),       # overlap
+    (dict(segs=[(0, 0, 0), (0, 128, 1), (128, 1024, 4)]), -1),        # empty span
+    (dict(segs=[(-1, 65, 0), (64, 64, 1), (128, 1024, 4)]), -1),      # negative start
+    (dict(segs=[(0, 64, 0), (64, 64, 9), (128, 1024, 4)]), -1),       # unknown kind
+    (dict(segs=[(0, 64, 0), (64, 1000, 4)]), -1),                     # video length != T*H*W
+    (dict(segs=[(0, 128, 0)]), -2),                                   # no video span
+    (dict(segs=[(0, 1024, 4), (1024, 1024, 4)]), -2),                 # two video spans
+    (dict(segs=GOOD, hd=64), -2),                                     # head_dim
+    (dict(segs=[(0, 128, 0), (128, 5 * 16 * 16, 4)], T=5), -2),       # grid not multiple of 4
+    (dict(segs=GOOD, keep=0.0), -2),
+    (dict(segs=GOOD, keep=100.5), -2),
+    (dict(segs=GOOD, keep=float("nan")), -2),
+    (dict(segs=GOOD, keep=0.0, select=1, tau=1.0), 0),                # keep unused in tau mode
+    (dict(segs=GOOD, select=1, tau=float("inf")), -2),
+    (dict(segs=GOOD, sink=3), -2),
+    (dict(segs=GOOD, select=2), -2),
+    (dict(segs=GOOD, coarse=5), -2),
+    (dict(segs=GOOD, heads=0), -1),
+    (dict(segs=GOOD, batch=0), -1),
+    (dict(segs=[(i * 4, 4, 0) for i in range(17)] + [(68, 1024, 4)]), -2),   # > 16 prefix spans
+    (dict(segs=[(0, 64, 0), (64, 4 * 4 * 4 * 64 * 65, 4)], T=4, H=256, W=260), -2),  # > 4096 video tiles
+])
+def test_plan_validation(case, expect):
+    assert plan_status(**case) == expect
+
+
+def test_null_options_defaults():
+    p = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0, use_options=False)
+    o = p.desc.options
+    assert (o.sink, o.select, o.coarse) == (V.VSA_SINK_EXACT_KV, V.VSA_SELECT_TOPK, V.VSA_COARSE_MEAN)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_shapes_match_oracle_geometry(name):
+    w = WORKLOADS[name]
+    p = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128,
+                            w.keep if w.keep > 0 else 100.0, sink=w.sink, select=w.select,
+                            coarse=w.coarse, tau=w.tau)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    sparse, dense = O.row_classes(geom, w.sink)
+    d = p.desc
+    assert d.n_prefix_tiles == geom.n_prefix
+    assert d.n_video_tiles == geom.n_video
+    assert d.n_tiles == geom.n_tiles
+    assert d.n_dense_rows == len(dense) and d.n_sparse_rows == len(sparse)
+    assert d.n_tokens == w.n_tokens
+    if w.select == V.VSA_SELECT_TOPK:
+        assert d.k == O.keep_count(w.keep, geom.n_video)
+        assert d.list_capacity == geom.n_prefix + d.k
+    else:
+        assert d.list_capacity == geom.n_tiles
+
+
+def test_workspace_layout():
+    w = WORKLOADS["full_tau_1.0"]
+    p = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, 100.0, sink=w.sink,
+                            select=w.select, tau=w.tau)
+    dbg = p.debug
+    d = p.desc
+    B, H, Tq, Vt, Qs, cap = 1, d.heads, d.n_tiles, d.n_video_tiles, d.n_sparse_rows, d.list_capacity
+    sizes = {"qbar": B * H * Tq * 512, "kbar": B * H * Vt * 512, "vbar": B * H * Vt * 512,
+             "bias": B * H * Vt * 4, "anchor": B * H * 512, "scores": B * H * Qs * Vt * 4,
+             "ocoarse": B * H * Qs * 512, "thr": B * H * 4, "lists": B * H * Qs * cap * 4,
+             "counts": B * H * Qs * 4}
+    spans = sorted((getattr(dbg, n), getattr(dbg, n) + s) for n, s in sizes.items())
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    for n in sizes:
+        assert getattr(dbg, n) % 256 == 0
+    assert spans[-1][1] <= dbg.total_bytes == p.workspace_bytes
+
+
+def test_forward_rejects_before_touching_the_gpu():
+    """Null pointers and a missing workspace are caught on the host."""
+    lib = VB._lib
+    p = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0)
+    rc = lib.vsa_forward(p.handle, None, None, None, None, None, None, 0, None)
+    assert rc == V.VSA_ERR_INVALID_ARGUMENT
+    fake = ctypes.c_void_p(1 << 40)
+    rc = lib.vsa_forward(p.handle, fake, fake, fake, None, fake, None, 0, None)
+    assert rc == V.VSA_ERR_WORKSPACE
+    rc = lib.vsa_forward(None, fake, fake, fake, None, fake, fake, 1 << 30, None)
+    assert rc == V.VSA_ERR_INVALID_ARGUMENT
+    st = VB.vsa_stats()
+    assert lib.vsa_read_stats(None, None, None, ctypes.byref(st)) == V.VSA_ERR_INVALID_ARGUMENT

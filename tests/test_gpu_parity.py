@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads run in the
+launch configuration the benchmark times and are compared on sampled
+(batch, head, query tile) rows plus properties that hold at any size.
+"""
+import functools
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import parity as PAR
+from oracle import vsa_oracle as O
+from workloads.synth import (WORKLOADS, Workload, make_inputs, scaled_down, SEG_TEXT,
+                             SEG_REF_IMAGE, SEG_REF_AUDIO, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS,
+                             SELECT_TOPK, SELECT_TAU, COARSE_MEAN, COARSE_MEAN_LOGMASS)
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import block_sparse_video_geometry_amd as V
+    return V
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_gpu(w, x, use_gate=True):
+    V = _lib()
+    print(f"[gpu] {w.name} heads={w.heads} grid={w.grid} keep={w.keep} sink={w.sink} "
+          f"select={w.select} coarse={w.coarse} tau={w.tau}", flush=True)
+    plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128, w.keep if w.keep > 0 else 100.0,
+                               sink=w.sink, select=w.select, coarse=w.coarse, tau=w.tau)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    g = to_dev(x["g"]) if (use_gate and x.get("g") is not None) else None
+    o = torch.empty_like(q)
+    ws = V.alloc_workspace(plan)
+    V.vsa_forward(plan, q, k, v, g, o, ws)
+    torch.cuda.synchronize()
+    return plan, ws, o, (q, k, v, g)
+
+
+FULL_SMALL_GRID = (8, 24, 44)
+SMALL_CASES = [
+    WORKLOADS["tiny"],
+    WORKLOADS["mid"],
+    scaled_down(WORKLOADS["full"], heads=3, grid=FULL_SMALL_GRID, name="full_small"),
+    scaled_down(WORKLOADS["full_smooth_20"], heads=2, grid=FULL_SMALL_GRID, name="smooth20_small"),
+    scaled_down(WORKLOADS["full_smooth_100"], heads=2, grid=FULL_SMALL_GRID, name="smooth100_small"),
+    scaled_down(WORKLOADS["full_tau_1.0"], heads=2, grid=FULL_SMALL_GRID, name="tau1_small"),
+    scaled_down(WORKLOADS["full_tau_1.5"], heads=2, grid=FULL_SMALL_GRID, name="tau15_small"),
+    scaled_down(WORKLOADS["full_tau_2.0"], heads=2, grid=FULL_SMALL_GRID, name="tau2_small"),
+    scaled_down(WORKLOADS["full_logmass"], heads=2, grid=FULL_SMALL_GRID, name="logmass_small"),
+    # ragged prefix tiles, video span first, exact_kv rows, odd head count
+    Workload("ragged_video_first", 3, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 64), (SEG_REF_AUDIO, 30)),
+             (8, 12, 16), 20.0, SINK_EXACT_KV, seed=71, recipe="scaled", video_first=True),
+    Workload("ragged_rows", 2, ((SEG_TEXT, 77), (SEG_REF_AUDIO, 129)), (4, 16, 20), 15.0,
+             SINK_EXACT_KV_AND_ROWS, seed=72, recipe="iid"),
+    Workload("no_prefix", 2, (), (8, 8, 16), 25.0, SINK_EXACT_KV, seed=73, recipe="scaled"),
+    Workload("no_prefix_rows", 1, (), (4, 8, 8), 50.0, SINK_EXACT_KV_AND_ROWS, seed=74),
+    Workload("keep_one_tile", 2, ((SEG_TEXT, 64),), (8, 8, 8), 0.5, SINK_EXACT_KV, seed=75,
+             recipe="scaled"),
+    Workload("keep_all", 2, ((SEG_TEXT, 40),), (4, 8, 12), 100.0, SINK_EXACT_KV, seed=76),
+    Workload("batch2", 2, ((SEG_TEXT, 64), (SEG_REF_IMAGE, 128)), (4, 8, 16), 25.0,
+             SINK_EXACT_KV_AND_ROWS, seed=77, recipe="scaled", batch=2),
+    Workload("one_video_tile", 1, ((SEG_TEXT, 10),), (4, 4, 4), 100.0, SINK_EXACT_KV, seed=78),
+    Workload("tau_logmass", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 64)), (8, 16, 16), 0.0,
+             SINK_EXACT_KV, SELECT_TAU, COARSE_MEAN_LOGMASS, 1.5, seed=79, recipe="offset"),
+    Workload("smooth_gate_rows", 4, ((SEG_TEXT, 128), (SEG_REF_IMAGE, 256)), (8, 16, 24), 10.0,
+             SINK_EXACT_KV_AND_ROWS, seed=80, recipe="smooth"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=[w.name for w in SMALL_CASES])
+def test_parity_small(w):
+    x = make_inputs(w)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[parity] {w.name}: rows={rep['rows']} exact={rep['exact_rows']} adopted={rep['adopted_rows']} "
+          f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e} s_err={rep['max_s_err']:.2e}",
+          flush=True)
+
+
+def test_parity_no_gate():
+    w = scaled_down(WORKLOADS["full"], heads=2, grid=(8, 16, 16), name="nogate")
+    x = make_inputs(w)
+    plan, ws, o, _ = run_gpu(w, x, use_gate=False)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    PAR.check_parity(w, dict(x, g=None), gpu)
+
+
+def test_deterministic_and_stats():
+    V = _lib()
+    w = scaled_down(WORKLOADS["full"], heads=2, grid=FULL_SMALL_GRID, name="det")
+    x = make_inputs(w)
+    plan, ws, o, (q, k, v, g) = run_gpu(w, x)
+    o2 = torch.empty_like(o)
+    V.vsa_forward(plan, q, k, v, g, o2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    st = V.vsa_read_stats(plan, ws)
+    d = plan.desc
+    P, Vt, Tq, kk = d.n_prefix_tiles, d.n_video_tiles, d.n_tiles, d.k
+    exp_pairs = w.heads * (Vt * (P + kk) + P * Tq)
+    assert st["executed_pairs"] == exp_pairs
+    assert st["dense_pairs"] == w.heads * Tq * Tq
+    assert st["kept_video_tiles"] == w.heads * Vt * kk
+    assert 0 < st["executed_pairs"] < st["dense_pairs"]
+
+
+def test_abi_errors_on_device():
+    V = _lib()
+    w = WORKLOADS["tiny"]
+    x = make_inputs(w)
+    plan = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, w.keep)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    o = torch.empty_like(q)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(V.VsaError) as e:
+        V.vsa_forward(plan, q, k, v, None, o, small)
+    assert e.value.status == V.VSA_ERR_WORKSPACE
+    ws = V.alloc_workspace(plan)
+    with pytest.raises(V.VsaError) as e:
+        V.vsa_forward(plan, q, k, v, None, q, ws)   # output aliases an input
+    assert e.value.status == V.VSA_ERR_INVALID_ARGUMENT
+    V.vsa_forward(plan, q, k, v, None, o, ws)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- full size
+@functools.lru_cache(maxsize=1)
+def _inputs_for_seed(name):
+    return make_inputs(WORKLOADS[name])
+
+
+FULL_CASES = ["full", "full_smooth_20", "full_smooth_100", "full_tau_1.0", "full_tau_1.5",
+              "full_tau_2.0", "full_logmass"]
+
+
+@pytest.mark.parametrize("name", FULL_CASES)
+def test_parity_full_size_sampled(name):
+    w = WORKLOADS[name]
+    # workloads that share a seed share their inputs
+    src = {"full_smooth_100": "full_smooth_20", "full_tau_1.5": "full_tau_1.0",
+           "full_tau_2.0": "full_tau_1.0", "full_logmass": "full_tau_1.0"}.get(name, name)
+    x = _inputs_for_seed(src)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar",
+                                                          "vbar", "bias", "ocoarse", "thr"))
+    d = plan.desc
+    P, Tq = d.n_prefix_tiles, d.n_tiles
+    # properties over every row
+    cnt = gpu["counts"]
+    if w.select == SELECT_TOPK:
+        assert np.all(cnt == P + d.k)
+    else:
+        assert np.all((cnt >= P) & (cnt <= Tq))
+    lists = gpu["lists"]
+    assert np.all(lists[..., :P] == np.arange(P))
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    heads = [(0, 0), (0, int(rng.integers(1, w.heads)))]
+    rows = sorted(set([0, P - 1, P, Tq - 1] + [int(r) for r in rng.integers(0, Tq, size=4)]))
+    rep = PAR.check_parity(w, x, gpu, heads=heads, rows=rows)
+    print(f"[parity-full] {name}: rows={rep['rows']} exact={rep['exact_rows']} adopted={rep['adopted_rows']} "
+          f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e}", flush=True)
