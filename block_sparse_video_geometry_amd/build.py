@@ -1,6 +1,8 @@
 """Build libvsa.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m block_sparse_video_geometry_amd.build [--jobs N]
+    python block_sparse_video_geometry_amd/build.py [--jobs N]
+
+(run by path: importing the package loads the library this script builds)
 
 Objects go to _build/ at the repository root; the library to
 block_sparse_video_geometry_amd/_lib/libvsa.so.  Always recompiles.
@@ -32,15 +34,17 @@ COMMON = [
 ]
 SOURCES = ["vsa_plan.cpp", "vsa_forward.hip", "k_pool.hip", "k_coarse.hip", "k_select.hip",
            "k_fine.hip"]
+# Per-file extras.  The fine kernel never sees a NaN (finite inputs; masked logits are -inf),
+# so fmaxf needs no quieting of signalling NaNs.
+EXTRA = {"k_fine.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> Path:
     obj = BUILD / (src + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", str(CSRC / src), "-o", str(obj)]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "c++"] + [c for c in COMMON if not c.startswith("--offload")] + \
               ["-c", str(CSRC / src), "-o", str(obj)]
-        cmd = [c for c in cmd]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

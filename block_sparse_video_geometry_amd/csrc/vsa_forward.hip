@@ -21,16 +21,27 @@ bool log_enabled() {
   return on != 0;
 }
 
+// Text of the last HIP failure seen by this thread (step and HIP error name).
+thread_local char g_last_error[160] = "";
+
+int hip_fail(const char* step, hipError_t e) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", step, hipGetErrorName(e),
+                hipGetErrorString(e));
+  return VSA_ERR_HIP;
+}
+
 // 1 = gfx950, -1 = other, 0 = not yet checked (per device ordinal)
 int g_arch_ok[64];
 
 int check_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return VSA_ERR_HIP;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
   if (dev < 0 || dev >= 64) return VSA_ERR_UNSUPPORTED;
   if (g_arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VSA_ERR_HIP;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
     g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
   }
   return g_arch_ok[dev] == 1 ? VSA_OK : VSA_ERR_UNSUPPORTED;
@@ -46,6 +57,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
+
+extern "C" const char* vsa_last_error(void) { return g_last_error; }
 
 struct vsa_timer {
   struct Rec {
@@ -118,11 +131,12 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   int rc = VSA_OK;
-#define VSA_STEP(name, call)                                  \
-  do {                                                        \
-    rc = timed(tm, name, st, [&] { call; });                  \
-    if (rc != VSA_OK) return rc;                              \
-    if (hipGetLastError() != hipSuccess) return VSA_ERR_HIP;  \
+#define VSA_STEP(name, call)                                   \
+  do {                                                         \
+    rc = timed(tm, name, st, [&] { call; });                   \
+    if (rc != VSA_OK) return rc;                               \
+    const hipError_t e_ = hipGetLastError();                   \
+    if (e_ != hipSuccess) return hip_fail(name, e_);           \
   } while (0)
 
   VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
@@ -163,9 +177,9 @@ int forward_common(const vsa_plan* plan, const void* q, const void* k, const voi
     const VsaGeom& G = plan->g;
     std::fprintf(stderr,
                  "[vsa] forward B=%d N=%d heads=%d P=%d Vt=%d k=%d sink=%d select=%d coarse=%d "
-                 "tau=%g gate=%d status=%d\n",
+                 "tau=%g gate=%d status=%d %s\n",
                  G.batch, G.N, G.heads, G.P, G.Vt, G.k, G.sink, G.select, G.coarse, (double)G.tau,
-                 g != nullptr, rc);
+                 g != nullptr, rc, rc == VSA_ERR_HIP ? g_last_error : "");
   }
   return rc;
 }

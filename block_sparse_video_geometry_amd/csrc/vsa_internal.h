@@ -8,6 +8,7 @@
 
 #define VSA_MAX_PREFIX_SEGS 16
 #define VSA_MAX_VIDEO_TILES 4096
+#define VSA_MAX_LIST 2048        // key tiles in one sparse row's list (staged in LDS by the fine kernel)
 #define VSA_HEAD_DIM 128
 #define VSA_TILE_TOKENS 64
 #define VSA_COARSE_ROWS 32   // sparse rows per workgroup of the coarse-score kernel

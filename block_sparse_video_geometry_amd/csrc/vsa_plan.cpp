@@ -121,6 +121,10 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     g.k = 0;
     g.cap = g.P + g.Vt;
   }
+  if (g.cap > VSA_MAX_LIST) {
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
   g.sink = o.sink;
   g.select = o.select;
   g.coarse = o.coarse;

@@ -63,14 +63,22 @@ class vsa_kernel_time(C.Structure):
 
 EXPORTS = ["vsa_plan_geometry", "vsa_plan_workspace_bytes", "vsa_plan_describe", "vsa_forward",
            "vsa_read_stats", "vsa_debug_views", "vsa_plan_destroy", "vsa_status_string",
+           "vsa_last_error",
            "vsa_timer_create", "vsa_timer_destroy", "vsa_timer_reset", "vsa_forward_timed",
            "vsa_timer_read"]
 
 
 def _load():
+    # torch ships its own HIP runtime; it must be initialised in the process before
+    # libvsa.so pulls in the system one, or the second runtime finds no device.  Loading
+    # torch first makes both share one set of GPU queues and allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not _LIB_PATH.exists():
-        raise ImportError(f"{_LIB_PATH} is not built: run `python -m "
-                          f"block_sparse_video_geometry_amd.build` (no fallback path exists)")
+        raise ImportError(f"{_LIB_PATH} is not built: run `python "
+                          f"block_sparse_video_geometry_amd/build.py` (no fallback path exists)")
     lib = C.CDLL(str(_LIB_PATH))
     P, I, S = C.c_void_p, C.c_int, C.c_size_t
     sig = {
@@ -83,6 +91,7 @@ def _load():
         "vsa_debug_views": (I, [P, C.POINTER(vsa_debug)]),
         "vsa_plan_destroy": (I, [P]),
         "vsa_status_string": (C.c_char_p, [I]),
+        "vsa_last_error": (C.c_char_p, []),
         "vsa_timer_create": (I, [C.POINTER(P)]),
         "vsa_timer_destroy": (I, [P]),
         "vsa_timer_reset": (I, [P]),
@@ -102,7 +111,8 @@ _lib = _load()
 class VsaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {vsa_status_string(status)} ({status})")
+        detail = _lib.vsa_last_error().decode() if status == VSA_ERR_HIP else ""
+        super().__init__(f"{what}: {vsa_status_string(status)} ({status}) {detail}".rstrip())
 
 
 def vsa_status_string(status: int) -> str:

@@ -62,7 +62,9 @@ typedef enum {
   VSA_ERR_UNSUPPORTED = -2,      /* outside what the kernels implement: head_dim != 128,
                                     grid dims not multiples of 4, not exactly one video span,
                                     keep outside (0, 100], > 4096 video tiles, > 16 prefix
-                                    segments, unknown mode, device not gfx950.  The caller
+                                    segments, a sparse row list longer than 2048 tiles
+                                    (P + k, or P + Vt in TAU mode), unknown mode, device
+                                    not gfx950.  The caller
                                     decides explicitly what to run instead. */
   VSA_ERR_WORKSPACE = -3,        /* workspace pointer null or smaller than required */
   VSA_ERR_HIP = -4,              /* a HIP runtime call or kernel launch failed */
@@ -200,6 +202,11 @@ int vsa_plan_destroy(vsa_plan* plan);
 
 /* Static string for a status code (never NULL). */
 const char* vsa_status_string(int status);
+
+/* Detail of the last VSA_ERR_HIP returned on the calling thread: the step
+ * and the HIP error name and text ("" if none).  Valid until the next call
+ * on the same thread. */
+const char* vsa_last_error(void);
 
 /* ---- kernel timing for measurement -------------------------------------
  * A timer records a HIP event pair around every kernel that
