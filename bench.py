@@ -40,6 +40,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fine_full_traffic.json"),
                     help="measured HBM bytes per fine launch (from rocprofv3 counters)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before timing, copy this many MiB device-to-device (a kernel of known "
+                         "traffic that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -122,6 +125,14 @@ def main():
     timer = V.Timer()
     stream = torch.cuda.current_stream()
 
+    if a.calib_copy_mb > 0:
+        n = a.calib_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(a.warmup):
         V.vsa_forward(plan, q, k, v, g, o, ws)
     torch.cuda.synchronize()

@@ -30,6 +30,11 @@
 // (max, sum, O) partials are merged through LDS and each wave writes 16 query
 // rows (gate combine, bf16 round-to-nearest-even, packed order).
 //
+// Per-tile scalar work is kept small: every LDS read address is a per-lane
+// base fixed for the whole kernel plus an immediate offset, and the source
+// location of the wave's tiles is computed 64 tiles at a time (one per lane)
+// and read back with readlane.
+//
 // Rows are ordered head-major, dense rows first, and mapped XCD-aware: the
 // hardware deals workgroup i to XCD i % 8, so XCD x receives a contiguous
 // range of heads and its L2 sees one head's K/V at a time.
@@ -45,6 +50,8 @@ constexpr int TILE_BYTES = 16384;    // one 64 x 128 bf16 tile
 constexpr int LIST_LDS = VSA_MAX_LIST;  // a sparse row's list is staged whole in LDS
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -53,16 +60,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 // [lds + 16 i, lds + 16 i + 16) with the 16 bytes at base + voff.  Issued from asm so the
 // compiler neither inserts its own (whole-queue) waits for the LDS write nor moves LDS
 // reads across it; completion is tracked with vmcnt by the waits below.  No register
-// results, so nothing is left pending in a VGPR.
+// results, so nothing is left pending in a VGPR.  M0 is used by nothing else in this
+// kernel, so it is set here and not restored.
 __device__ __forceinline__ void dma16(const char* base, unsigned voff, unsigned lds) {
-  unsigned saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(base), "s"(lds)
       : "memory");
 }
@@ -75,71 +80,40 @@ __device__ __forceinline__ void wait_vm() {
 // Wait for this wave's LDS reads; a compiler memory barrier before the next DMA.
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-// key held by row r of 16-row MFMA block kb in the S^T product
-__device__ __forceinline__ int kperm(int kb, int r) {
-  return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
-}
-// K tile: 16-byte chunk c of key row `row` lives at chunk c ^ kswz(row)
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
-// V tile: 16-byte chunk c of key row `row` lives at chunk c ^ vswz(row)
-__device__ __forceinline__ int vswz(int row) { return (2 * (row & 3) + 8 * ((row >> 3) & 1)) & 15; }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// LDS byte address of an LDS pointer (wave-uniform here)
 __device__ __forceinline__ unsigned lds_u32(lds_char* p) {
   return __builtin_amdgcn_readfirstlane((unsigned)(size_t)p);
 }
 
-__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Uniform description of where a key tile's 64 rows live.
-struct TileSrc {
-  long long base;   // byte offset of the tile's first token row (head h)
-  int video;        // 4x4x4 video tile (else prefix run of consecutive tokens)
-  int nvalid;       // valid rows
-};
-
-__device__ __forceinline__ TileSrc tile_src(const VsaGeom& g, int b, int h, int t) {
-  TileSrc s;
-  int tok0;
-  if (t >= g.P) {
-    const int j = t - g.P;
-    const int tw = j % g.tw_n;
-    const int rest = j / g.tw_n;
-    const int th = rest % g.th_n;
-    const int tt = rest / g.th_n;
-    tok0 = g.vstart + (4 * tt * g.H + 4 * th) * g.W + 4 * tw;
-    s.video = 1;
-    s.nvalid = VSA_TILE_TOKENS;
-  } else {
-    const int sg = prefix_seg(g, t);
-    const int off = (t - g.pre_tile0[sg]) * VSA_TILE_TOKENS;
-    tok0 = g.pre_start[sg] + off;
-    const int rem = g.pre_len[sg] - off;
-    s.video = 0;
-    s.nvalid = rem < VSA_TILE_TOKENS ? rem : VSA_TILE_TOKENS;
-  }
-  s.base = row_offset(g, b, tok0, h) * 2;
-  return s;
-}
+// Tile layout in LDS.
+//  K: key row r at r*256; its 16-byte chunk c at position c ^ kswz(r),
+//     kswz(r) = (r & 3) | ((r >> 3) & 3) << 2.
+//  V: key row r at r*256; chunk c at position c ^ vswz(r),
+//     vswz(r) = (2 (r & 3) + 8 ((r >> 3) & 1)) & 15.
+// QK reads K rows kperm(kb, ql) = 32(kb>>1) + 8(ql>>2) + 4(kb&1) + (ql&3), for which
+// kswz = ql: the lane address is base_k[ks] + 256 * (32(kb>>1) + 4(kb&1)).
+// PV reads V rows 32c + 8 grp + (ql>>2) + 4h, for which vswz = 2(ql>>2) + 8(grp&1):
+// the lane address is base_v[db] + 256 * (32c + 4h).
+// The DMA lane offsets below follow the same two swizzles.
 
 __global__ __launch_bounds__(256) void vsa_fine_kernel(
     VsaGeom g, const char* __restrict__ kptr, const char* __restrict__ vptr,
     const u32x4* __restrict__ q, const unsigned short* __restrict__ gate,
     const float* __restrict__ ocoarse, const int* __restrict__ lists,
     const int* __restrict__ counts, unsigned short* __restrict__ o, int per_xcd) {
-  // per wave: K tile then V tile; separate arrays so LDS reads of one are never
+  // per wave: a K tile and a V tile; separate arrays so LDS reads of one are never
   // taken as aliasing DMA writes in flight to the other
   __shared__ __attribute__((aligned(16))) char klds_all[NW * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char vlds_all[NW * TILE_BYTES];
   __shared__ float mbuf[NW][64];
   __shared__ float lbuf[NW][64];
   __shared__ int lst_lds[LIST_LDS];
+  __shared__ int seg_lds[3][VSA_MAX_PREFIX_SEGS + 1];  // prefix segment table (start, len, tile0)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -151,19 +125,19 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   const bool dense = qt < g.n_dense;
   const int srow = qt - g.n_dense;
   int nlist;
-  const int* lst = nullptr;
   if (dense) {
     nlist = g.Tq;
   } else {
     nlist = min(counts[(size_t)bh * g.Qs + srow], g.cap);  // cap <= LIST_LDS (plan)
-    lst = lists + ((size_t)bh * g.Qs + srow) * g.cap;
+    const int* lst = lists + ((size_t)bh * g.Qs + srow) * g.cap;
+    for (int i = tid; i < nlist; i += 256) lst_lds[i] = lst[i];
   }
-
-  // stage the list in LDS: the loop then reads tile ids without touching the memory counters
-  if (!dense)
-    for (int i = tid; i < nlist; i += 256) lst_lds[i] = lst[i];  // nlist <= cap <= LIST_LDS (plan)
+  if (tid <= VSA_MAX_PREFIX_SEGS) {
+    seg_lds[0][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_start[tid] : 0;
+    seg_lds[1][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_len[tid] : 0;
+    seg_lds[2][tid] = g.pre_tile0[tid];
+  }
   __syncthreads();
-  auto tile_at = [&](int i) -> int { return dense ? i : lst_lds[i]; };
 
   const int grp = lane >> 4, ql = lane & 15;
   // Q^T operands: lane holds queries 16 qb + ql, dims 32 ks + 8 grp .. +7
@@ -180,45 +154,104 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       for (int ks = 0; ks < 4; ++ks) qv[qb][ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
   }
-
   // Q must be in registers before the first DMA: a wait the compiler sees, so it does not
   // re-wait (whole queue) for these loads inside the loop
   __builtin_amdgcn_s_waitcnt(0);
 
-  // per-lane DMA offsets.  Rows 4n + gi of instruction n (gi = lane / 16),
-  // 16-byte position lane % 16 holds chunk (lane % 16) ^ swizzle(row).
-  const int rowbytes = g.heads * VSA_HEAD_DIM * 2;
+  // DMA lane offsets: instruction n covers key rows 4n .. 4n+3; lane = 16 gi + pos writes
+  // row 4n + gi, position pos, i.e. chunk pos ^ swizzle(4n + gi).  The swizzles depend on
+  // n only through (n >> 1) & 3 (K) and (n >> 1) & 1 (V).
+  const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
   const int gi = lane >> 4, pos = lane & 15;
   unsigned koff[4], voff[2];
 #pragma unroll
   for (int m = 0; m < 4; ++m) koff[m] = gi * rowbytes + ((pos ^ (gi | (m << 2))) << 4);
 #pragma unroll
   for (int m = 0; m < 2; ++m) voff[m] = gi * rowbytes + ((pos ^ ((2 * gi + 8 * m) & 15)) << 4);
-  const long long plane = (long long)g.H * g.W * rowbytes;  // token stride dt -> bytes
-  const long long line = (long long)g.W * rowbytes;         // token stride dh -> bytes
+  const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
+  const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
+  const long long bh_off = ((long long)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2);
+  const char* kbh = kptr + bh_off;
+  const char* vbh = vptr + bh_off;
 
   lds_char* kbuf = (lds_char*)(klds_all + wave * TILE_BYTES);
   lds_char* vbuf = (lds_char*)(vlds_all + wave * TILE_BYTES);
+  const unsigned kbuf_u = lds_u32(kbuf), vbuf_u = lds_u32(vbuf);
 
-  auto issue = [&](const char* __restrict__ X, const TileSrc& s, lds_char* dst, bool is_k) {
-    if (s.nvalid == VSA_TILE_TOKENS) {
+  // LDS read bases (see the layout note above)
+  unsigned kbase[4], vbase[8];
+  {
+    const unsigned lrow = (unsigned)(8 * (ql >> 2) + (ql & 3)) * 256;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kbase[ks] = kbuf_u + lrow + (((4 * ks + grp) ^ ql) << 4);
+    const unsigned vrow = (unsigned)(8 * grp + (ql >> 2)) * 256 + 8 * (ql & 1);
+    const int vm = (ql >> 2) + 4 * (grp & 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vbase[db] = vbuf_u + vrow + ((2 * (db ^ vm) + ((ql & 3) >> 1)) << 4);
+  }
+
+  // Tile descriptors, 64 at a time: lane l describes this wave's tile 64 batch + l.
+  // off = byte offset of the tile's first token row in the (b, h) plane;
+  // flags = video | nvalid << 1.
+  const int my_n = nlist > wave ? (nlist - wave + NW - 1) / NW : 0;
+  unsigned d_off = 0, d_flags = 0;
+  auto describe = [&](int batch) {
+    const int j = batch * 64 + lane;
+    int t = 0;
+    if (j < my_n) t = dense ? wave + NW * j : lst_lds[wave + NW * j];
+    int tok0, video, nvalid;
+    if (t >= g.P) {
+      const int jv = t - g.P;
+      const int tw = jv % g.tw_n;
+      const int rest = jv / g.tw_n;
+      const int th = rest % g.th_n;
+      const int tt = rest / g.th_n;
+      tok0 = g.vstart + (4 * tt * g.H + 4 * th) * g.W + 4 * tw;
+      video = 1;
+      nvalid = VSA_TILE_TOKENS;
+    } else {
+      // per-lane segment lookup from LDS (indexing the argument struct per lane would
+      // become vector loads, whose waits would drain the DMA queue)
+      int sg = 0;
+      for (int i = 1; i < g.n_pre_segs; ++i)
+        if (t >= seg_lds[2][i]) sg = i;
+      const int off = (t - seg_lds[2][sg]) * VSA_TILE_TOKENS;
+      tok0 = seg_lds[0][sg] + off;
+      const int rem = seg_lds[1][sg] - off;
+      video = 0;
+      nvalid = rem < VSA_TILE_TOKENS ? rem : VSA_TILE_TOKENS;
+    }
+    d_off = (unsigned)tok0 * rowbytes;
+    d_flags = (unsigned)video | ((unsigned)nvalid << 1);
+  };
+
+  // bring tile (off, flags) of X into LDS at dst
+  auto issue = [&](const char* __restrict__ X, unsigned off, unsigned flags, unsigned dst,
+                   bool is_k) {
+    const int nvalid = (int)(flags >> 1);
+    if (flags & 1) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
-        // rows 4n..4n+3: video (dt, dh) = (n >> 2, n & 3); prefix tokens 4n..4n+3
-        const long long sb = s.video ? s.base + (n >> 2) * plane + (n & 3) * line
-                                     : s.base + (long long)(4 * n) * rowbytes;
-        const unsigned off = is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1];
-        dma16(X + sb, off, lds_u32(dst) + 1024 * n);  // uniform SGPR base + 32-bit lane offset
+        // rows 4n..4n+3 of a video tile: (dt, dh) = (n >> 2, n & 3)
+        const char* sb = X + off + (n >> 2) * plane + (n & 3) * line;
+        dma16(sb, is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1], dst + 1024 * n);
+      }
+    } else if (nvalid == VSA_TILE_TOKENS) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const char* sb = X + off + (4 * n) * rowbytes;  // prefix tokens 4n .. 4n+3
+        dma16(sb, is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1], dst + 1024 * n);
       }
     } else {
       // partial prefix tile: padding rows re-read the last valid row (masked later)
-      const char* base = X + s.base;
+      const char* sb = X + off;
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
-        const int row = min(4 * n + gi, s.nvalid - 1);
-        const unsigned off = (is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1]) +
-                             (unsigned)((row - gi) * rowbytes);
-        dma16(base, off, lds_u32(dst) + 1024 * n);
+        const int row = min(4 * n + gi, nvalid - 1);
+        const unsigned lo = (is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1]) +
+                            (unsigned)(row - gi) * rowbytes;
+        dma16(sb, lo, dst + 1024 * n);
       }
     }
   };
@@ -236,20 +269,23 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   }
   const float sl2 = g.scale * LOG2E;
 
-  const int my_n = nlist > wave ? (nlist - wave + NW - 1) / NW : 0;
-  int t_cur = 0;
-  TileSrc src{};
+  unsigned c_off = 0, c_flags = 0;  // current tile
   if (my_n > 0) {
-    t_cur = tile_at(wave);
-    src = tile_src(g, b, h, t_cur);
-    issue(kptr, src, kbuf, true);
-    issue(vptr, src, vbuf, false);
+    describe(0);
+    c_off = __builtin_amdgcn_readlane(d_off, 0);
+    c_flags = __builtin_amdgcn_readlane(d_flags, 0);
+    issue(kbh, c_off, c_flags, kbuf_u, true);
+    issue(vbh, c_off, c_flags, vbuf_u, false);
   }
   for (int j = 0; j < my_n; ++j) {
     const bool has_next = j + 1 < my_n;
-    int t_next = 0;
-    if (has_next) t_next = tile_at(wave + NW * (j + 1));
-    const int nvalid = src.nvalid;
+    unsigned n_off = 0, n_flags = 0;
+    if (has_next) {
+      if (((j + 1) & 63) == 0) describe((j + 1) >> 6);
+      n_off = __builtin_amdgcn_readlane(d_off, (j + 1) & 63);
+      n_flags = __builtin_amdgcn_readlane(d_flags, (j + 1) & 63);
+    }
+    const int nvalid = (int)(c_flags >> 1);
 
     // ---- S^T = K Q^T (K(t) landed; V(t) may still be in flight)
     wait_vm<16>();
@@ -260,11 +296,10 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       for (int qb = 0; qb < 4; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int key = kperm(kb, ql);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a =
-            as_bf16x8(((lds_u32x4*)kbuf)[key * 16 + ((4 * ks + grp) ^ kswz(key))]);
+        const unsigned a_addr = kbase[ks] + 256 * (32 * (kb >> 1) + 4 * (kb & 1));
+        const bf16x8 a = as_bf16x8(*(const lds_u32x4*)(size_t)a_addr);
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb)
           sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[qb][ks], sacc[kb][qb], 0, 0, 0);
@@ -272,11 +307,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     }
     // K buffer is free once its reads returned: fetch the next tile's K
     wait_lgkm0();
-    TileSrc nsrc{};
-    if (has_next) {
-      nsrc = tile_src(g, b, h, t_next);
-      issue(kptr, nsrc, kbuf, true);
-    }
+    if (has_next) issue(kbh, n_off, n_flags, kbuf_u, true);
 
     // ---- online softmax; lane holds keys 32(kb>>1) + 8 grp + 4(kb&1) + i of queries 16 qb + ql
     if (nvalid < VSA_TILE_TOKENS) {
@@ -346,14 +377,9 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        // lanes of group grp read rows 32c + 8 grp + (ql >> 2) (+4), dims 16 db + 4 (ql & 3)
-        const int row0 = 32 * c + 8 * grp + (ql >> 2);
-        const int chunk = 2 * db + ((ql & 3) >> 1);
-        const int half = (ql & 1) * 8;
-        const int a0 = row0 * 256 + ((chunk ^ vswz(row0)) << 4) + half;
-        const int a1 = (row0 + 4) * 256 + ((chunk ^ vswz(row0 + 4)) << 4) + half;
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbuf + a0));
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbuf + a1));
+        const unsigned a0 = vbase[db] + 256 * (32 * c);
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a0);
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a0 + 1024));
         const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
         const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
         const bf16x8 a = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
@@ -363,11 +389,10 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       }
     }
     wait_lgkm0();
-    if (has_next) issue(vptr, nsrc, vbuf, false);
-    src = nsrc;
-    t_cur = t_next;
+    if (has_next) issue(vbh, n_off, n_flags, vbuf_u, false);
+    c_off = n_off;
+    c_flags = n_flags;
   }
-  (void)t_cur;
 
   // ---- merge the four waves' partials
 #pragma unroll
@@ -381,8 +406,8 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int qb = 0; qb < 4; ++qb) mbuf[wave][16 * qb + ql] = mrun[qb];
   }
   __syncthreads();
-  // partial O of this wave: queries 0..31 in its K tile area, 32..63 in its V tile area,
-  // each [32 q][32 chunks of 4 fp32]
+  // partial O of wave w: queries 0..31 in its K tile area, 32..63 in its V tile area,
+  // each [32 q][32 chunks of 4 fp32], chunk c of query q at c ^ (q & 31)
   auto part = [&](int w, int qq) -> lds_u32x4* {
     return (lds_u32x4*)((qq < 32 ? klds_all : vlds_all) + w * TILE_BYTES) + (qq & 31) * 32;
   };
