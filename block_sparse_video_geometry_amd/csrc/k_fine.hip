@@ -294,15 +294,31 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      // operands of key block kb+1 are read while the 16 MFMAs of block kb issue
+      bf16x8 ka[2][4];
+      auto kread = [&](int kb, bf16x8* dst) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+        for (int ks = 0; ks < 4; ++ks)
+          dst[ks] = as_bf16x8(*(const lds_u32x4*)(size_t)(kbase[ks] + 256 * (32 * (kb >> 1) + 4 * (kb & 1))));
+      };
+      kread(0, ka[0]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const unsigned a_addr = kbase[ks] + 256 * (32 * (kb >> 1) + 4 * (kb & 1));
-        const bf16x8 a = as_bf16x8(*(const lds_u32x4*)(size_t)a_addr);
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < 3) kread(kb + 1, ka[(kb + 1) & 1]);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qv[qb][ks], sacc[kb][qb], 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb)
+            sacc[kb][qb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb & 1][ks], qv[qb][ks], sacc[kb][qb], 0, 0, 0);
+      }
+      // pin the order: reads of block 0, then (reads of kb+1, MFMAs of kb)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       }
     }
     // K buffer is free once its reads returned: fetch the next tile's K
@@ -335,15 +351,26 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       mloc[qb] = m * sl2;
       grow |= mloc[qb] > mrun[qb] + RESCALE_TH;
     }
-    if (__ballot(grow)) {  // wave-uniform: move the running max, rescale O and l
+    if (j == 0) {
+      // first tile: O and l are still zero, only the running max is set
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) mrun[qb] = mloc[qb];
+    } else if (__ballot(grow)) {  // wave-uniform, rare: move the running max, rescale O and l
+      float alpha[4];
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
         const float mn = fmaxf(mrun[qb], mloc[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mn);
+        alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - mn);
         mrun[qb] = mn;
-        lsum[qb] *= alpha;
+        lsum[qb] *= alpha[qb];
+      }
+      // one 16-value slice at a time (scheduling barriers), so this rare path does not need
+      // all 128 accumulators in VGPRs at once
 #pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[db][qb] *= alpha;
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) oacc[db][qb] *= alpha[qb];
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     bf16x8 pb[4][2];
@@ -373,19 +400,37 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       wait_vm<16>();
     else
       wait_vm<0>();
+    {
+      // V^T operands of dim block db+1 (both 32-key steps) are read while the 8 MFMAs of
+      // block db issue
+      bf16x8 va[2][2];
+      auto vread = [&](int db, bf16x8* dst) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 2; ++c) {
+          const unsigned a0 = vbase[db] + 256 * (32 * c);
+          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a0);
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a0 + 1024));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
+          const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
+          dst[c] = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+        }
+      };
+      vread(0, va[0]);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const unsigned a0 = vbase[db] + 256 * (32 * c);
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a0);
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a0 + 1024));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
-        const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
-        const bf16x8 a = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+        if (db < 7) vread(db + 1, va[(db + 1) & 1]);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qb][c], oacc[db][qb], 0, 0, 0);
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb)
+            oacc[db][qb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db & 1][c], pb[qb][c], oacc[db][qb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        if (db < 7) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
       }
     }
     wait_lgkm0();
