@@ -56,19 +56,19 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16) with the 16 bytes at base + voff.  Issued from asm so the
-// compiler neither inserts its own (whole-queue) waits for the LDS write nor moves LDS
-// reads across it; completion is tracked with vmcnt by the waits below.  No register
-// results, so nothing is left pending in a VGPR.  M0 is used by nothing else in this
-// kernel, so it is set here and not restored.
-__device__ __forceinline__ void dma16(const char* base, unsigned voff, unsigned lds) {
+// Direct buffer -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16) with the 16 bytes at buffer offset soff + voff (zero when
+// out of the resource's range).  Issued from asm so the compiler neither inserts its own
+// (whole-queue) waits for the LDS write nor moves LDS reads across it; completion is
+// tracked with vmcnt by the waits below.  No register results, so nothing is left pending
+// in a VGPR.  M0 is used by nothing else in this kernel, so it is set here and not restored.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, unsigned lds) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
-      : "v"(voff), "s"(base), "s"(lds)
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
       : "memory");
 }
 // Wait until at most N vector-memory operations of this wave are outstanding; also a
@@ -84,6 +84,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 
 __device__ __forceinline__ unsigned lds_u32(lds_char* p) {
   return __builtin_amdgcn_readfirstlane((unsigned)(size_t)p);
+}
+
+// Value of an accumulator register moved to a VGPR by an explicit, non-speculated move.
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
 }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
@@ -112,6 +119,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   __shared__ __attribute__((aligned(16))) char vlds_all[NW * TILE_BYTES];
   __shared__ float mbuf[NW][64];
   __shared__ float lbuf[NW][64];
+  __shared__ __attribute__((aligned(16))) float sbuf[NW][64];
   __shared__ int lst_lds[LIST_LDS];
   __shared__ int seg_lds[3][VSA_MAX_PREFIX_SEGS + 1];  // prefix segment table (start, len, tile0)
 
@@ -171,8 +179,13 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
   const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
   const long long bh_off = ((long long)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2);
-  const char* kbh = kptr + bh_off;
-  const char* vbh = vptr + bh_off;
+  // One buffer resource per tensor over this (b, h) plane.  Offsets past its last byte read
+  // zero: the padding rows of a partial prefix tile at the end of the sequence, and the
+  // loads for the tile after a wave's last one (offset >= 2^31, never in range).
+  const int nrec = (int)((unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kptr + bh_off), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vptr + bh_off), 0, nrec, 0x00020000);
+  constexpr unsigned NO_TILE = 0x80000000u;
 
   lds_char* kbuf = (lds_char*)(klds_all + wave * TILE_BYTES);
   lds_char* vbuf = (lds_char*)(vlds_all + wave * TILE_BYTES);
@@ -225,35 +238,17 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     d_off = (unsigned)tok0 * rowbytes;
     d_flags = (unsigned)video | ((unsigned)nvalid << 1);
   };
-
-  // bring tile (off, flags) of X into LDS at dst
-  auto issue = [&](const char* __restrict__ X, unsigned off, unsigned flags, unsigned dst,
-                   bool is_k) {
-    const int nvalid = (int)(flags >> 1);
-    if (flags & 1) {
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        // rows 4n..4n+3 of a video tile: (dt, dh) = (n >> 2, n & 3)
-        const char* sb = X + off + (n >> 2) * plane + (n & 3) * line;
-        dma16(sb, is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1], dst + 1024 * n);
-      }
-    } else if (nvalid == VSA_TILE_TOKENS) {
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        const char* sb = X + off + (4 * n) * rowbytes;  // prefix tokens 4n .. 4n+3
-        dma16(sb, is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1], dst + 1024 * n);
-      }
-    } else {
-      // partial prefix tile: padding rows re-read the last valid row (masked later)
-      const char* sb = X + off;
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        const int row = min(4 * n + gi, nvalid - 1);
-        const unsigned lo = (is_k ? koff[(n >> 1) & 3] : voff[(n >> 1) & 1]) +
-                            (unsigned)(row - gi) * rowbytes;
-        dma16(sb, lo, dst + 1024 * n);
-      }
-    }
+  // Row group n (key rows 4n .. 4n+3) of a tile starts at off + (n >> 2) * stp + (n & 3) * stl:
+  // a video tile steps dt and dh, a prefix tile 16 and 4 tokens.
+  auto steps = [&](unsigned flags, unsigned& stp, unsigned& stl) {
+    stp = (flags & 1) ? plane : 16 * rowbytes;
+    stl = (flags & 1) ? line : 4 * rowbytes;
+  };
+  auto kdma = [&](int n, unsigned off, unsigned stp, unsigned stl) {
+    bdma16(krs, koff[(n >> 1) & 3], off + (n >> 2) * stp + (n & 3) * stl, kbuf_u + 1024 * n);
+  };
+  auto vdma = [&](int n, unsigned off, unsigned stp, unsigned stl) {
+    bdma16(vrs, voff[(n >> 1) & 1], off + (n >> 2) * stp + (n & 3) * stl, vbuf_u + 1024 * n);
   };
 
   f32x4 oacc[8][4];
@@ -269,31 +264,33 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   }
   const float sl2 = g.scale * LOG2E;
 
+  // Per tile t: V(t) is fetched while QK(t) runs (one row group per four MFMAs), K(t+1)
+  // while the softmax of t runs.  At the top of an iteration only K(t) is outstanding.
   unsigned c_off = 0, c_flags = 0;  // current tile
   if (my_n > 0) {
     describe(0);
     c_off = __builtin_amdgcn_readlane(d_off, 0);
     c_flags = __builtin_amdgcn_readlane(d_flags, 0);
-    issue(kbh, c_off, c_flags, kbuf_u, true);
-    issue(vbh, c_off, c_flags, vbuf_u, false);
+    unsigned stp, stl;
+    steps(c_flags, stp, stl);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) kdma(n, c_off, stp, stl);
   }
   for (int j = 0; j < my_n; ++j) {
-    const bool has_next = j + 1 < my_n;
-    unsigned n_off = 0, n_flags = 0;
-    if (has_next) {
+    unsigned n_off = NO_TILE, n_flags = 0;
+    if (j + 1 < my_n) {
       if (((j + 1) & 63) == 0) describe((j + 1) >> 6);
       n_off = __builtin_amdgcn_readlane(d_off, (j + 1) & 63);
       n_flags = __builtin_amdgcn_readlane(d_flags, (j + 1) & 63);
     }
     const int nvalid = (int)(c_flags >> 1);
+    unsigned c_stp, c_stl, n_stp, n_stl;
+    steps(c_flags, c_stp, c_stl);
+    steps(n_flags, n_stp, n_stl);
 
-    // ---- S^T = K Q^T (K(t) landed; V(t) may still be in flight)
-    wait_vm<16>();
+    // ---- S^T = K Q^T (K(t) landed), with the V(t) loads spread over the MFMAs
+    wait_vm<0>();
     f32x4 sacc[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       // operands of key block kb+1 are read while the 16 MFMAs of block kb issue
       bf16x8 ka[2][4];
@@ -307,23 +304,22 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       for (int kb = 0; kb < 4; ++kb) {
         if (kb < 3) kread(kb + 1, ka[(kb + 1) & 1]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb)
-            sacc[kb][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb & 1][ks], qv[qb][ks], sacc[kb][qb], 0, 0, 0);
-      }
-      // pin the order: reads of block 0, then (reads of kb+1, MFMAs of kb)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                ka[kb & 1][ks], qv[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb][qb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          vdma(4 * kb + ks, c_off, c_stp, c_stl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    // K buffer is free once its reads returned: fetch the next tile's K
+    // K buffer is free once its reads returned
     wait_lgkm0();
-    if (has_next) issue(kbh, n_off, n_flags, kbuf_u, true);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) kdma(n, n_off, n_stp, n_stl);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax; lane holds keys 32(kb>>1) + 8 grp + 4(kb&1) + i of queries 16 qb + ql
     if (nvalid < VSA_TILE_TOKENS) {
@@ -364,15 +360,35 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
         mrun[qb] = mn;
         lsum[qb] *= alpha[qb];
       }
-      // one 16-value slice at a time (scheduling barriers), so this rare path does not need
-      // all 128 accumulators in VGPRs at once
+      // O <- diag(alpha) O with exact fp32 MFMAs (one product and zero additions per
+      // element), so O is never touched by VALU inside the loop and stays in the
+      // accumulator registers.  For accumulator element i the B operand (4 x 16) is
+      // O[4 g + i][d] at lane (g, d), and A_i (16 x 4) has alpha[r] at [r][g] where
+      // r == 4 g + i: lane (grp, ql) holds A_i[ql][grp].
+      float asel[4][4];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) oacc[db][qb] *= alpha[qb];
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int i = 0; i < 4; ++i) asel[qb][i] = ql == 4 * grp + i ? alpha[qb] : 0.f;
+      // The B operands are read out of the accumulator file by explicit moves inside this
+      // branch (the compiler would otherwise copy all 128 accumulators on every iteration);
+      // the NOPs cover the MFMA-result-to-VALU-read latency for those moves.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          float ob[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ob[i] = acc_read(oacc[db][qb][i]);
+          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][0], ob[0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0);
+#pragma unroll
+          for (int i = 1; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][i], ob[i], acc, 0, 0, 0);
+          oacc[db][qb] = acc;
+        }
     }
+    // P = exp2(S sl2 - m) as bf16 PV operands, with the rest of K(t+1) in between
     bf16x8 pb[4][2];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -393,15 +409,16 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
         w[3] = pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3]);
         pb[qb][c] = as_bf16x8(w);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int n = 0; n < 3; ++n) kdma(4 + 3 * qb + n, n_off, n_stp, n_stl);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- O^T += V^T P^T (V(t) landed; K(t_next) may be in flight)
-    if (has_next)
-      wait_vm<16>();
-    else
-      wait_vm<0>();
+    // ---- O += P V (V(t) landed; the 16 loads of K(t+1) may be in flight)
+    wait_vm<16>();
     {
-      // V^T operands of dim block db+1 (both 32-key steps) are read while the 8 MFMAs of
+      // V operands of dim block db+1 (both 32-key steps) are read while the 8 MFMAs of
       // block db issue
       bf16x8 va[2][2];
       auto vread = [&](int db, bf16x8* dst) {
@@ -424,7 +441,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb)
             oacc[db][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db & 1][c], pb[qb][c], oacc[db][qb], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[qb][c], va[db & 1][c], oacc[db][qb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
@@ -433,13 +450,17 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
       }
     }
+    // V buffer is free once its reads returned
     wait_lgkm0();
-    if (has_next) issue(vbh, n_off, n_flags, vbuf_u, false);
     c_off = n_off;
     c_flags = n_flags;
   }
+  // the loads issued for the tile after the last one (out of range, writing zeros) must
+  // land before the K buffer is reused below
+  wait_vm<0>();
 
-  // ---- merge the four waves' partials
+  // ---- merge the four waves' partials.  Softmax statistics are per lane for queries
+  // 16 qb + ql; O is held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     lsum[qb] += __shfl_xor(lsum[qb], 16);
@@ -451,11 +472,6 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int qb = 0; qb < 4; ++qb) mbuf[wave][16 * qb + ql] = mrun[qb];
   }
   __syncthreads();
-  // partial O of wave w: queries 0..31 in its K tile area, 32..63 in its V tile area,
-  // each [32 q][32 chunks of 4 fp32], chunk c of query q at c ^ (q & 31)
-  auto part = [&](int w, int qq) -> lds_u32x4* {
-    return (lds_u32x4*)((qq < 32 ? klds_all : vlds_all) + w * TILE_BYTES) + (qq & 31) * 32;
-  };
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     const int qq = 16 * qb + ql;
@@ -463,57 +479,76 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
 #pragma unroll
     for (int w = 1; w < NW; ++w) mt = fmaxf(mt, mbuf[w][qq]);
     const float sc = mrun[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[qb] - mt);
-    if (grp == 0) lbuf[wave][qq] = lsum[qb] * sc;
+    if (grp == 0) {
+      lbuf[wave][qq] = lsum[qb] * sc;
+      sbuf[wave][qq] = sc;
+    }
+  }
+  __syncthreads();
+  // partial O^T of wave w: dims 0..63 in its K tile area, 64..127 in its V tile area, each
+  // dim a 256-byte row of 64 fp32 queries; the 16-byte chunk of queries 4c..4c+3 sits at
+  // chunk c ^ (dim & 15)
+  auto part = [&](int w, int d) -> lds_u32x4* {
+    return (lds_u32x4*)((d < 64 ? klds_all : vlds_all) + w * TILE_BYTES) + (d & 63) * 16;
+  };
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const f32x4 sc4 = *(const f32x4*)&sbuf[wave][16 * qb + 4 * grp];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const f32x4 v = oacc[db][qb] * sc;
-      part(wave, qq)[(4 * db + grp) ^ (qq & 31)] = __builtin_bit_cast(u32x4, v);
+      const f32x4 v = oacc[db][qb] * sc4;
+      part(wave, 16 * db + ql)[(4 * qb + grp) ^ ql] = __builtin_bit_cast(u32x4, v);
     }
   }
   __syncthreads();
 
-  // ---- epilogue: wave w writes queries 16 w + lane/4, dims 32 (lane%4) .. +31
-  const int qq = 16 * wave + (lane >> 2);
-  const int qr = lane & 3;
-  const int qtok = tile_token(g, qt, qq);
-  if (qtok < 0) return;
-  float ltot = 0.f;
+  // ---- epilogue: wave w writes queries 16 w + 4 (lane / 16) .. +3, dims 8 (lane % 16) .. +7
+  const int qg = lane >> 4, dg = lane & 15;
+  const int q0 = 16 * wave + 4 * qg;
+  float r[4][8];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) ltot += lbuf[w][qq];
-  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty list gives O_fine = 0
-  float r[32];
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * dg + e;
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      s += __builtin_bit_cast(f32x4, part(w, qq)[(8 * qr + cc) ^ (qq & 31)]);
+    for (int w = 0; w < NW; ++w) s += __builtin_bit_cast(f32x4, part(w, d)[(q0 >> 2) ^ (d & 15)]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[4 * cc + e] = s[e] * inv;
+    for (int i = 0; i < 4; ++i) r[i][e] = s[i];
   }
-  const long long orow = row_offset(g, b, qtok, h) + 32 * qr;
-  if (!dense && gate != nullptr) {
-    const u32x4* gp = reinterpret_cast<const u32x4*>(gate + orow);
-    const f32x4* cp = reinterpret_cast<const f32x4*>(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM + 32 * qr);
+  f32x4 oc0 = f32x4{0.f, 0.f, 0.f, 0.f}, oc1 = oc0;
+  const bool gated = !dense && gate != nullptr;
+  if (gated) {
+    const f32x4* cp = reinterpret_cast<const f32x4*>(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM + 8 * dg);
+    oc0 = cp[0];
+    oc1 = cp[1];
+  }
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const u32x4 gv = gp[c4];
-      const f32x4 o0 = cp[2 * c4], o1 = cp[2 * c4 + 1];
-      r[8 * c4 + 0] += bf16lo(gv[0]) * o0[0];
-      r[8 * c4 + 1] += bf16hi(gv[0]) * o0[1];
-      r[8 * c4 + 2] += bf16lo(gv[1]) * o0[2];
-      r[8 * c4 + 3] += bf16hi(gv[1]) * o0[3];
-      r[8 * c4 + 4] += bf16lo(gv[2]) * o1[0];
-      r[8 * c4 + 5] += bf16hi(gv[2]) * o1[1];
-      r[8 * c4 + 6] += bf16lo(gv[3]) * o1[2];
-      r[8 * c4 + 7] += bf16hi(gv[3]) * o1[3];
+  for (int i = 0; i < 4; ++i) {
+    const int qq = q0 + i;
+    const int qtok = tile_token(g, qt, qq);
+    if (qtok < 0) continue;
+    float ltot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ltot += lbuf[w][qq];
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty list gives O_fine = 0
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = r[i][e] * inv;
+    const long long orow = row_offset(g, b, qtok, h) + 8 * dg;
+    if (gated) {
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(gate + orow);
+      y[0] += bf16lo(gv[0]) * oc0[0];
+      y[1] += bf16hi(gv[0]) * oc0[1];
+      y[2] += bf16lo(gv[1]) * oc0[2];
+      y[3] += bf16hi(gv[1]) * oc0[3];
+      y[4] += bf16lo(gv[2]) * oc1[0];
+      y[5] += bf16hi(gv[2]) * oc1[1];
+      y[6] += bf16lo(gv[3]) * oc1[2];
+      y[7] += bf16hi(gv[3]) * oc1[3];
     }
+    *reinterpret_cast<u32x4*>(o + orow) = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
   }
-  u32x4* op = reinterpret_cast<u32x4*>(o + orow);
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4)
-    op[c4] = u32x4{pack_bf16x2(r[8 * c4], r[8 * c4 + 1]), pack_bf16x2(r[8 * c4 + 2], r[8 * c4 + 3]),
-                   pack_bf16x2(r[8 * c4 + 4], r[8 * c4 + 5]), pack_bf16x2(r[8 * c4 + 6], r[8 * c4 + 7])};
 }
 
 }  // namespace

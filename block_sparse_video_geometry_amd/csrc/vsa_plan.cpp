@@ -70,8 +70,10 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   const int64_t N = pos;
   if (n_video != 1) return VSA_ERR_UNSUPPORTED;
   if (n_prefix > VSA_MAX_PREFIX_SEGS) return VSA_ERR_UNSUPPORTED;
-  // 32-bit token and element indexing inside the kernels
-  if (N * (int64_t)heads * VSA_HEAD_DIM >= ((int64_t)1 << 31)) return VSA_ERR_UNSUPPORTED;
+  // 32-bit token and element indexing inside the kernels; the fine kernel's buffer loads
+  // address one batch item's K or V with 32-bit byte offsets and keep 2^31 free for an
+  // always-out-of-range offset
+  if (N * (int64_t)heads * VSA_HEAD_DIM >= ((int64_t)1 << 30)) return VSA_ERR_UNSUPPORTED;
 
   vsa_plan* p = new (std::nothrow) vsa_plan();
   if (p == nullptr) return VSA_ERR_NO_MEMORY;

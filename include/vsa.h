@@ -63,7 +63,9 @@ typedef enum {
                                     grid dims not multiples of 4, not exactly one video span,
                                     keep outside (0, 100], > 4096 video tiles, > 16 prefix
                                     segments, a sparse row list longer than 2048 tiles
-                                    (P + k, or P + Vt in TAU mode), unknown mode, device
+                                    (P + k, or P + Vt in TAU mode), N * heads * head_dim
+                                    >= 2^30 (one batch item's Q, K or V is addressed
+                                    with 32-bit byte offsets), unknown mode, device
                                     not gfx950.  The caller
                                     decides explicitly what to run instead. */
   VSA_ERR_WORKSPACE = -3,        /* workspace pointer null or smaller than required */
