@@ -93,6 +93,21 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
+// Reductions over the four lanes ql, ql + 16, ql + 32, ql + 48 (one query's partial values)
+// with the row-swap VALU permutes, which do not go through the LDS queue.
+__device__ __forceinline__ float group_max(float m) {
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -342,9 +357,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[kb][qb][i]);
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mloc[qb] = m * sl2;
+      mloc[qb] = group_max(m) * sl2;
       grow |= mloc[qb] > mrun[qb] + RESCALE_TH;
     }
     if (j == 0) {
@@ -463,8 +476,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   // 16 qb + ql; O is held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    lsum[qb] += __shfl_xor(lsum[qb], 16);
-    lsum[qb] += __shfl_xor(lsum[qb], 32);
+    lsum[qb] = group_sum(lsum[qb]);
   }
   __syncthreads();  // every wave is done with its K/V buffers
   if (grp == 0) {
