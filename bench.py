@@ -13,6 +13,7 @@ before timing starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -47,10 +48,11 @@ def parse():
 
 
 def cpu_baseline(w, x, target_s):
-    """Time the fp64 oracle on a bounded sample of the same workload: head 0,
-    its coarse branch and selection for every sparse row, and the fine branch
-    of as many query tiles (dense and sparse alternately) as fit in about
-    target_s seconds.  Reported as effective TFLOP/s over the sampled pairs."""
+    """Time the fp64 oracle on a bounded sample of the same workload: heads in
+    order, each with its pooling, coarse branch and selection and then the fine
+    branch of its query tiles (dense and sparse alternately, in growing
+    batches), until about target_s seconds have passed.  Reported as
+    effective TFLOP/s over the sampled pairs."""
     from threadpoolctl import threadpool_info
     from oracle import vsa_oracle as O
     geom = O.map_geometry(w.segments(), *w.grid)
@@ -61,26 +63,32 @@ def cpu_baseline(w, x, target_s):
             order.append(dense[i])
         if i < len(sparse):
             order.append(sparse[i])
-    Qh = O.bf16_bits_to_f64(x["q"][0, :, 0])
-    Kh = O.bf16_bits_to_f64(x["k"][0, :, 0])
-    Vh = O.bf16_bits_to_f64(x["v"][0, :, 0])
-    Gh = O.bf16_bits_to_f64(x["g"][0, :, 0])
+    dense_set = set(dense)
     k = O.keep_count(w.keep, geom.n_video)
     t0 = time.perf_counter()
-    rows = []
-    n = 1
+    rows = 0
     pairs = 0
-    while True:
-        batch = order[len(rows):len(rows) + n]
-        if not batch:
+    heads = 0
+    done = False
+    for h in range(w.heads):
+        Qh = O.bf16_bits_to_f64(x["q"][0, :, h])
+        Kh = O.bf16_bits_to_f64(x["k"][0, :, h])
+        Vh = O.bf16_bits_to_f64(x["v"][0, :, h])
+        Gh = O.bf16_bits_to_f64(x["g"][0, :, h])
+        heads += 1
+        pos, n = 0, 1
+        while pos < len(order):
+            batch = order[pos:pos + n]
+            O.forward_head(Qh, Kh, Vh, Gh, geom, w.keep, w.sink, w.select, w.coarse, w.tau, rows=batch)
+            pos += len(batch)
+            rows += len(batch)
+            pairs += sum(geom.n_tiles if r in dense_set else geom.n_prefix + k for r in batch)
+            if time.perf_counter() - t0 >= target_s:
+                done = True
+                break
+            n = min(64, n * 2)
+        if done:
             break
-        O.forward_head(Qh, Kh, Vh, Gh, geom, w.keep, w.sink, w.select, w.coarse, w.tau, rows=batch)
-        rows.extend(batch)
-        pairs += sum(geom.n_tiles if r in dense else geom.n_prefix + k for r in batch)
-        el = time.perf_counter() - t0
-        if el >= target_s:
-            break
-        n = min(64, n * 2)
     el = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
@@ -88,10 +96,11 @@ def cpu_baseline(w, x, target_s):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, head 0 of the same inputs: pooling + coarse + selection "
-                   f"for each sampled row and the fine branch of {len(rows)} of {geom.n_tiles} query "
-                   f"tiles ({pairs} pairs) in {el:.1f} s; dense and sparse rows alternate"),
-        "seconds": el,
+        "sample": (f"fp64 numpy oracle on the same inputs, heads taken in order ({heads} started): "
+                   f"pooling + coarse + selection per head and the fine branch of {rows} query-tile rows "
+                   f"({pairs} pairs of {w.heads * (geom.n_video * (geom.n_prefix + k) + geom.n_prefix * geom.n_tiles) if w.sink == 2 else 'n/a'}) "
+                   f"in {el:.1f} s; dense and sparse rows alternate"),
+        "seconds": round(el, 2),
     }
 
 
@@ -138,16 +147,18 @@ def main():
     torch.cuda.synchronize()
     stats = V.vsa_read_stats(plan, ws)
     timer.reset()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(a.steps):
+    evs[0].record(stream)
+    for i in range(a.steps):
         V.vsa_forward_timed(plan, q, k, v, g, o, ws, timer)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms = total_ms / a.steps
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
+    median_ms = per_call[len(per_call) // 2] if len(per_call) % 2 else 0.5 * (
+        per_call[len(per_call) // 2 - 1] + per_call[len(per_call) // 2])
     kt = timer.read()
     flop = stats["executed_pairs"] * PAIR_FLOP
     tflops = flop / (ms * 1e-3) / 1e12
@@ -155,10 +166,17 @@ def main():
     fine_launches, fine_ms = kt["fine"]
     fine_avg_ms = fine_ms / fine_launches
     fine_tflops = flop / (fine_avg_ms * 1e-3) / 1e12
+    # measured HBM bytes per fine launch, valid only for the kernel source the counters were
+    # taken on (and the workload they were taken for)
     traffic = None
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+            t = json.load(f)
+        src = os.path.join(ROOT, "block_sparse_video_geometry_amd", "csrc", "k_fine.hip")
+        with open(src, "rb") as f:
+            cur = hashlib.sha256(f.read()).hexdigest()[:16]
+        if t.get("kernel_source_sha256_16") == cur and t.get("workload") == w.name:
+            traffic = t.get("bytes_per_launch")
     kernels = {n: {"launches": c, "avg_us": 1e3 * t / max(c, 1)} for n, (c, t) in kt.items()}
     N, H = w.n_tokens, w.heads
     tensor_bytes = w.batch * N * H * 128 * 2
@@ -175,6 +193,7 @@ def main():
         "warmup": a.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_layer": round(ms, 4),
+        "ms_per_layer_median": round(median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

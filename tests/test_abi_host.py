@@ -72,6 +72,8 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, batch=0), -1),
     (dict(segs=[(i * 4, 4, 0) for i in range(17)] + [(68, 1024, 4)]), -2),   # > 16 prefix spans
     (dict(segs=[(0, 64, 0), (64, 4 * 4 * 4 * 64 * 65, 4)], T=4, H=256, W=260), -2),  # > 4096 video tiles
+    (dict(segs=GOOD, heads=7000), 0),                                 # N*H*128 just under 2^30
+    (dict(segs=GOOD, heads=7300), -2),                                # N*H*128 >= 2^30 (32-bit offsets)
 ])
 def test_plan_validation(case, expect):
     assert plan_status(**case) == expect
