@@ -93,21 +93,6 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
-// Reductions over the four lanes ql, ql + 16, ql + 32, ql + 48 (one query's partial values)
-// with the row-swap VALU permutes, which do not go through the LDS queue.
-__device__ __forceinline__ float group_max(float m) {
-  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float x) {
-  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }

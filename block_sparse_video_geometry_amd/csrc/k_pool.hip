@@ -10,18 +10,18 @@
 //
 // HBM-bound: each (tile, head) slice of Q, K, V is read once; one wave per
 // (tile, head), 16 lanes per token (16 x 16 B = one 256-byte head row), four
-// tokens per load instruction, all 16 loads of a tile in flight.
+// tokens per load instruction; a video tile's 48 loads (Q, K, V) are all in flight at once.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace {
 
-// Sum of this wave's 64 tile rows of one head: lane group grp = lane/16 owns
-// rows 4p + grp, lane chunk c = lane%16 owns dims 8c..8c+7.  Result reduced
-// over the four groups (every lane holds its chunk's sums).
-__device__ __forceinline__ void tile_sum(const VsaGeom& g, const u32x4* __restrict__ X, int b,
-                                         int h, int t, int grp, int c, float acc[8]) {
-  u32x4 buf[16];
+// This wave's 64 tile rows of one head: lane group grp = lane/16 owns rows 4p + grp, lane
+// chunk c = lane%16 owns dims 8c..8c+7.  tile_load only issues the loads, so a wave can
+// have the Q, K and V rows of a tile in flight at once; tile_sum reduces them over the
+// four groups (every lane holds its chunk's sums).
+__device__ __forceinline__ void tile_load(const VsaGeom& g, const u32x4* __restrict__ X, int b, int h,
+                                          int t, int grp, int c, u32x4 buf[16]) {
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
     const int tok = tile_token(g, t, 4 * p + grp);
@@ -30,6 +30,8 @@ __device__ __forceinline__ void tile_sum(const VsaGeom& g, const u32x4* __restri
     else
       buf[p] = u32x4{0u, 0u, 0u, 0u};
   }
+}
+__device__ __forceinline__ void tile_sum(const u32x4 buf[16], float acc[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
@@ -41,10 +43,7 @@ __device__ __forceinline__ void tile_sum(const VsaGeom& g, const u32x4* __restri
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i] += __shfl_xor(acc[i], 16);
-    acc[i] += __shfl_xor(acc[i], 32);
-  }
+  for (int i = 0; i < 8; ++i) acc[i] = group_sum(acc[i]);
 }
 
 __device__ __forceinline__ void store8(float* dst, const float v[8], float mul) {
@@ -60,22 +59,34 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* _
                                                        float* __restrict__ kbar,
                                                        float* __restrict__ vbar,
                                                        float* __restrict__ bias) {
-  const int t = blockIdx.x;
+  // head groups fastest: consecutive workgroups read neighbouring 1 KB pieces of the same
+  // token rows, which keeps HBM page locality
+  const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + wave;
+  const int h = blockIdx.x * 4 + wave;
   const int b = blockIdx.z;
   if (h >= g.heads) return;
   const int grp = lane >> 4, c = lane & 15;
   const size_t bh = (size_t)b * g.heads + h;
   const float inv = 1.0f / (float)tile_valid(g, t);
   float acc[8];
-  tile_sum(g, q, b, h, t, grp, c, acc);
-  if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
-  if (t < g.P) return;
+  u32x4 bq[16];
+  tile_load(g, q, b, h, t, grp, c, bq);
+  if (t < g.P) {
+    tile_sum(bq, acc);
+    if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+    return;
+  }
+  // video tile: all 48 loads in flight before the first sum
+  u32x4 bk[16], bv[16];
+  tile_load(g, k, b, h, t, grp, c, bk);
+  tile_load(g, v, b, h, t, grp, c, bv);
   const int j = t - g.P;
-  tile_sum(g, k, b, h, t, grp, c, acc);
+  tile_sum(bq, acc);
+  if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  tile_sum(bk, acc);
   if (grp == 0) store8(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
-  tile_sum(g, v, b, h, t, grp, c, acc);
+  tile_sum(bv, acc);
   if (grp == 0) store8(vbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
   if (g.coarse == VSA_COARSE_MEAN && lane == 0) bias[bh * g.Vt + j] = 0.0f;
 }
@@ -106,9 +117,9 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
                                                           const float* __restrict__ kbar,
                                                           const float* __restrict__ anchor,
                                                           float* __restrict__ bias) {
-  const int j = blockIdx.x;
+  const int j = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + wave;
+  const int h = blockIdx.x * 4 + wave;
   const int b = blockIdx.z;
   if (h >= g.heads) return;
   const int grp = lane >> 4, c = lane & 15;
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
 
 void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void* v, float* qbar,
                      float* kbar, float* vbar, float* bias, hipStream_t st) {
-  dim3 grid(g.Tq, (g.heads + 3) / 4, g.batch);
+  dim3 grid((g.heads + 3) / 4, g.Tq, g.batch);
   hipLaunchKernelGGL(vsa_pool_kernel, grid, dim3(256), 0, st, g, (const u32x4*)q, (const u32x4*)k,
                      (const u32x4*)v, qbar, kbar, vbar, bias);
 }
@@ -168,7 +179,7 @@ void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipSt
 
 void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
                         float* bias, hipStream_t st) {
-  dim3 grid(g.Vt, (g.heads + 3) / 4, g.batch);
+  dim3 grid((g.heads + 3) / 4, g.Vt, g.batch);
   hipLaunchKernelGGL(vsa_logmass_kernel, grid, dim3(256), 0, st, g, (const u32x4*)k, kbar, anchor,
                      bias);
 }

@@ -68,3 +68,19 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
   return x;
 }
+
+// Reductions over the four lanes l, l + 16, l + 32, l + 48 (rows of the wave) with the
+// row-swap VALU permutes, which do not go through the LDS queue.
+__device__ __forceinline__ float group_max(float m) {
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+

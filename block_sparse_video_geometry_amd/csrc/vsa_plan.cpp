@@ -109,6 +109,10 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     return VSA_ERR_UNSUPPORTED;
   }
   g.Tq = g.P + g.Vt;
+  if (g.Tq > 65535) {  // tiles index the second grid dimension of the pooling launches
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
   g.N = (int32_t)N;
   g.heads = heads;
   g.batch = batch;

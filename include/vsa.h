@@ -61,7 +61,8 @@ typedef enum {
   VSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad spans, negative sizes, aliasing */
   VSA_ERR_UNSUPPORTED = -2,      /* outside what the kernels implement: head_dim != 128,
                                     grid dims not multiples of 4, not exactly one video span,
-                                    keep outside (0, 100], > 4096 video tiles, > 16 prefix
+                                    keep outside (0, 100], > 4096 video tiles, > 65535
+                                    tiles in all, > 16 prefix
                                     segments, a sparse row list longer than 2048 tiles
                                     (P + k, or P + Vt in TAU mode), N * heads * head_dim
                                     >= 2^30 (one batch item's Q, K or V is addressed

@@ -72,6 +72,7 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, batch=0), -1),
     (dict(segs=[(i * 4, 4, 0) for i in range(17)] + [(68, 1024, 4)]), -2),   # > 16 prefix spans
     (dict(segs=[(0, 64, 0), (64, 4 * 4 * 4 * 64 * 65, 4)], T=4, H=256, W=260), -2),  # > 4096 video tiles
+    (dict(segs=[(0, 64 * 65536, 0), (64 * 65536, 1024, 4)], heads=1), -2),  # > 65535 tiles
     (dict(segs=GOOD, heads=7000), 0),                                 # N*H*128 just under 2^30
     (dict(segs=GOOD, heads=7300), -2),                                # N*H*128 >= 2^30 (32-bit offsets)
 ])

@@ -169,3 +169,23 @@ def test_parity_full_size_sampled(name):
     rep = PAR.check_parity(w, x, gpu, heads=heads, rows=rows)
     print(f"[parity-full] {name}: rows={rep['rows']} exact={rep['exact_rows']} adopted={rep['adopted_rows']} "
           f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e}", flush=True)
+
+
+def test_parity_growing_logits():
+    """Keys scaled up tile by tile (x1 for the prefix tile, up to x8.5 for the last video
+    tile), so along every row's list the running max grows by far more than the lazy
+    threshold: the rare rescale of O and l runs several times per row."""
+    from workloads.synth import bf16_bits_to_f32, f32_to_bf16_bits
+    w = Workload("growing_logits", 2, ((SEG_TEXT, 64),), (8, 8, 16), 100.0, SINK_EXACT_KV_AND_ROWS,
+                 seed=81, recipe="iid")
+    x = make_inputs(w)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    kf = bf16_bits_to_f32(x["k"])
+    for t, toks in enumerate(geom.tiles):
+        kf[:, toks] *= np.float32(1.0 + 0.5 * t)
+    x = dict(x, k=f32_to_bf16_bits(kf))
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[parity] growing_logits: rows={rep['rows']} max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e}",
+          flush=True)
