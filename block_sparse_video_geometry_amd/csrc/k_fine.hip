@@ -14,19 +14,21 @@
 // waves split the row's key-tile list (wave w takes entries w, w+4, ...) and
 // each runs all 64 queries against its tiles, so every K/V byte is read from
 // LDS once.  Per wave and tile:
-//   K, V tiles  -> LDS by direct global->LDS DMA (global_load_lds_dwordx4),
-//                  16 KB each, XOR-swizzled 16-byte chunks; the next tile's K
-//                  is fetched while this tile's softmax and PV run, its V while
-//                  the next QK runs.  Waits are per wave (vmcnt), no barriers.
+//   K, V tiles  -> LDS by direct buffer->LDS DMA (buffer_load_dwordx4 ... lds),
+//                  16 KB each, XOR-swizzled 16-byte chunks, refilled by 32-row
+//                  halves as soon as a half has been read.  Waits are per wave
+//                  (vmcnt), no barriers.
 //   S^T (64 keys x 64 queries) = K . Q^T     64 x mfma_f32_16x16x32_bf16
-//   online softmax in fp32 with exp2; the running max moves only when a row's
-//   max grows by more than 2^16, so the O rescale is skipped on almost every tile
-//   O^T (128 x 64) += V^T . P^T               64 x mfma_f32_16x16x32_bf16,
-//                  V^T operands read with ds_read_b64_tr_b16
+//   online softmax in fp32 with exp2, software-pipelined: the softmax of tile j
+//   runs on the VALU between the QK MFMAs of tile j+1.  The running max moves
+//   only when a row's max grows by more than 2^16, so the O rescale is skipped
+//   on almost every tile.
+//   O (64 x 128) += P . V                     64 x mfma_f32_16x16x32_bf16,
+//                  V operands read with ds_read_b64_tr_b16
 // S^T puts keys on MFMA rows: each lane holds one query per 16-query block,
 // and the key order inside every 32-key step is permuted (kperm) so a lane's
-// eight probabilities are eight consecutive keys -- exactly the P^T operand
-// of the PV product, with no register shuffles.  At the end the four waves'
+// eight probabilities are eight consecutive keys -- exactly the P operand of
+// the PV product, with no register shuffles.  At the end the four waves'
 // (max, sum, O) partials are merged through LDS and each wave writes 16 query
 // rows (gate combine, bf16 round-to-nearest-even, packed order).
 //
@@ -126,6 +128,8 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   __shared__ __attribute__((aligned(16))) float sbuf[NW][64];
   __shared__ int lst_lds[LIST_LDS];
   __shared__ int seg_lds[3][VSA_MAX_PREFIX_SEGS + 1];  // prefix segment table (start, len, tile0)
+  __shared__ __attribute__((aligned(16))) char glds[64 * VSA_HEAD_DIM * 2];  // the tile's gate rows
+  __shared__ __attribute__((aligned(16))) char oclds[1024];  // its coarse output row (first 512 B)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -136,23 +140,9 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   const int b = bh / g.heads, h = bh - b * g.heads;
   const bool dense = qt < g.n_dense;
   const int srow = qt - g.n_dense;
-  int nlist;
-  if (dense) {
-    nlist = g.Tq;
-  } else {
-    nlist = min(counts[(size_t)bh * g.Qs + srow], g.cap);  // cap <= LIST_LDS (plan)
-    const int* lst = lists + ((size_t)bh * g.Qs + srow) * g.cap;
-    for (int i = tid; i < nlist; i += 256) lst_lds[i] = lst[i];
-  }
-  if (tid <= VSA_MAX_PREFIX_SEGS) {
-    seg_lds[0][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_start[tid] : 0;
-    seg_lds[1][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_len[tid] : 0;
-    seg_lds[2][tid] = g.pre_tile0[tid];
-  }
-  __syncthreads();
-
   const int grp = lane >> 4, ql = lane & 15;
-  // Q^T operands: lane holds queries 16 qb + ql, dims 32 ks + 8 grp .. +7
+  // Q^T operands: lane holds queries 16 qb + ql, dims 32 ks + 8 grp .. +7.  Issued first,
+  // so they land while the list is staged.
   bf16x8 qv[4][4];
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
@@ -166,14 +156,57 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       for (int ks = 0; ks < 4; ++ks) qv[qb][ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
   }
-  // Q must be in registers before the first DMA: a wait the compiler sees, so it does not
-  // re-wait (whole queue) for these loads inside the loop
-  __builtin_amdgcn_s_waitcnt(0);
+
+  const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
+  const long long bh_off = ((long long)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2);
+  // One buffer resource per tensor over this (b, h) plane.  Offsets past its last byte read
+  // zero: the padding rows of a partial prefix tile at the end of the sequence, and the
+  // loads for the tile after a wave's last one (offset >= 2^31, never in range).
+  const int nrec = (int)((unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2);
+  constexpr unsigned NO_TILE = 0x80000000u;
+
+  // The epilogue's operands are copied to LDS now, so it waits on no global load: the
+  // tile's gate rows (instruction n of wave w covers query rows 16 w + 4 n .. +3, lane
+  // 16 r + c writing row 16 w + 4 n + r, chunk c; padding rows read zeros) and its coarse
+  // output row (lanes 0-31; lanes 32-63 read zeros past the end).
+  const bool gated = !dense && gate != nullptr;
+  if (gated) {
+    const __amdgpu_buffer_rsrc_t grs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)gate + bh_off), 0, nrec, 0x00020000);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int tok = tile_token(g, qt, 16 * wave + 4 * n + (lane >> 4));
+      const unsigned off = tok >= 0 ? (unsigned)tok * rowbytes + ((unsigned)(lane & 15) << 4) : NO_TILE;
+      bdma16(grs, off, 0u, lds_u32((lds_char*)(glds + 1024 * (4 * wave + n))));
+    }
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM), 0, VSA_HEAD_DIM * 4, 0x00020000);
+      bdma16(crs, (unsigned)lane << 4, 0u, lds_u32((lds_char*)oclds));
+    }
+  }
+
+  int nlist;
+  if (dense) {
+    nlist = g.Tq;
+  } else {
+    // the list is staged to its capacity (entries past the count are never read), so its
+    // loads need not wait for the count's
+    const int cnt = counts[(size_t)bh * g.Qs + srow];
+    const int* lst = lists + ((size_t)bh * g.Qs + srow) * g.cap;
+    for (int i = tid; i < g.cap; i += 256) lst_lds[i] = lst[i];  // cap <= LIST_LDS (plan)
+    nlist = min(cnt, g.cap);
+  }
+  if (tid <= VSA_MAX_PREFIX_SEGS) {
+    seg_lds[0][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_start[tid] : 0;
+    seg_lds[1][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_len[tid] : 0;
+    seg_lds[2][tid] = g.pre_tile0[tid];
+  }
+  __syncthreads();
 
   // DMA lane offsets: instruction n covers key rows 4n .. 4n+3; lane = 16 gi + pos writes
   // row 4n + gi, position pos, i.e. chunk pos ^ swizzle(4n + gi).  The swizzles depend on
   // n only through (n >> 1) & 3 (K) and (n >> 1) & 1 (V).
-  const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
   const int gi = lane >> 4, pos = lane & 15;
   unsigned koff[4], voff[2];
 #pragma unroll
@@ -182,31 +215,24 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   for (int m = 0; m < 2; ++m) voff[m] = gi * rowbytes + ((pos ^ ((2 * gi + 8 * m) & 15)) << 4);
   const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
   const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
-  const long long bh_off = ((long long)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2);
-  // One buffer resource per tensor over this (b, h) plane.  Offsets past its last byte read
-  // zero: the padding rows of a partial prefix tile at the end of the sequence, and the
-  // loads for the tile after a wave's last one (offset >= 2^31, never in range).
-  const int nrec = (int)((unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kptr + bh_off), 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vptr + bh_off), 0, nrec, 0x00020000);
-  constexpr unsigned NO_TILE = 0x80000000u;
 
   lds_char* kbuf = (lds_char*)(klds_all + wave * TILE_BYTES);
   lds_char* vbuf = (lds_char*)(vlds_all + wave * TILE_BYTES);
   const unsigned kbuf_u = lds_u32(kbuf), vbuf_u = lds_u32(vbuf);
 
   // LDS read bases (see the layout note above)
-  unsigned kbase[4], vbase[8];
+  unsigned kbase[4];
   {
     const unsigned lrow = (unsigned)(8 * (ql >> 2) + (ql & 3)) * 256;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kbase[ks] = kbuf_u + lrow + (((4 * ks + grp) ^ ql) << 4);
-    const unsigned vrow = (unsigned)(8 * grp + (ql >> 2)) * 256 + 8 * (ql & 1);
-    const int vm = (ql >> 2) + 4 * (grp & 1);
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      vbase[db] = vbuf_u + vrow + ((2 * (db ^ vm) + ((ql & 3) >> 1)) << 4);
   }
+  // V read address of dim block db: vbase0 + 32 (db ^ vm), computed per use (an XOR and
+  // an add) to keep eight address registers free
+  const unsigned vbase0 = vbuf_u + (unsigned)(8 * grp + (ql >> 2)) * 256 + 8 * (ql & 1) + (((ql & 3) >> 1) << 4);
+  const unsigned vm = (unsigned)((ql >> 2) + 4 * (grp & 1));
 
   // Tile descriptors, 64 at a time: lane l describes this wave's tile 64 batch + l.
   // off = byte offset of the tile's first token row in the (b, h) plane;
@@ -267,97 +293,214 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     lsum[qb] = 0.f;
   }
   const float sl2 = g.scale * LOG2E;
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Per tile t: V(t) is fetched while QK(t) runs (one row group per four MFMAs), K(t+1)
-  // while the softmax of t runs.  At the top of an iteration only K(t) is outstanding.
-  unsigned c_off = 0, c_flags = 0;  // current tile
+  // K operand of MFMA step s = (key block s >> 2, dims 32 (s & 3) ..): rows kperm, see the
+  // layout note
+  auto kread = [&](int s) -> bf16x8 {
+    const int kb = s >> 2;
+    return as_bf16x8(*(const lds_u32x4*)(size_t)(kbase[s & 3] + 256 * (32 * (kb >> 1) + 4 * (kb & 1))));
+  };
+  // V operand of PV step u = (32-key step c = u >> 3, dim block db = u & 7)
+  auto vread = [&](int u) -> bf16x8 {
+    const unsigned c = (unsigned)u >> 3, db = (unsigned)u & 7;
+    const unsigned a0 = vbase0 + ((db ^ vm) << 5) + 256 * (32 * c);
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a0);
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a0 + 1024));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
+    const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
+    return as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+  };
+  // Keys past the end of a partial tile never win.  Lane holds keys
+  // 32 (kb >> 1) + 8 grp + 4 (kb & 1) + i of queries 16 qb + ql.
+  auto mask = [&](f32x4 (&s)[4][4], int nvalid) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool dead = 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i >= nvalid;
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) s[kb][qb][i] = dead ? -INFINITY : s[kb][qb][i];
+      }
+  };
+
+  // Tile pipeline.  Iteration j starts with S(j) in registers and runs two phases:
+  //   R1: S(j+1) = K(j+1) Q^T on the MFMAs (key rows 0-31, then 32-63), with the softmax
+  //       of S(j) on the VALU in between;
+  //   R2: O += P(j) V(j) on the MFMAs (key rows 0-31 of V, then 32-63), with the moves of
+  //       S(j+1) out of the accumulator registers in between.
+  // So the exp work of one tile runs under the MFMAs of the next.  The K and V buffers are
+  // refilled by 32-row halves as soon as a half has been read, one load per four MFMAs:
+  //   R1 first half:  V(j) rows 32-63      R1 second half: K(j+2) rows 0-31
+  //   R2 first half:  K(j+2) rows 32-63    R2 second half: V(j+1) rows 0-31
+  // Every half lands at least half a phase after it was issued; each wait leaves the 15 or
+  // 16 loads issued after the awaited half in flight.  P(j) is taken against
+  // the running max as it stands; the tile's own max comes out of the same pass and, in
+  // the rare case it passes the running max by more than RESCALE_TH, the max is moved
+  // (O and l rescaled) and P(j) is taken again.
+  unsigned c_off = NO_TILE, c_flags = 0, n_off = NO_TILE, n_flags = 0;
+  f32x4 scur[4][4];
   if (my_n > 0) {
     describe(0);
     c_off = __builtin_amdgcn_readlane(d_off, 0);
     c_flags = __builtin_amdgcn_readlane(d_flags, 0);
+    if (my_n > 1) {
+      n_off = __builtin_amdgcn_readlane(d_off, 1);
+      n_flags = __builtin_amdgcn_readlane(d_flags, 1);
+    }
     unsigned stp, stl;
     steps(c_flags, stp, stl);
 #pragma unroll
     for (int n = 0; n < 16; ++n) kdma(n, c_off, stp, stl);
   }
-  for (int j = 0; j < my_n; ++j) {
-    unsigned n_off = NO_TILE, n_flags = 0;
-    if (j + 1 < my_n) {
-      if (((j + 1) & 63) == 0) describe((j + 1) >> 6);
-      n_off = __builtin_amdgcn_readlane(d_off, (j + 1) & 63);
-      n_flags = __builtin_amdgcn_readlane(d_flags, (j + 1) & 63);
-    }
-    const int nvalid = (int)(c_flags >> 1);
-    unsigned c_stp, c_stl, n_stp, n_stl;
-    steps(c_flags, c_stp, c_stl);
-    steps(n_flags, n_stp, n_stl);
-
-    // ---- S^T = K Q^T (K(t) landed), with the V(t) loads spread over the MFMAs
-    wait_vm<0>();
-    f32x4 sacc[4][4];
+  // Q, the epilogue's copies and K(0) landed.  A wait the compiler sees, on every path to
+  // the loop, so it does not wait (whole queue) for the Q loads again inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
+  if (my_n > 0) {
+    unsigned stp, stl;
+    steps(c_flags, stp, stl);
     {
-      // operands of key block kb+1 are read while the 16 MFMAs of block kb issue
-      bf16x8 ka[2][4];
-      auto kread = [&](int kb, bf16x8* dst) {
+      f32x4 s0[4][4];
+      bf16x8 ka[2];
+      ka[0] = kread(0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          dst[ks] = as_bf16x8(*(const lds_u32x4*)(size_t)(kbase[ks] + 256 * (32 * (kb >> 1) + 4 * (kb & 1))));
-      };
-      kread(0, ka[0]);
+      for (int s = 0; s < 16; ++s) {
+        if (s < 15) ka[(s + 1) & 1] = kread(s + 1);
+        const int kb = s >> 2, ks = s & 3;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3) kread(kb + 1, ka[(kb + 1) & 1]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb)
-            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                ka[kb & 1][ks], qv[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[kb][qb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          vdma(4 * kb + ks, c_off, c_stp, c_stl);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int qb = 0; qb < 4; ++qb)
+          s0[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s & 1], qv[qb][ks],
+                                                               ks == 0 ? zero4 : s0[kb][qb], 0, 0, 0);
       }
-    }
-    // K buffer is free once its reads returned
-    wait_lgkm0();
-#pragma unroll
-    for (int n = 0; n < 4; ++n) kdma(n, n_off, n_stp, n_stl);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- online softmax; lane holds keys 32(kb>>1) + 8 grp + 4(kb&1) + i of queries 16 qb + ql
-    if (nvalid < VSA_TILE_TOKENS) {
+      // S(0) to VGPRs by the same explicit moves as every later tile, so S stays in one
+      // register file across the loop.  The scheduling barrier keeps every MFMA above the
+      // NOPs, which cover the MFMA-result-to-VALU-read latency the compiler does not see
+      // through the asm moves.
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-          if (key >= nvalid)
+        for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) sacc[kb][qb][i] = -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i) scur[kb][qb][i] = acc_read(s0[kb][qb][i]);
     }
-    float mloc[4];
-    bool grow = false;
+    // K buffer is free once its reads returned: K(1) (zeros past the end of the list), then
+    // V(0) rows 0-31, as iteration 0 expects them in flight
+    wait_lgkm0();
+    unsigned n_stp, n_stl;
+    steps(n_flags, n_stp, n_stl);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) vdma(n, c_off, stp, stl);
+    if ((int)(c_flags >> 1) < VSA_TILE_TOKENS) mask(scur, (int)(c_flags >> 1));
+    // the first tile sets the running max
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      float m = sacc[0][qb][0];
+      float m = scur[0][qb][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[kb][qb][i]);
-      mloc[qb] = group_max(m) * sl2;
-      grow |= mloc[qb] > mrun[qb] + RESCALE_TH;
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, scur[kb][qb][i]);
+      mrun[qb] = group_max(m) * sl2;
     }
-    if (j == 0) {
-      // first tile: O and l are still zero, only the running max is set
+  }
+
+  for (int j = 0; j < my_n; ++j) {
+    unsigned nn_off = NO_TILE, nn_flags = 0;
+    if (j + 2 < my_n) {
+      if (((j + 2) & 63) == 0) describe((j + 2) >> 6);
+      nn_off = __builtin_amdgcn_readlane(d_off, (j + 2) & 63);
+      nn_flags = __builtin_amdgcn_readlane(d_flags, (j + 2) & 63);
+    }
+    unsigned c_stp, c_stl, n_stp, n_stl, nn_stp, nn_stl;
+    steps(c_flags, c_stp, c_stl);
+    steps(n_flags, n_stp, n_stl);
+    steps(nn_flags, nn_stp, nn_stl);
+
+    // softmax of S(j), chunk s = (key block s >> 2, query block s & 3): P against the
+    // running max, the tile max and the tile's row sums on the way; P packed to bf16
+    // PV operands once both key blocks of a 32-key step are done
+    bf16x8 pb[4][2];
+    float tmax[4], lt[4];
+    unsigned pe[4][2];  // bf16 pairs of the even key block, until its odd partner is done
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) mrun[qb] = mloc[qb];
-    } else if (__ballot(grow)) {  // wave-uniform, rare: move the running max, rescale O and l
+    for (int qb = 0; qb < 4; ++qb) {
+      tmax[qb] = -INFINITY;
+      lt[qb] = 0.f;
+    }
+    auto soft = [&](int s) {
+      const int kb = s >> 2, qb = s & 3;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = scur[kb][qb][i];
+        tmax[qb] = fmaxf(tmax[qb], x);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(x, sl2, -mrun[qb]));
+        lt[qb] += p[i];
+      }
+      if (kb & 1) {
+        pb[qb][kb >> 1] = as_bf16x8(u32x4{pe[qb][0], pe[qb][1], pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+      } else {
+        pe[qb][0] = pack_bf16x2(p[0], p[1]);
+        pe[qb][1] = pack_bf16x2(p[2], p[3]);
+      }
+    };
+
+    // ---- R1.  On the last tile the K buffer holds the zeros loaded for the tile past the
+    // end; that product is not used, and costs nothing next to the softmax beside it.
+    // K(j+1) rows 0-31 landed (in flight after them: K(j+1) rows 32-63, V(j) rows 0-31).
+    wait_vm<16>();
+    f32x4 snext[4][4];
+    {
+      bf16x8 ka[2];
+      ka[0] = kread(0);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        // K(j+1) rows 32-63 landed before their first read (in flight after them: V(j)
+        // rows 0-31 and the 7 loads of V(j) rows 32-63 issued so far)
+        if (s == 7) wait_vm<15>();
+        if (s < 15) ka[(s + 1) & 1] = kread(s + 1);
+        const int kb = s >> 2, ks = s & 3;
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          snext[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s & 1], qv[qb][ks],
+                                                                  ks == 0 ? zero4 : snext[kb][qb], 0, 0, 0);
+        soft(s);
+        if (s < 15) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s < 8)
+          vdma(8 + s, c_off, c_stp, c_stl);  // V(j) rows 32-63
+        else
+          kdma(s - 8, nn_off, nn_stp, nn_stl);  // K(j+2) rows 0-31 (read by steps 0-7)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // P(j) and its row sums are produced above, under the MFMAs, even though the rare
+    // path below takes them again: an empty asm that reads and rewrites them keeps the
+    // compiler from sinking that work past the check.
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      asm volatile("" : "+v"(pb[qb][0]), "+v"(pb[qb][1]), "+v"(lt[qb]));
+    }
+
+    // ---- the max check (wave-uniform; rarely taken).  A row's tile max passes the
+    // threshold iff one of its four lanes' maxima does, so the lanes compare their own.
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) grow |= tmax[qb] * sl2 > mrun[qb] + RESCALE_TH;
+    if (__ballot(grow)) {
       float alpha[4];
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const float mn = fmaxf(mrun[qb], mloc[qb]);
+        const float mn = fmaxf(mrun[qb], group_max(tmax[qb]) * sl2);
         alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - mn);
         mrun[qb] = mn;
         lsum[qb] *= alpha[qb];
@@ -375,6 +518,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
       // The B operands are read out of the accumulator file by explicit moves inside this
       // branch (the compiler would otherwise copy all 128 accumulators on every iteration);
       // the NOPs cover the MFMA-result-to-VALU-read latency for those moves.
+      __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int db = 0; db < 8; ++db)
@@ -383,84 +527,64 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
           float ob[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) ob[i] = acc_read(oacc[db][qb][i]);
-          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][0], ob[0], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                           0, 0, 0);
+          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][0], ob[0], zero4, 0, 0, 0);
 #pragma unroll
           for (int i = 1; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][i], ob[i], acc, 0, 0, 0);
           oacc[db][qb] = acc;
         }
+      // P(j) again, against the moved max
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) lt[qb] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) soft(s);
     }
-    // P = exp2(S sl2 - m) as bf16 PV operands, with the rest of K(t+1) in between
-    bf16x8 pb[4][2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float p[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][i], sl2, -mrun[qb]));
-          lsum[qb] += p[kb][i];
-        }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 w;
-        w[0] = pack_bf16x2(p[2 * c][0], p[2 * c][1]);
-        w[1] = pack_bf16x2(p[2 * c][2], p[2 * c][3]);
-        w[2] = pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]);
-        w[3] = pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3]);
-        pb[qb][c] = as_bf16x8(w);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int n = 0; n < 3; ++n) kdma(4 + 3 * qb + n, n_off, n_stp, n_stl);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int qb = 0; qb < 4; ++qb) lsum[qb] += lt[qb];
 
-    // ---- O += P V (V(t) landed; the 16 loads of K(t+1) may be in flight)
+    // ---- R2.  K(j+1) reads returned (the K buffer may be refilled); V(j) rows 0-31 landed
+    // (in flight after them: V(j) rows 32-63, K(j+2) rows 0-31).
+    wait_lgkm0();
     wait_vm<16>();
+    // S(j+1) is read out of the accumulator registers below: cover the MFMA-result latency
+    // (the barrier keeps the QK MFMAs above the NOPs)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     {
-      // V operands of dim block db+1 (both 32-key steps) are read while the 8 MFMAs of
-      // block db issue
-      bf16x8 va[2][2];
-      auto vread = [&](int db, bf16x8* dst) {
+      // step u = (32-key step u >> 3, dim block u & 7); its V operand is read during step u-1
+      bf16x8 va[2];
+      va[0] = vread(0);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const unsigned a0 = vbase[db] + 256 * (32 * c);
-          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a0);
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(a0 + 1024));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, r0);
-          const u32x2 w1 = __builtin_bit_cast(u32x2, r1);
-          dst[c] = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+      for (int u = 0; u < 16; ++u) {
+        // V(j) rows 32-63 landed before their first read (in flight after them: K(j+2)
+        // rows 0-31 and the 7 loads of K(j+2) rows 32-63 issued so far)
+        if (u == 7) wait_vm<15>();
+        if (u < 15) va[(u + 1) & 1] = vread(u + 1);
+        const int c = u >> 3, db = u & 7;
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[qb][c], va[u & 1], oacc[db][qb], 0, 0, 0);
+          // four of the 64 values of S(j+1) per step: key block u >> 2, query block u & 3
+          scur[u >> 2][u & 3][qb] = acc_read(snext[u >> 2][u & 3][qb]);
         }
-      };
-      vread(0, va[0]);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if (db < 7) vread(db + 1, va[(db + 1) & 1]);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb)
-            oacc[db][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[qb][c], va[db & 1][c], oacc[db][qb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if (db < 7) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < 8)
+          kdma(8 + u, nn_off, nn_stp, nn_stl);  // K(j+2) rows 32-63 (read by R1 steps 8-15)
+        else
+          vdma(u - 8, n_off, n_stp, n_stl);  // V(j+1) rows 0-31 (read by steps 0-7)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // V buffer is free once its reads returned
     wait_lgkm0();
     c_off = n_off;
     c_flags = n_flags;
+    n_off = nn_off;
+    n_flags = nn_flags;
+    if (j + 1 < my_n && (int)(c_flags >> 1) < VSA_TILE_TOKENS) mask(scur, (int)(c_flags >> 1));
   }
-  // the loads issued for the tile after the last one (out of range, writing zeros) must
-  // land before the K buffer is reused below
+  // the loads issued past the end of the list (out of range, writing zeros) must land
+  // before the K buffer is reused below
   wait_vm<0>();
-
   // ---- merge the four waves' partials.  Softmax statistics are per lane for queries
   // 16 qb + ql; O is held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].
 #pragma unroll
@@ -517,9 +641,8 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int i = 0; i < 4; ++i) r[i][e] = s[i];
   }
   f32x4 oc0 = f32x4{0.f, 0.f, 0.f, 0.f}, oc1 = oc0;
-  const bool gated = !dense && gate != nullptr;
   if (gated) {
-    const f32x4* cp = reinterpret_cast<const f32x4*>(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM + 8 * dg);
+    const f32x4* cp = (const f32x4*)(oclds + 32 * dg);
     oc0 = cp[0];
     oc1 = cp[1];
   }
@@ -537,7 +660,7 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     for (int e = 0; e < 8; ++e) y[e] = r[i][e] * inv;
     const long long orow = row_offset(g, b, qtok, h) + 8 * dg;
     if (gated) {
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(gate + orow);
+      const u32x4 gv = *(const u32x4*)(glds + 256 * qq + 16 * dg);
       y[0] += bf16lo(gv[0]) * oc0[0];
       y[1] += bf16hi(gv[0]) * oc0[1];
       y[2] += bf16lo(gv[1]) * oc0[2];
