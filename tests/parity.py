@@ -8,9 +8,12 @@ valid top-k within GAP (size P + k, every prefix tile, every kept logit
 the GPU's list for that row before the outputs are compared.  Tau mode: the
 GPU must agree wherever |S - thr| > GAP and its choice is adopted elsewhere.
 
-Outputs, over every valid element produced: max |O_gpu - O_ref| <= 2e-2 and
-||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2 (bf16 inputs, fp32 accumulation,
-bf16 output).
+Outputs, over every valid element produced:
+|O_gpu - O_ref| <= 2e-2 + 2^-8 |O_ref| and ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2.
+The output is bf16, so rounding it alone moves an element by up to half an ulp,
+at most 2^-8 of its magnitude (up to 0.0156 for |O| in [4, 8)); 2e-2 bounds the
+rest (bf16 inputs, bf16 probabilities in the PV product, fp32 accumulation in
+any order).
 """
 from __future__ import annotations
 
@@ -21,6 +24,7 @@ from oracle import vsa_oracle as O
 GAP = 1e-4
 TOL_ABS = 2e-2
 TOL_REL = 1e-2
+OUT_ROUND = 2.0 ** -8  # bf16 output: half an ulp is at most this fraction of the value
 
 
 def bits_to_f64(b):
@@ -51,7 +55,7 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
     B, N, H, D = x["q"].shape
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
-    rep = dict(rows=0, exact_rows=0, adopted_rows=0, max_abs=0.0, err2=0.0, ref2=0.0,
+    rep = dict(rows=0, exact_rows=0, adopted_rows=0, max_abs=0.0, max_excess=0.0, err2=0.0, ref2=0.0,
                max_s_err=0.0, max_pool_err=0.0, max_oc_err=0.0, max_bias_err=0.0, s_mag=1.0,
                bias_mag=1.0)
     g_all = x.get("g")
@@ -134,11 +138,13 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
         assert np.all(np.isfinite(og)), f"(b{b},h{h}) non-finite GPU output"
         diff = og - orf
         rep["max_abs"] = max(rep["max_abs"], float(np.abs(diff).max()))
+        rep["max_excess"] = max(rep["max_excess"], float((np.abs(diff) - OUT_ROUND * np.abs(orf)).max()))
         rep["err2"] += float((diff ** 2).sum())
         rep["ref2"] += float((orf ** 2).sum())
         rep["rows"] += len(list(row_ids))
     rep["rel_l2"] = (rep["err2"] / rep["ref2"]) ** 0.5 if rep["ref2"] > 0 else 0.0
-    assert rep["max_abs"] <= tol_abs, f"max abs error {rep['max_abs']:.3g} > {tol_abs}"
+    assert rep["max_excess"] <= tol_abs, \
+        f"error beyond bf16 output rounding {rep['max_excess']:.3g} > {tol_abs} (max abs {rep['max_abs']:.3g})"
     assert rep["rel_l2"] <= tol_rel, f"relative L2 error {rep['rel_l2']:.3g} > {tol_rel}"
     if check_intermediates:
         # fp32 dot products of length 128 on pooled values: ~1e-6 relative to the logit size
