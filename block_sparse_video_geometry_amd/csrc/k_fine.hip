@@ -51,9 +51,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 // exponent range, and with logits of std 3 a rescale is then practically never needed
 // (at 2^8 about one tile in twelve paid for one).
 constexpr float RESCALE_TH = 16.0f;
-constexpr int NW = 4;                // waves per workgroup
 constexpr int TILE_BYTES = 16384;    // one 64 x 128 bf16 tile
-constexpr int LIST_LDS = VSA_MAX_LIST;  // a sparse row's list is staged whole in LDS
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -99,6 +97,14 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
+// A wave-uniform pointer, held in SGPRs (the buffer resources feed scalar asm operands)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const unsigned long long x = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return (const void*)(((unsigned long long)hi << 32) | lo);
+}
+
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -114,25 +120,20 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // the lane address is base_v[db] + 256 * (32c + 4h).
 // The DMA lane offsets below follow the same two swizzles.
 
-__global__ __launch_bounds__(256) void vsa_fine_kernel(
+__global__ __launch_bounds__(64) void vsa_fine_kernel(
     VsaGeom g, const char* __restrict__ kptr, const char* __restrict__ vptr,
     const u32x4* __restrict__ q, const unsigned short* __restrict__ gate,
     const float* __restrict__ ocoarse, const int* __restrict__ lists,
     const int* __restrict__ counts, unsigned short* __restrict__ o, int per_xcd) {
-  // per wave: a K tile and a V tile; separate arrays so LDS reads of one are never
-  // taken as aliasing DMA writes in flight to the other
-  __shared__ __attribute__((aligned(16))) char klds_all[NW * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char vlds_all[NW * TILE_BYTES];
-  __shared__ float mbuf[NW][64];
-  __shared__ float lbuf[NW][64];
-  __shared__ __attribute__((aligned(16))) float sbuf[NW][64];
-  __shared__ int lst_lds[LIST_LDS];
+  // a K tile and a V tile; separate arrays so LDS reads of one are never taken as aliasing
+  // DMA writes in flight to the other.  About 33 KB in all, so four workgroups share a CU.
+  __shared__ __attribute__((aligned(16))) char klds[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char vlds[TILE_BYTES];
+  __shared__ float lbuf[64];
   __shared__ int seg_lds[3][VSA_MAX_PREFIX_SEGS + 1];  // prefix segment table (start, len, tile0)
-  __shared__ __attribute__((aligned(16))) char glds[64 * VSA_HEAD_DIM * 2];  // the tile's gate rows
-  __shared__ __attribute__((aligned(16))) char oclds[1024];  // its coarse output row (first 512 B)
+  extern __shared__ int lst_lds[];                     // a sparse row's list (cap entries)
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int lane = threadIdx.x;
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (item >= g.batch * g.heads * g.Tq) return;
   const int bh = item / g.Tq;
@@ -165,27 +166,6 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   const int nrec = (int)((unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2);
   constexpr unsigned NO_TILE = 0x80000000u;
 
-  // The epilogue's operands are copied to LDS now, so it waits on no global load: the
-  // tile's gate rows (instruction n of wave w covers query rows 16 w + 4 n .. +3, lane
-  // 16 r + c writing row 16 w + 4 n + r, chunk c; padding rows read zeros) and its coarse
-  // output row (lanes 0-31; lanes 32-63 read zeros past the end).
-  const bool gated = !dense && gate != nullptr;
-  if (gated) {
-    const __amdgpu_buffer_rsrc_t grs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)gate + bh_off), 0, nrec, 0x00020000);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int tok = tile_token(g, qt, 16 * wave + 4 * n + (lane >> 4));
-      const unsigned off = tok >= 0 ? (unsigned)tok * rowbytes + ((unsigned)(lane & 15) << 4) : NO_TILE;
-      bdma16(grs, off, 0u, lds_u32((lds_char*)(glds + 1024 * (4 * wave + n))));
-    }
-    if (wave == 0) {
-      const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM), 0, VSA_HEAD_DIM * 4, 0x00020000);
-      bdma16(crs, (unsigned)lane << 4, 0u, lds_u32((lds_char*)oclds));
-    }
-  }
-
   int nlist;
   if (dense) {
     nlist = g.Tq;
@@ -194,13 +174,13 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
     // loads need not wait for the count's
     const int cnt = counts[(size_t)bh * g.Qs + srow];
     const int* lst = lists + ((size_t)bh * g.Qs + srow) * g.cap;
-    for (int i = tid; i < g.cap; i += 256) lst_lds[i] = lst[i];  // cap <= LIST_LDS (plan)
+    for (int i = lane; i < g.cap; i += 64) lst_lds[i] = lst[i];
     nlist = min(cnt, g.cap);
   }
-  if (tid <= VSA_MAX_PREFIX_SEGS) {
-    seg_lds[0][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_start[tid] : 0;
-    seg_lds[1][tid] = tid < VSA_MAX_PREFIX_SEGS ? g.pre_len[tid] : 0;
-    seg_lds[2][tid] = g.pre_tile0[tid];
+  if (lane <= VSA_MAX_PREFIX_SEGS) {
+    seg_lds[0][lane] = lane < VSA_MAX_PREFIX_SEGS ? g.pre_start[lane] : 0;
+    seg_lds[1][lane] = lane < VSA_MAX_PREFIX_SEGS ? g.pre_len[lane] : 0;
+    seg_lds[2][lane] = g.pre_tile0[lane];
   }
   __syncthreads();
 
@@ -215,11 +195,13 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   for (int m = 0; m < 2; ++m) voff[m] = gi * rowbytes + ((pos ^ ((2 * gi + 8 * m) & 15)) << 4);
   const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
   const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kptr + bh_off), 0, nrec, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vptr + bh_off), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(kptr + bh_off), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(vptr + bh_off), 0, nrec, 0x00020000);
 
-  lds_char* kbuf = (lds_char*)(klds_all + wave * TILE_BYTES);
-  lds_char* vbuf = (lds_char*)(vlds_all + wave * TILE_BYTES);
+  lds_char* kbuf = (lds_char*)klds;
+  lds_char* vbuf = (lds_char*)vlds;
   const unsigned kbuf_u = lds_u32(kbuf), vbuf_u = lds_u32(vbuf);
 
   // LDS read bases (see the layout note above)
@@ -234,15 +216,15 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   const unsigned vbase0 = vbuf_u + (unsigned)(8 * grp + (ql >> 2)) * 256 + 8 * (ql & 1) + (((ql & 3) >> 1) << 4);
   const unsigned vm = (unsigned)((ql >> 2) + 4 * (grp & 1));
 
-  // Tile descriptors, 64 at a time: lane l describes this wave's tile 64 batch + l.
+  // Tile descriptors, 64 at a time: lane l describes tile 64 batch + l of the list.
   // off = byte offset of the tile's first token row in the (b, h) plane;
   // flags = video | nvalid << 1.
-  const int my_n = nlist > wave ? (nlist - wave + NW - 1) / NW : 0;
+  const int my_n = nlist;
   unsigned d_off = 0, d_flags = 0;
   auto describe = [&](int batch) {
     const int j = batch * 64 + lane;
     int t = 0;
-    if (j < my_n) t = dense ? wave + NW * j : lst_lds[wave + NW * j];
+    if (j < my_n) t = dense ? j : lst_lds[j];
     int tok0, video, nvalid;
     if (t >= g.P) {
       const int jv = t - g.P;
@@ -585,93 +567,78 @@ __global__ __launch_bounds__(256) void vsa_fine_kernel(
   // the loads issued past the end of the list (out of range, writing zeros) must land
   // before the K buffer is reused below
   wait_vm<0>();
-  // ---- merge the four waves' partials.  Softmax statistics are per lane for queries
-  // 16 qb + ql; O is held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].
+  // ---- O and l to LDS.  Softmax statistics are per lane for queries 16 qb + ql; O is
+  // held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].  O^T goes to the K/V
+  // buffers: dims 0..63 in the K area, 64..127 in the V area, each dim a 256-byte row of
+  // 64 fp32 queries; the 16-byte chunk of queries 4c..4c+3 sits at chunk c ^ (dim & 15).
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     lsum[qb] = group_sum(lsum[qb]);
+    if (grp == 0) lbuf[16 * qb + ql] = lsum[qb];
   }
-  __syncthreads();  // every wave is done with its K/V buffers
-  if (grp == 0) {
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) mbuf[wave][16 * qb + ql] = mrun[qb];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const int qq = 16 * qb + ql;
-    float mt = mbuf[0][qq];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mt = fmaxf(mt, mbuf[w][qq]);
-    const float sc = mrun[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[qb] - mt);
-    if (grp == 0) {
-      lbuf[wave][qq] = lsum[qb] * sc;
-      sbuf[wave][qq] = sc;
-    }
-  }
-  __syncthreads();
-  // partial O^T of wave w: dims 0..63 in its K tile area, 64..127 in its V tile area, each
-  // dim a 256-byte row of 64 fp32 queries; the 16-byte chunk of queries 4c..4c+3 sits at
-  // chunk c ^ (dim & 15)
-  auto part = [&](int w, int d) -> lds_u32x4* {
-    return (lds_u32x4*)((d < 64 ? klds_all : vlds_all) + w * TILE_BYTES) + (d & 63) * 16;
+  auto part = [&](int d) -> lds_u32x4* {
+    return (lds_u32x4*)(d < 64 ? klds : vlds) + (d & 63) * 16;
   };
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const f32x4 sc4 = *(const f32x4*)&sbuf[wave][16 * qb + 4 * grp];
+  for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const f32x4 v = oacc[db][qb] * sc4;
-      part(wave, 16 * db + ql)[(4 * qb + grp) ^ ql] = __builtin_bit_cast(u32x4, v);
-    }
-  }
+    for (int db = 0; db < 8; ++db) part(16 * db + ql)[(4 * qb + grp) ^ ql] = __builtin_bit_cast(u32x4, oacc[db][qb]);
   __syncthreads();
 
-  // ---- epilogue: wave w writes queries 16 w + 4 (lane / 16) .. +3, dims 8 (lane % 16) .. +7
+  // ---- epilogue, four passes: pass w writes queries 16 w + 4 (lane / 16) .. +3, dims
+  // 8 (lane % 16) .. +7.  The gate and coarse-output loads are issued first.
   const int qg = lane >> 4, dg = lane & 15;
-  const int q0 = 16 * wave + 4 * qg;
-  float r[4][8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = 8 * dg + e;
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += __builtin_bit_cast(f32x4, part(w, d)[(q0 >> 2) ^ (d & 15)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i][e] = s[i];
-  }
+  const bool gated = !dense && gate != nullptr;
   f32x4 oc0 = f32x4{0.f, 0.f, 0.f, 0.f}, oc1 = oc0;
+  u32x4 gv[4][4];
+  int qtok[4][4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qtok[w][i] = tile_token(g, qt, 16 * w + 4 * qg + i);
+      gv[w][i] = u32x4{0u, 0u, 0u, 0u};
+      if (gated && qtok[w][i] >= 0)
+        gv[w][i] = *reinterpret_cast<const u32x4*>(gate + row_offset(g, b, qtok[w][i], h) + 8 * dg);
+    }
   if (gated) {
-    const f32x4* cp = (const f32x4*)(oclds + 32 * dg);
+    const f32x4* cp = reinterpret_cast<const f32x4*>(ocoarse + ((size_t)bh * g.Qs + srow) * VSA_HEAD_DIM + 8 * dg);
     oc0 = cp[0];
     oc1 = cp[1];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qq = q0 + i;
-    const int qtok = tile_token(g, qt, qq);
-    if (qtok < 0) continue;
-    float ltot = 0.f;
+  for (int w = 0; w < 4; ++w) {
+    const int q0 = 16 * w + 4 * qg;
+    float r[4][8];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) ltot += lbuf[w][qq];
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty list gives O_fine = 0
-    float y[8];
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * dg + e;
+      const f32x4 sv = __builtin_bit_cast(f32x4, part(d)[(q0 >> 2) ^ (d & 15)]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = r[i][e] * inv;
-    const long long orow = row_offset(g, b, qtok, h) + 8 * dg;
-    if (gated) {
-      const u32x4 gv = *(const u32x4*)(glds + 256 * qq + 16 * dg);
-      y[0] += bf16lo(gv[0]) * oc0[0];
-      y[1] += bf16hi(gv[0]) * oc0[1];
-      y[2] += bf16lo(gv[1]) * oc0[2];
-      y[3] += bf16hi(gv[1]) * oc0[3];
-      y[4] += bf16lo(gv[2]) * oc1[0];
-      y[5] += bf16hi(gv[2]) * oc1[1];
-      y[6] += bf16lo(gv[3]) * oc1[2];
-      y[7] += bf16hi(gv[3]) * oc1[3];
+      for (int i = 0; i < 4; ++i) r[i][e] = sv[i];
     }
-    *reinterpret_cast<u32x4*>(o + orow) = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                                pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (qtok[w][i] < 0) continue;
+      const float ltot = lbuf[q0 + i];
+      const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty list gives O_fine = 0
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = r[i][e] * inv;
+      if (gated) {
+        const u32x4 gw = gv[w][i];
+        y[0] += bf16lo(gw[0]) * oc0[0];
+        y[1] += bf16hi(gw[0]) * oc0[1];
+        y[2] += bf16lo(gw[1]) * oc0[2];
+        y[3] += bf16hi(gw[1]) * oc0[3];
+        y[4] += bf16lo(gw[2]) * oc1[0];
+        y[5] += bf16hi(gw[2]) * oc1[1];
+        y[6] += bf16lo(gw[3]) * oc1[2];
+        y[7] += bf16hi(gw[3]) * oc1[3];
+      }
+      *reinterpret_cast<u32x4*>(o + row_offset(g, b, qtok[w][i], h) + 8 * dg) =
+          u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    }
   }
 }
 
@@ -682,7 +649,7 @@ void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void*
                      hipStream_t st) {
   const int total = g.batch * g.heads * g.Tq;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(vsa_fine_kernel, dim3(8 * per_xcd), dim3(256), 0, st, g, (const char*)k,
+  hipLaunchKernelGGL(vsa_fine_kernel, dim3(8 * per_xcd), dim3(64), (size_t)g.cap * sizeof(int), st, g, (const char*)k,
                      (const char*)v, (const u32x4*)q, (const unsigned short*)gate, ocoarse, lists,
                      counts, (unsigned short*)o, per_xcd);
 }
