@@ -10,47 +10,49 @@
 // VSA", "Technical Architecture": the learned gate (to_gate_compress) scales
 // the compressed branch, O = O_fine + G * O_coarse.
 //
-// Work item: one (batch, head, query tile) per 256-thread workgroup.  The four
-// waves split the row's key-tile list (wave w takes entries w, w+4, ...) and
-// each runs all 64 queries against its tiles, so every K/V byte is read from
-// LDS once.  Per wave and tile:
+// Work item: one (batch, head, query tile) per 64-thread workgroup: one wave
+// runs all 64 queries against the row's whole key-tile list, so every K/V byte
+// is read from LDS once and no partials are merged.  About 33 KB of LDS, so
+// four workgroups (one per SIMD) share a CU.  Per tile:
 //   K, V tiles  -> LDS by direct buffer->LDS DMA (buffer_load_dwordx4 ... lds),
 //                  16 KB each, XOR-swizzled 16-byte chunks, refilled by 32-row
-//                  halves as soon as a half has been read.  Waits are per wave
-//                  (vmcnt), no barriers.
+//                  halves as soon as a half has been read.  Waits are vmcnt
+//                  counts, no barriers.
 //   S^T (64 keys x 64 queries) = K . Q^T     64 x mfma_f32_16x16x32_bf16
 //   online softmax in fp32 with exp2, software-pipelined: the softmax of tile j
-//   runs on the VALU between the QK MFMAs of tile j+1.  The running max moves
-//   only when a row's max grows by more than 2^16, so the O rescale is skipped
-//   on almost every tile.
+//   runs on the VALU between the QK MFMAs of tile j+1.  The running max is
+//   moved only when a tile's probabilities against it grow past 2^16, so the O
+//   rescale is skipped on almost every tile.
 //   O (64 x 128) += P . V                     64 x mfma_f32_16x16x32_bf16,
 //                  V operands read with ds_read_b64_tr_b16
 // S^T puts keys on MFMA rows: each lane holds one query per 16-query block,
 // and the key order inside every 32-key step is permuted (kperm) so a lane's
 // eight probabilities are eight consecutive keys -- exactly the P operand of
-// the PV product, with no register shuffles.  At the end the four waves'
-// (max, sum, O) partials are merged through LDS and each wave writes 16 query
-// rows (gate combine, bf16 round-to-nearest-even, packed order).
+// the PV product, with no register shuffles.  At the end O^T goes through LDS
+// and the wave writes the 64 query rows (gate combine, bf16 round-to-nearest-
+// even, packed order).
 //
-// Per-tile scalar work is kept small: every LDS read address is a per-lane
-// base fixed for the whole kernel plus an immediate offset, and the source
+// Per-tile scalar work is kept small: every K read address is a per-lane base
+// fixed for the whole kernel plus an immediate offset (a V read address adds
+// one XOR and shift to a fixed base), and the source
 // location of the wave's tiles is computed 64 tiles at a time (one per lane)
 // and read back with readlane.
 //
 // Rows are ordered head-major, dense rows first, and mapped XCD-aware: the
 // hardware deals workgroup i to XCD i % 8, so XCD x receives a contiguous
-// range of heads and its L2 sees one head's K/V at a time.
+// range of heads and its L2 sees few heads' K/V at a time.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-// Lazy rescale threshold (log2 units): P = exp2(S sl2 - m) is taken against a running max
-// that may lag the true one by up to 2^16.  P, O and l stay far inside the fp32 / bf16
-// exponent range, and with logits of std 3 a rescale is then practically never needed
-// (at 2^8 about one tile in twelve paid for one).
-constexpr float RESCALE_TH = 16.0f;
+// Lazy rescale: P = exp2(S sl2 - m) is taken against a running max m that may lag the
+// true one.  m is moved (O and l rescaled) only when, for some row, one lane's sum of the
+// tile's probabilities passes 2^16: that sum bounds each of them, so P, O and l stay far
+// inside the fp32 / bf16 range, and an overflow to inf is caught by the same test.  With
+// logits of std 3 a rescale is then practically never needed.
+constexpr float RESCALE_SUM = 65536.0f;
 constexpr int TILE_BYTES = 16384;    // one 64 x 128 bf16 tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -316,10 +318,9 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   //   R1 first half:  V(j) rows 32-63      R1 second half: K(j+2) rows 0-31
   //   R2 first half:  K(j+2) rows 32-63    R2 second half: V(j+1) rows 0-31
   // Every half lands at least half a phase after it was issued; each wait leaves the 15 or
-  // 16 loads issued after the awaited half in flight.  P(j) is taken against
-  // the running max as it stands; the tile's own max comes out of the same pass and, in
-  // the rare case it passes the running max by more than RESCALE_TH, the max is moved
-  // (O and l rescaled) and P(j) is taken again.
+  // 16 loads issued after the awaited half in flight.  P(j) is taken against the running
+  // max as it stands; in the rare case its row sums pass RESCALE_SUM the max is moved to
+  // the tile's (O and l rescaled) and P(j) is taken again.
   unsigned c_off = NO_TILE, c_flags = 0, n_off = NO_TILE, n_flags = 0;
   f32x4 scur[4][4];
   if (my_n > 0) {
@@ -402,24 +403,19 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     steps(nn_flags, nn_stp, nn_stl);
 
     // softmax of S(j), chunk s = (key block s >> 2, query block s & 3): P against the
-    // running max, the tile max and the tile's row sums on the way; P packed to bf16
-    // PV operands once both key blocks of a 32-key step are done
+    // running max and the lane's share of the tile's row sums; P packed to bf16 PV
+    // operands once both key blocks of a 32-key step are done
     bf16x8 pb[4][2];
-    float tmax[4], lt[4];
+    float lt[4];
     unsigned pe[4][2];  // bf16 pairs of the even key block, until its odd partner is done
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      tmax[qb] = -INFINITY;
-      lt[qb] = 0.f;
-    }
+    for (int qb = 0; qb < 4; ++qb) lt[qb] = 0.f;
     auto soft = [&](int s) {
       const int kb = s >> 2, qb = s & 3;
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = scur[kb][qb][i];
-        tmax[qb] = fmaxf(tmax[qb], x);
-        p[i] = __builtin_amdgcn_exp2f(fmaf(x, sl2, -mrun[qb]));
+        p[i] = __builtin_amdgcn_exp2f(fmaf(scur[kb][qb][i], sl2, -mrun[qb]));
         lt[qb] += p[i];
       }
       if (kb & 1) {
@@ -473,16 +469,21 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
       asm volatile("" : "+v"(pb[qb][0]), "+v"(pb[qb][1]), "+v"(lt[qb]));
     }
 
-    // ---- the max check (wave-uniform; rarely taken).  A row's tile max passes the
-    // threshold iff one of its four lanes' maxima does, so the lanes compare their own.
+    // ---- the rescale check (wave-uniform; rarely taken): a lane's share of a row sum
+    // passing RESCALE_SUM (or not finite) moves the running max to the tile's max
     bool grow = false;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) grow |= tmax[qb] * sl2 > mrun[qb] + RESCALE_TH;
+    for (int qb = 0; qb < 4; ++qb) grow |= !(lt[qb] <= RESCALE_SUM);
     if (__ballot(grow)) {
       float alpha[4];
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        const float mn = fmaxf(mrun[qb], group_max(tmax[qb]) * sl2);
+        float m = scur[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, scur[kb][qb][i]);
+        const float mn = fmaxf(mrun[qb], group_max(m) * sl2);
         alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - mn);
         mrun[qb] = mn;
         lsum[qb] *= alpha[qb];
