@@ -9,92 +9,188 @@
 // S_ij = s qbar_i . kbar_j + b_j for every sparse query tile i and every
 // video key tile j; P = softmax_j(S); O_c,i = sum_j P_ij vbar_j.  All fp32
 // (the ranking must hold the oracle's order wherever its logit gap > 1e-4;
-// bf16 inputs to this dot product would not).  Small next to the fine
-// branch: ~4.6 GFLOP fp32 at 32 heads x 564 tiles.
+// bf16 inputs to this dot product would not), on the fp32 MFMAs: two dense
+// contractions per head, ~4.6 GFLOP at 32 heads x 564 tiles, fused in one
+// kernel so the logits are written once and never read back here.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
 namespace {
 
-constexpr int ROWS = VSA_COARSE_ROWS;  // 32 sparse rows per workgroup
-constexpr int CHUNK = 64;              // video tiles per LDS chunk
-constexpr int LDSW = VSA_HEAD_DIM + 4; // padded row (floats)
+constexpr int CROWS = VSA_COARSE_ROWS;  // 64 sparse rows per workgroup, 16 per wave
+constexpr int CCH = 64;                 // video tiles per LDS chunk
+constexpr int LW = VSA_HEAD_DIM + 4;    // padded LDS row (floats)
+constexpr float LOG2E_F = 1.4426950408889634f;
 
-__global__ __launch_bounds__(256) void vsa_scores_kernel(VsaGeom g, const float* __restrict__ qbar,
+// One workgroup per (64 sparse rows, head, batch); wave w owns rows 16 w .. 16 w + 15.
+// Per chunk of 64 video tiles (K-bar, V-bar and the bias staged in LDS, the next chunk's
+// loads in flight meanwhile):
+//   S^T = K-bar Q-bar^T on fp32 MFMAs (v_mfma_f32_16x16x4_f32).  MFMA step t of a
+//     16-tile block contracts dims k(t, g) = 16 (t >> 2) + 4 g + (t & 3) for lane group g,
+//     so both operands are 16-byte reads (Q-bar stays in registers).  Lane (g, r) ends
+//     with S[row r][tiles 16 cb + 4 g .. +3] of block cb.
+//   S = scale S + b goes out to the scores (and the tau sums), then an online softmax in
+//     fp32 (exp2 of log2-scaled logits, the running max and sum per row).
+//   O^T += V-bar^T P^T on fp32 MFMAs: P^T is exactly the S^T layout, and the output dims
+//     are ordered d(db, r) = 64 (db >> 2) + 4 r + (db & 3) so V-bar is read 16 bytes at a
+//     time.  A lane's O values all belong to its own row, so the rescale and the final
+//     1 / l stay in the lane.
+__global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float* __restrict__ qbar,
                                                          const float* __restrict__ kbar,
+                                                         const float* __restrict__ vbar,
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ scores,
+                                                         float* __restrict__ ocoarse,
                                                          double* __restrict__ statp) {
-  __shared__ float qs[ROWS][LDSW];
-  __shared__ float ks[CHUNK][LDSW];
+  __shared__ __attribute__((aligned(16))) float ks[CCH][LW];
+  __shared__ __attribute__((aligned(16))) float vs[CCH][LW];
+  __shared__ float bs[CCH];
   __shared__ double red[4][2];
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const size_t bh = (size_t)blockIdx.z * g.heads + blockIdx.y;
-  const int s0 = blk * ROWS;
-  for (int i = tid; i < ROWS * 32; i += 256) {
-    const int r = i >> 5, c4 = i & 31;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (s0 + r < g.Qs)
-      x = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + s0 + r) * VSA_HEAD_DIM)[c4];
-    *reinterpret_cast<f32x4*>(&qs[r][4 * c4]) = x;
+  const int row = blockIdx.x * CROWS + 16 * wave + lr;  // the sparse row of this lane's values
+  const bool live = row < g.Qs;
+
+  // Q-bar operand: qf[m] = Q-bar[row][16 m + 4 lg .. +3] (zeros past the last row)
+  f32x4 qf[8];
+  {
+    const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? row : 0)) * VSA_HEAD_DIM);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) qf[m] = live ? qp[4 * m + lg] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int ty = tid >> 4, tx = tid & 15;
-  const float* bias_bh = bias + bh * g.Vt;
+  const float* kb = kbar + bh * g.Vt * VSA_HEAD_DIM;
+  const float* vb = vbar + bh * g.Vt * VSA_HEAD_DIM;
+  const float* bb = bias + bh * g.Vt;
+
+  // chunk staging: thread tid moves rows (tid >> 5) + 8 r, 16-byte column tid & 31
+  f32x4 kr[8], vr[8];
+  float br = 0.f;
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int j = j0 + (tid >> 5) + 8 * r;
+      kr[r] = vr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j < g.Vt) {
+        kr[r] = reinterpret_cast<const f32x4*>(kb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
+        vr[r] = reinterpret_cast<const f32x4*>(vb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
+      }
+    }
+    br = (tid < CCH && j0 + tid < g.Vt) ? bb[j0 + tid] : 0.f;
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      *reinterpret_cast<f32x4*>(&ks[(tid >> 5) + 8 * r][4 * (tid & 31)]) = kr[r];
+      *reinterpret_cast<f32x4*>(&vs[(tid >> 5) + 8 * r][4 * (tid & 31)]) = vr[r];
+    }
+    if (tid < CCH) bs[tid] = br;
+  };
+
+  float mrow = -INFINITY, lrow = 0.f;  // running max (log2 units) and this lane's share of the sum
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   double ssum = 0.0, ssq = 0.0;
-  for (int j0 = 0; j0 < g.Vt; j0 += CHUNK) {
+  const bool vec_out = (g.Vt & 3) == 0;  // 16-byte score stores stay aligned
+
+  fetch(0);
+  for (int j0 = 0; j0 < g.Vt; j0 += CCH) {
+    __syncthreads();  // the previous chunk's LDS reads are done
+    stash();
     __syncthreads();
-    for (int i = tid; i < CHUNK * 32; i += 256) {
-      const int r = i >> 5, c4 = i & 31;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + r < g.Vt)
-        x = reinterpret_cast<const f32x4*>(kbar + (bh * g.Vt + j0 + r) * VSA_HEAD_DIM)[c4];
-      *reinterpret_cast<f32x4*>(&ks[r][4 * c4]) = x;
+    if (j0 + CCH < g.Vt) fetch(j0 + CCH);
+
+    f32x4 st[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[16 * cb + lr][16 * m + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qf[m][e], acc, 0, 0, 0);
+      }
+      st[cb] = acc;
     }
-    __syncthreads();
-    float acc[2][4];
+
+    // logits out (and the tau sums), then the chunk's softmax step
+    float cm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int cb = 0; cb < 4; ++cb) {
+      const int jl = 16 * cb + 4 * lg;
+      f32x4 sv;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[r][m] = 0.f;
-#pragma unroll 4
-    for (int d = 0; d < VSA_HEAD_DIM; d += 4) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs[2 * ty][d]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs[2 * ty + 1][d]);
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = st[cb][i] * g.scale + bs[jl + i];
+        const bool valid = j0 + jl + i < g.Vt;
+        if (live && valid) {
+          ssum += (double)sv[i];
+          ssq += (double)sv[i] * (double)sv[i];
+        }
+        st[cb][i] = valid ? sv[i] * LOG2E_F : -INFINITY;
+        cm = fmaxf(cm, st[cb][i]);
+      }
+      if (live) {
+        float* dst = scores + (bh * g.Qs + row) * g.Vt + j0 + jl;
+        if (vec_out && j0 + jl + 3 < g.Vt) {
+          *reinterpret_cast<f32x4*>(dst) = sv;
+        } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&ks[tx + 16 * m][d]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[0][m] = fmaf(a0[e], bv[e], acc[0][m]);
-          acc[1][m] = fmaf(a1[e], bv[e], acc[1][m]);
+          for (int i = 0; i < 4; ++i)
+            if (j0 + jl + i < g.Vt) dst[i] = sv[i];
         }
       }
     }
+    const float mn = fmaxf(mrow, group_max(cm));
+    const float alpha = __builtin_amdgcn_exp2f(mrow - mn);  // 0 on the first chunk
+    mrow = mn;
+    lrow *= alpha;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int s = s0 + 2 * ty + r;
+    for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = j0 + tx + 16 * m;
-        if (s < g.Qs && j < g.Vt) {
-          const float S = acc[r][m] * g.scale + bias_bh[j];
-          scores[(bh * g.Qs + s) * g.Vt + j] = S;
-          ssum += (double)S;
-          ssq += (double)S * (double)S;
-        }
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st[cb][i] = __builtin_amdgcn_exp2f(st[cb][i] - mn);
+        lrow += st[cb][i];
       }
-    }
+
+    // O^T += V-bar^T P^T: step (cb, t) covers tiles 16 cb + 4 lg + t
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x4 vv = *reinterpret_cast<const f32x4*>(&vs[16 * cb + 4 * lg + t][64 * hh + 4 * lr]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            oacc[4 * hh + q] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[q], st[cb][t], oacc[4 * hh + q], 0, 0, 0);
+        }
   }
+
+  // O_c = O / l: oacc[4 hh + q][i] = O[row][64 hh + 16 lg + 4 i + q]
+  const float lt = group_sum(lrow);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (live) {
+    float* orow = ocoarse + (bh * g.Qs + row) * VSA_HEAD_DIM;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(orow + 64 * hh + 16 * lg + 4 * i) =
+            f32x4{oacc[4 * hh][i], oacc[4 * hh + 1][i], oacc[4 * hh + 2][i], oacc[4 * hh + 3][i]} * inv;
+  }
+
   if (g.select != VSA_SELECT_TAU) return;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     ssum += __shfl_xor(ssum, m);
     ssq += __shfl_xor(ssq, m);
   }
-  if ((tid & 63) == 0) {
-    red[tid >> 6][0] = ssum;
-    red[tid >> 6][1] = ssq;
+  if (lane == 0) {
+    red[wave][0] = ssum;
+    red[wave][1] = ssq;
   }
   __syncthreads();
   if (tid == 0) {
@@ -103,77 +199,8 @@ __global__ __launch_bounds__(256) void vsa_scores_kernel(VsaGeom g, const float*
       a += red[w][0];
       q += red[w][1];
     }
-    statp[(bh * g.coarse_blocks + blk) * 2 + 0] = a;
-    statp[(bh * g.coarse_blocks + blk) * 2 + 1] = q;
-  }
-}
-
-constexpr int OROWS = 16;  // sparse rows per workgroup of the output kernel
-constexpr int OCH = 32;    // video tiles per chunk
-
-__global__ __launch_bounds__(256) void vsa_coarse_out_kernel(VsaGeom g, const float* __restrict__ scores,
-                                                             const float* __restrict__ vbar,
-                                                             float* __restrict__ ocoarse) {
-  __shared__ float rowm[OROWS], rowinv[OROWS];
-  __shared__ float vs[OCH][VSA_HEAD_DIM];
-  __shared__ float ps[OROWS][OCH + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const size_t bh = (size_t)blockIdx.z * g.heads + blockIdx.y;
-  const int s0 = blockIdx.x * OROWS;
-  for (int rr = 0; rr < OROWS / 4; ++rr) {
-    const int r = wave * (OROWS / 4) + rr;
-    const int s = s0 + r;
-    float mx = -INFINITY, se = 0.f;
-    if (s < g.Qs) {
-      const float* S = scores + (bh * g.Qs + s) * g.Vt;
-      for (int j = lane; j < g.Vt; j += 64) mx = fmaxf(mx, S[j]);
-      mx = wave_max(mx);
-      for (int j = lane; j < g.Vt; j += 64) se += expf(S[j] - mx);
-      se = wave_sum(se);
-    }
-    if (lane == 0) {
-      rowm[r] = mx;
-      rowinv[r] = s < g.Qs ? 1.0f / se : 0.f;
-    }
-  }
-  const int r = tid >> 4, c0 = (tid & 15) * 8;
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < g.Vt; j0 += OCH) {
-    __syncthreads();
-    for (int i = tid; i < OCH * 32; i += 256) {
-      const int jr = i >> 5, c4 = i & 31;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + jr < g.Vt)
-        x = reinterpret_cast<const f32x4*>(vbar + (bh * g.Vt + j0 + jr) * VSA_HEAD_DIM)[c4];
-      *reinterpret_cast<f32x4*>(&vs[jr][4 * c4]) = x;
-    }
-    for (int i = tid; i < OROWS * OCH; i += 256) {
-      const int pr = i / OCH, pj = i % OCH;
-      const int s = s0 + pr, j = j0 + pj;
-      float p = 0.f;
-      if (s < g.Qs && j < g.Vt) p = expf(scores[(bh * g.Qs + s) * g.Vt + j] - rowm[pr]) * rowinv[pr];
-      ps[pr][pj] = p;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int jj = 0; jj < OCH; ++jj) {
-      const float p = ps[r][jj];
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&vs[jj][c0]);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&vs[jj][c0 + 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = fmaf(p, v0[e], acc[e]);
-        acc[4 + e] = fmaf(p, v1[e], acc[4 + e]);
-      }
-    }
-  }
-  const int s = s0 + r;
-  if (s < g.Qs) {
-    f32x4* dst = reinterpret_cast<f32x4*>(ocoarse + (bh * g.Qs + s) * VSA_HEAD_DIM + c0);
-    dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    dst[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    statp[(bh * g.coarse_blocks + blockIdx.x) * 2 + 0] = a;
+    statp[(bh * g.coarse_blocks + blockIdx.x) * 2 + 1] = q;
   }
 }
 
@@ -195,18 +222,12 @@ __global__ void vsa_tau_kernel(VsaGeom g, const double* __restrict__ statp, floa
 
 }  // namespace
 
-void vsa_launch_scores(const VsaGeom& g, const float* qbar, const float* kbar, const float* bias,
-                       float* scores, double* statp, hipStream_t st) {
+void vsa_launch_coarse(const VsaGeom& g, const float* qbar, const float* kbar, const float* vbar,
+                       const float* bias, float* scores, float* ocoarse, double* statp, hipStream_t st) {
   if (g.Qs == 0) return;
   dim3 grid(g.coarse_blocks, g.heads, g.batch);
-  hipLaunchKernelGGL(vsa_scores_kernel, grid, dim3(256), 0, st, g, qbar, kbar, bias, scores, statp);
-}
-
-void vsa_launch_coarse_out(const VsaGeom& g, const float* scores, const float* vbar, float* ocoarse,
-                           hipStream_t st) {
-  if (g.Qs == 0) return;
-  dim3 grid((g.Qs + OROWS - 1) / OROWS, g.heads, g.batch);
-  hipLaunchKernelGGL(vsa_coarse_out_kernel, grid, dim3(256), 0, st, g, scores, vbar, ocoarse);
+  hipLaunchKernelGGL(vsa_coarse_kernel, grid, dim3(256), 0, st, g, qbar, kbar, vbar, bias, scores, ocoarse,
+                     statp);
 }
 
 void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream_t st) {

@@ -144,8 +144,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
     VSA_STEP("logmass", vsa_launch_logmass(G, k, kbar, anchor, bias, st));
   }
-  VSA_STEP("scores", vsa_launch_scores(G, qbar, kbar, bias, scores, statp, st));
-  VSA_STEP("coarse_out", vsa_launch_coarse_out(G, scores, vbar, ocoarse, st));
+  VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, st));
   if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
   VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
   VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, st));

@@ -11,7 +11,7 @@
 #define VSA_MAX_LIST 2048        // key tiles in one sparse row's list (staged in LDS by the fine kernel)
 #define VSA_HEAD_DIM 128
 #define VSA_TILE_TOKENS 64
-#define VSA_COARSE_ROWS 32   // sparse rows per workgroup of the coarse-score kernel
+#define VSA_COARSE_ROWS 64   // sparse rows per workgroup of the coarse kernel
 
 // Geometry and options of one plan, passed to every kernel by value.  Tile ids:
 // prefix tiles [0, P) in packed order, video tiles [P, P + Vt) raster (tt, th, tw).

@@ -17,14 +17,11 @@ void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipSt
 void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
                         float* bias, hipStream_t st);
 
-// Coarse logits S = s qbar kbar^T + bias of the sparse rows, and per-workgroup
-// (sum, sum of squares) partials for the tau statistics.
-void vsa_launch_scores(const VsaGeom& g, const float* qbar, const float* kbar, const float* bias,
-                       float* scores, double* statp, hipStream_t st);
-
-// Row softmax of S and O_coarse = P vbar.
-void vsa_launch_coarse_out(const VsaGeom& g, const float* scores, const float* vbar, float* ocoarse,
-                           hipStream_t st);
+// Coarse branch: S = scale qbar kbar^T + b for the sparse rows against the video tiles
+// (written to scores, with the per-block tau sums), the row softmax, and
+// O_coarse = softmax(S) vbar, in one fused fp32-MFMA kernel.
+void vsa_launch_coarse(const VsaGeom& g, const float* qbar, const float* kbar, const float* vbar,
+                       const float* bias, float* scores, float* ocoarse, double* statp, hipStream_t st);
 
 // tau threshold mean + tau * std per (batch, head) from the partials.
 void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream_t st);
