@@ -101,12 +101,27 @@ void launch_npl(const VsaGeom& g, const float* scores, const float* thr, int* li
 void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, int* lists,
                        int* counts, hipStream_t st) {
   if (g.Qs == 0) return;
+  // slots per lane; exact up to 16, so no all-padding slot joins the 32 ballot rounds
   const int npl = (g.Vt + 63) / 64;
-  if (npl <= 1) launch_npl<1>(g, scores, thr, lists, counts, st);
-  else if (npl <= 2) launch_npl<2>(g, scores, thr, lists, counts, st);
-  else if (npl <= 4) launch_npl<4>(g, scores, thr, lists, counts, st);
-  else if (npl <= 8) launch_npl<8>(g, scores, thr, lists, counts, st);
-  else if (npl <= 16) launch_npl<16>(g, scores, thr, lists, counts, st);
-  else if (npl <= 32) launch_npl<32>(g, scores, thr, lists, counts, st);
-  else launch_npl<64>(g, scores, thr, lists, counts, st);
+  switch (npl) {
+    case 1: launch_npl<1>(g, scores, thr, lists, counts, st); break;
+    case 2: launch_npl<2>(g, scores, thr, lists, counts, st); break;
+    case 3: launch_npl<3>(g, scores, thr, lists, counts, st); break;
+    case 4: launch_npl<4>(g, scores, thr, lists, counts, st); break;
+    case 5: launch_npl<5>(g, scores, thr, lists, counts, st); break;
+    case 6: launch_npl<6>(g, scores, thr, lists, counts, st); break;
+    case 7: launch_npl<7>(g, scores, thr, lists, counts, st); break;
+    case 8: launch_npl<8>(g, scores, thr, lists, counts, st); break;
+    case 9: launch_npl<9>(g, scores, thr, lists, counts, st); break;
+    case 10: launch_npl<10>(g, scores, thr, lists, counts, st); break;
+    case 11: launch_npl<11>(g, scores, thr, lists, counts, st); break;
+    case 12: launch_npl<12>(g, scores, thr, lists, counts, st); break;
+    case 13: launch_npl<13>(g, scores, thr, lists, counts, st); break;
+    case 14: launch_npl<14>(g, scores, thr, lists, counts, st); break;
+    case 15: launch_npl<15>(g, scores, thr, lists, counts, st); break;
+    case 16: launch_npl<16>(g, scores, thr, lists, counts, st); break;
+    default:
+      if (npl <= 32) launch_npl<32>(g, scores, thr, lists, counts, st);
+      else launch_npl<64>(g, scores, thr, lists, counts, st);
+  }
 }
