@@ -73,6 +73,12 @@ SMALL_CASES = [
              SINK_EXACT_KV, SELECT_TAU, COARSE_MEAN_LOGMASS, 1.5, seed=79, recipe="offset"),
     Workload("smooth_gate_rows", 4, ((SEG_TEXT, 128), (SEG_REF_IMAGE, 256)), (8, 16, 24), 10.0,
              SINK_EXACT_KV_AND_ROWS, seed=80, recipe="smooth"),
+    # an odd number of video tiles (3 x 5 x 7 = 105) spanning two 64-tile chunks of the
+    # coarse kernel, and a sparse row count that is not a multiple of its 64-row blocks
+    Workload("odd_video_grid", 2, ((SEG_TEXT, 70),), (12, 20, 28), 20.0, SINK_EXACT_KV_AND_ROWS,
+             seed=82, recipe="scaled"),
+    Workload("odd_video_grid_tau", 2, ((SEG_TEXT, 70),), (12, 20, 28), 0.0, SINK_EXACT_KV,
+             SELECT_TAU, COARSE_MEAN_LOGMASS, 1.0, seed=83, recipe="offset"),
 ]
 
 
