@@ -3,12 +3,14 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload full]
                     [--no-cpu-baseline] [--cpu-seconds 15]
 
-One step = one whole vsa_forward (pool, [log-mass], coarse scores, coarse
-softmax + O_coarse, [tau], selection, fine attention + gated combine) on the
-full clip shape: 32 heads, head_dim 128, prefix 512 text + 1536 reference-image
-+ 256 reference-audio tokens, video grid 32x24x44 (33,792 tokens), keep 10%,
+One step = one whole vsa_forward (pool, [log-mass], coarse logits + softmax +
+O_coarse, [tau], selection, fine attention + gated combine) on the full clip
+shape: 32 heads, head_dim 128, prefix 512 text + 1536 reference-image + 256
+reference-audio tokens, video grid 32x24x44 (33,792 tokens), keep 10%,
 exact_kv_and_rows.  Inputs are seeded synthetic bf16 tensors, resident in HBM
-before timing starts.  Prints one JSON line.
+before timing starts.  Prints one JSON line: the headline times plain forwards;
+per-kernel times come from a second pass with HIP events between the kernels, and
+ms_per_step_graph from replays of the same forward captured into a HIP graph.
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fine_full_traffic.json"),
                     help="measured HBM bytes per fine launch (from rocprofv3 counters)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (ms_per_step_graph)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy this many MiB device-to-device (a kernel of known "
                          "traffic that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -146,19 +150,34 @@ def main():
         V.vsa_forward(plan, q, k, v, g, o, ws)
     torch.cuda.synchronize()
     stats = V.vsa_read_stats(plan, ws)
+    def timed_steps(step):
+        """Time exactly a.steps calls of step() with events on the launch stream."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(a.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
+        med = per_call[len(per_call) // 2] if len(per_call) % 2 else 0.5 * (
+            per_call[len(per_call) // 2 - 1] + per_call[len(per_call) // 2])
+        return evs[0].elapsed_time(evs[-1]) / a.steps, med
+
+    # the headline: plain forwards on the caller's stream
+    ms, median_ms = timed_steps(lambda: V.vsa_forward(plan, q, k, v, g, o, ws))
+    # per-kernel HIP-event times (the fine kernel's feeds the roofline line)
     timer.reset()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(a.steps):
-        V.vsa_forward_timed(plan, q, k, v, g, o, ws, timer)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    total_ms = evs[0].elapsed_time(evs[-1])
-    ms = total_ms / a.steps
-    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
-    median_ms = per_call[len(per_call) // 2] if len(per_call) % 2 else 0.5 * (
-        per_call[len(per_call) // 2 - 1] + per_call[len(per_call) // 2])
+    timed_steps(lambda: V.vsa_forward_timed(plan, q, k, v, g, o, ws, timer))
+    # the same forward captured once into a HIP graph and replayed
+    graph_ms = None
+    if not a.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            V.vsa_forward(plan, q, k, v, g, o, ws)
+        for _ in range(a.warmup):
+            graph.replay()
+        graph_ms, _ = timed_steps(graph.replay)
     kt = timer.read()
     flop = stats["executed_pairs"] * PAIR_FLOP
     tflops = flop / (ms * 1e-3) / 1e12
@@ -194,6 +213,7 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_layer": round(ms, 4),
         "ms_per_layer_median": round(median_ms, 4),
+        "ms_per_step_graph": round(graph_ms, 4) if graph_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
