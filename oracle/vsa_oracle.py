@@ -30,7 +30,8 @@ Method, in the pages' order:
      VSA item; [SPK-es] "Que cambia Spark-Attn").
   3. optional log-mass bias on the pooled logits, anchored at the mean video
      query ([SPK-es] "Que cambia Spark-Attn", Spark-Reweight item, and the
-     figure caption on exp(E[x]) vs E[exp(x)]).
+     figure caption on exp(E[x]) vs E[exp(x)]); optionally with weighted key /
+     value summaries in place of the means (same Spark-Reweight item).
   4. selection: top-k video key tiles per query tile at a keep fraction
      ([FH3] "The mechanism"; [BSA-es] top-k item), or a per-head threshold
      mean + tau * std ([BSA-es] Sol-Attn item); prefix tiles never pruned
@@ -67,7 +68,11 @@ the design notes):
     over every (sparse query tile, video key tile) logit; keep S > thr; a
     row whose list ends up empty has a zero fine output;
   * log-mass bias b_j = log(mean_t exp(l_t - p_j)) with l_t = s q_a . k_t,
-    p_j = s q_a . kbar_j and q_a the mean of all video queries.
+    p_j = s q_a . kbar_j and q_a the mean of all video queries;
+  * weighted summaries (the page does not give the weights): the anchor's own
+    attention over the tile, w_t = softmax_t(l_t); ktil_j = sum_t w_t k_t,
+    vtil_j = sum_t w_t v_t; the bias keeps the same anchor identity,
+    b_j = log(mean_t exp(l_t)) - s q_a . ktil_j.
 """
 from __future__ import annotations
 
@@ -83,7 +88,7 @@ HEAD_DIM = 128
 SEG_TEXT, SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_OTHER_PREFIX, SEG_VIDEO = 0, 1, 2, 3, 4
 SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 1, 2
 SELECT_TOPK, SELECT_TAU = 0, 1
-COARSE_MEAN, COARSE_MEAN_LOGMASS = 0, 1
+COARSE_MEAN, COARSE_MEAN_LOGMASS, COARSE_WEIGHTED_LOGMASS = 0, 1, 2
 
 
 def softmax_scale(head_dim: int = HEAD_DIM) -> float:
@@ -219,6 +224,35 @@ def logmass_bias(Q: np.ndarray, K: np.ndarray, geom: Geometry, scale: float):
     return b, q_a
 
 
+def weighted_summaries(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry, scale: float):
+    """Weighted key / value summaries of the video tiles plus the log-mass bias.
+
+    [SPK-es] "Que cambia Spark-Attn", Spark-Reweight: weighted summaries replace
+    the mean-pooled key / value summary, with the log-mass bias on top and the
+    mean video query as the per-head anchor.  The weights are the anchor's
+    attention over the tile's keys (the page does not give them):
+      q_a = mean of Q over all valid video tokens
+      l_t = s q_a . k_t,  w_t = exp(l_t) / sum_{t' in j} exp(l_t')
+      ktil_j = sum_t w_t k_t,  vtil_j = sum_t w_t v_t
+      b_j = log( mean_{t in j} exp(l_t) ) - s q_a . ktil_j
+    so that exp(s q_a . ktil_j + b_j) is mean_t exp(l_t), as for the plain bias.
+    Returns (ktil [Vt, D], vtil [Vt, D], b [Vt], q_a [D]).
+    """
+    vt = geom.tiles[geom.n_prefix:]
+    q_a = Q[np.concatenate(vt)].mean(axis=0)
+    D = K.shape[1]
+    ktil, vtil, b = np.empty((len(vt), D)), np.empty((len(vt), D)), np.empty(len(vt))
+    for j, toks in enumerate(vt):
+        ell = scale * (K[toks] @ q_a)
+        m = ell.max()
+        e = np.exp(ell - m)
+        w = e / e.sum()
+        ktil[j] = w @ K[toks]
+        vtil[j] = w @ V[toks]
+        b[j] = m + math.log(np.mean(e)) - scale * (q_a @ ktil[j])
+    return ktil, vtil, b, q_a
+
+
 def coarse_branch(Qbar: np.ndarray, Kbar: np.ndarray, Vbar: np.ndarray,
                   bias: np.ndarray, scale: float):
     """Coarse scores, softmax and output for a set of query tiles.
@@ -308,6 +342,8 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
     Vbar = pool_tiles(V, vt)
     if coarse == COARSE_MEAN_LOGMASS:
         bias, q_a = logmass_bias(Q, K, geom, scale)
+    elif coarse == COARSE_WEIGHTED_LOGMASS:
+        Kbar, Vbar, bias, q_a = weighted_summaries(Q, K, V, geom, scale)
     elif coarse == COARSE_MEAN:
         bias, q_a = np.zeros(len(vt)), None
     else:

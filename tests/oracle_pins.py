@@ -27,7 +27,7 @@ from oracle import vsa_oracle as O
 from workloads.synth import (Workload, make_inputs, f32_to_bf16_bits, SEG_TEXT,
                              SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_VIDEO, SINK_EXACT_KV,
                              SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, SELECT_TAU,
-                             COARSE_MEAN, COARSE_MEAN_LOGMASS)
+                             COARSE_MEAN, COARSE_MEAN_LOGMASS, COARSE_WEIGHTED_LOGMASS)
 
 GOLDEN = json.loads((Path(__file__).parent / "golden" / "page_numbers.json").read_text())
 D = 128
@@ -364,6 +364,55 @@ def check_logmass():
         assert abs(lhs - rhs) <= 1e-12 * rhs
 
 
+def check_weighted_summaries():
+    """Weighted key / value summaries ([SPK-es] Spark-Reweight; weights read as the
+    anchor's attention over the tile) against an independent routine and reductions:
+      * vtil_j and ktil_j are torch's float64 scaled_dot_product_attention of the
+        anchor (the mean of the video queries, taken over the 4x4x4 cubes of an
+        independent reshape) over tile j's keys and values / keys;
+      * exp(s q_a . ktil_j + b_j) is the mean token exponential, summed directly;
+      * a tile whose keys are all equal gives ktil = that key, vtil = the mean value
+        and b = 0;
+      * a zero anchor (video queries in +q / -q pairs) weighs every token equally,
+        so the whole forward equals the plain-mean mode's."""
+    w = Workload("ws", 1, ((SEG_TEXT, 64),), (4, 8, 8), 25.0, SINK_EXACT_KV, seed=43, recipe="offset")
+    x = make_inputs(w)
+    geom = geom_of(w)
+    cubes = video_cube_tokens(w)
+    # tile 0: every key equal to its first one
+    kb = x["k"].copy()
+    kb[0, cubes[0], 0] = kb[0, cubes[0][0], 0]
+    Qh, Kh, Vh = as_f64(x["q"][0, :, 0]), as_f64(kb[0, :, 0]), as_f64(x["v"][0, :, 0])
+    s = 1.0 / math.sqrt(D)
+    ktil, vtil, b, q_a = O.weighted_summaries(Qh, Kh, Vh, geom, s)
+    q_ref = Qh[np.concatenate(cubes)].mean(axis=0)
+    assert np.abs(q_a - q_ref).max() < 1e-14
+    for j, toks in enumerate(cubes):
+        v_ref = torch_sdpa(q_ref[None, :], Kh[toks], Vh[toks])[0]
+        k_ref = torch_sdpa(q_ref[None, :], Kh[toks], Kh[toks])[0]
+        assert np.abs(vtil[j] - v_ref).max() < 1e-12 * (1 + np.abs(v_ref).max()), j
+        assert np.abs(ktil[j] - k_ref).max() < 1e-12 * (1 + np.abs(k_ref).max()), j
+        lhs = math.exp(s * float(q_ref @ k_ref) + b[j])
+        rhs = math.fsum(math.exp(s * float(q_ref @ Kh[t])) for t in toks) / len(toks)
+        assert abs(lhs - rhs) <= 1e-12 * rhs, (j, lhs, rhs)
+    assert np.abs(ktil[0] - Kh[cubes[0][0]]).max() < 1e-14
+    assert np.abs(vtil[0] - Vh[cubes[0]].mean(axis=0)).max() < 1e-14
+    assert abs(b[0]) < 1e-14
+    # zero anchor: pair every video query with its negation
+    xz = dict(x)
+    qz = x["q"].copy()
+    vid = np.concatenate(cubes)
+    qz[0, vid[1::2], 0] = qz[0, vid[0::2], 0] ^ np.uint16(0x8000)
+    xz["q"] = qz
+    ow, iw = O.forward(xz, w.segments(), w.grid, w.keep, w.sink, coarse=COARSE_WEIGHTED_LOGMASS,
+                       want_intermediates=True)
+    om, im = O.forward(xz, w.segments(), w.grid, w.keep, w.sink, coarse=COARSE_MEAN,
+                       want_intermediates=True)
+    assert np.abs(iw[(0, 0)]["anchor"]).max() == 0.0
+    assert np.abs(iw[(0, 0)]["S"] - im[(0, 0)]["S"]).max() < 1e-12
+    assert np.abs(ow - om).max() < 1e-12
+
+
 # ---------------------------------------------------------------- P-8 combine
 def check_combine(w: Workload):
     x = make_inputs(w, with_gate=True)
@@ -438,6 +487,7 @@ ALL_CHECKS = [
     ("tau_limits", lambda: check_tau_limits(SMALL)),
     ("tau_fractions", check_tau_fractions),
     ("logmass", check_logmass),
+    ("weighted_summaries", check_weighted_summaries),
     ("combine", lambda: check_combine(SMALL)),
     ("metamorphic", lambda: check_metamorphic(SMALL_VIDEO_FIRST)),
     ("prefix_permutation", check_prefix_permutation),

@@ -14,7 +14,7 @@ from oracle import vsa_oracle as O
 
 _orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
                                       "logmass_bias", "coarse_branch", "tau_threshold",
-                                      "keep_count", "pool_tiles", "fine_row")}
+                                      "keep_count", "pool_tiles", "fine_row", "weighted_summaries")}
 
 
 def _geom_swapped_axes(segments, T, H, W):
@@ -64,6 +64,28 @@ def _tau_variance(S, tau):
     return mu + tau * float(np.mean((vals - mu) ** 2))
 
 
+def _weighted_plain_means(Q, K, V, geom, scale):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
+    tiles = geom.tiles[geom.n_prefix:]
+    return (np.stack([K[t].mean(axis=0) for t in tiles]), np.stack([V[t].mean(axis=0) for t in tiles]),
+            b, qa)
+
+
+def _weighted_unnormalized(Q, K, V, geom, scale):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
+    tiles = geom.tiles[geom.n_prefix:]
+    ell = [scale * (K[t] @ qa) for t in tiles]
+    e = [np.exp(l - l.max()) for l in ell]
+    return np.stack([ei @ K[t] for ei, t in zip(e, tiles)]), np.stack([ei @ V[t] for ei, t in zip(e, tiles)]), b, qa
+
+
+def _weighted_bias_vs_mean(Q, K, V, geom, scale):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
+    tiles = geom.tiles[geom.n_prefix:]
+    b2 = np.array([b[j] + scale * (qa @ kt[j]) - scale * (qa @ K[t].mean(axis=0)) for j, t in enumerate(tiles)])
+    return kt, vt, b2, qa
+
+
 def _fine_k_for_v(Q, K, V, geom, qtile, key_tiles, scale):
     return _orig["fine_row"](Q, K, K, geom, qtile, key_tiles, scale)
 
@@ -83,6 +105,9 @@ MUTATIONS = [
     ("keep_floor", "keep_count", lambda p, n: max(1, min(n, math.floor(p * n / 100.0))), "keep_counts"),
     ("pool_sum", "pool_tiles", lambda X, tiles: np.stack([X[t].sum(axis=0) for t in tiles]), "pooling"),
     ("fine_k_as_v", "fine_row", _fine_k_for_v, "dense_equivalence"),
+    ("weighted_plain_means", "weighted_summaries", _weighted_plain_means, "weighted_summaries"),
+    ("weighted_unnormalized", "weighted_summaries", _weighted_unnormalized, "weighted_summaries"),
+    ("weighted_bias_vs_mean", "weighted_summaries", _weighted_bias_vs_mean, "weighted_summaries"),
 ]
 
 
