@@ -6,7 +6,8 @@
 // Dispersa...", VSA item: cubic tiling plus a coarse compression branch).
 // Log-mass bias: same Spark page, Spark-Reweight item: mean pooling stands
 // exp(E[x]) in for E[exp(x)]; a bias per tile, scored with the mean video
-// query as the anchor, restores the missing mass.
+// query as the anchor, restores the missing mass.  The same item's weighted
+// summaries replace the means by the anchor's attention over each tile.
 //
 // HBM-bound: each (tile, head) slice of Q, K, V is read once; one wave per
 // (tile, head), 16 lanes per token (16 x 16 B = one 256-byte head row), four
@@ -112,9 +113,17 @@ __global__ __launch_bounds__(1024) void vsa_anchor_kernel(VsaGeom g, const float
 }
 
 // b_j = log(mean_t exp(s q_a . (k_t - kbar_j))), max-shifted.  One wave per
-// (video tile, head).
+// (video tile, head).  WEIGHTED (Spark-Reweight's weighted summaries, read as the
+// anchor's attention over the tile): with the centred logits l'_t = s q_a . (k_t - kbar_j)
+// and w_t = softmax_t(l'_t), the kernel also writes
+//   ktil_j = kbar_j + sum_t w_t (k_t - kbar_j),  vtil_j = sum_t w_t v_t
+// over kbar_j and vbar_j, and the bias b_j = log(mean_t exp(l'_t)) - sum_t w_t l'_t, which is
+// log(mean_t exp(s q_a . k_t)) - s q_a . ktil_j.
+template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4* __restrict__ k,
-                                                          const float* __restrict__ kbar,
+                                                          const u32x4* __restrict__ v,
+                                                          float* __restrict__ kbar,
+                                                          float* __restrict__ vbar,
                                                           const float* __restrict__ anchor,
                                                           float* __restrict__ bias) {
   const int j = blockIdx.y;
@@ -135,9 +144,14 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
     kb[i] = k4[0][i];
     kb[4 + i] = k4[1][i];
   }
-  u32x4 buf[16];
+  // rows 4 p + grp of the tile, dims 8 c .. 8 c + 7
+  u32x4 buf[16], vbuf[16];
 #pragma unroll
-  for (int p = 0; p < 16; ++p) buf[p] = k[row_offset(g, b, tile_token(g, t, 4 * p + grp), h) / 8 + c];
+  for (int p = 0; p < 16; ++p) {
+    const long long ro = row_offset(g, b, tile_token(g, t, 4 * p + grp), h) / 8 + c;
+    buf[p] = k[ro];
+    if (WEIGHTED) vbuf[p] = v[ro];
+  }
   float ell[16];
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
@@ -156,12 +170,52 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
   for (int p = 1; p < 16; ++p) mx = fmaxf(mx, ell[p]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float se = 0.f;
+  float e[16], se = 0.f;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) se += expf(ell[p] - mx);
+  for (int p = 0; p < 16; ++p) {
+    e[p] = expf(ell[p] - mx);
+    se += e[p];
+  }
   se += __shfl_xor(se, 16);
   se += __shfl_xor(se, 32);
-  if (lane == 0) bias[bh * g.Vt + j] = mx + logf(se * (1.0f / VSA_TILE_TOKENS));
+  const float lme = mx + logf(se * (1.0f / VSA_TILE_TOKENS));  // log mean exp of the l'_t
+  if (!WEIGHTED) {
+    if (lane == 0) bias[bh * g.Vt + j] = lme;
+    return;
+  }
+  // weighted sums over this lane's rows, then over the four row groups
+  float ew = 0.f, ak[8], av[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ak[i] = av[i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    ew += e[p] * ell[p];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      ak[2 * w] += e[p] * (bf16lo(buf[p][w]) - kb[2 * w]);
+      ak[2 * w + 1] += e[p] * (bf16hi(buf[p][w]) - kb[2 * w + 1]);
+      av[2 * w] += e[p] * bf16lo(vbuf[p][w]);
+      av[2 * w + 1] += e[p] * bf16hi(vbuf[p][w]);
+    }
+  }
+  ew += __shfl_xor(ew, 16);
+  ew += __shfl_xor(ew, 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ak[i] += __shfl_xor(ak[i], 16);
+    ak[i] += __shfl_xor(ak[i], 32);
+    av[i] += __shfl_xor(av[i], 16);
+    av[i] += __shfl_xor(av[i], 32);
+  }
+  const float inv = 1.0f / se;
+  if (grp == 0) {
+    float kt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kt[i] = kb[i] + ak[i] * inv;
+    store8(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, kt, 1.0f);
+    store8(vbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, av, inv);
+  }
+  if (lane == 0) bias[bh * g.Vt + j] = lme - ew * inv;
 }
 
 }  // namespace
@@ -177,9 +231,13 @@ void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipSt
   hipLaunchKernelGGL(vsa_anchor_kernel, dim3(g.heads, g.batch), dim3(1024), 0, st, g, qbar, anchor);
 }
 
-void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
-                        float* bias, hipStream_t st) {
+void vsa_launch_logmass(const VsaGeom& g, const void* k, const void* v, float* kbar, float* vbar,
+                        const float* anchor, float* bias, hipStream_t st) {
   dim3 grid((g.heads + 3) / 4, g.Vt, g.batch);
-  hipLaunchKernelGGL(vsa_logmass_kernel, grid, dim3(256), 0, st, g, (const u32x4*)k, kbar, anchor,
-                     bias);
+  if (g.coarse == VSA_COARSE_WEIGHTED_LOGMASS)
+    hipLaunchKernelGGL(vsa_logmass_kernel<true>, grid, dim3(256), 0, st, g, (const u32x4*)k, (const u32x4*)v,
+                       kbar, vbar, anchor, bias);
+  else
+    hipLaunchKernelGGL(vsa_logmass_kernel<false>, grid, dim3(256), 0, st, g, (const u32x4*)k, (const u32x4*)v,
+                       kbar, vbar, anchor, bias);
 }

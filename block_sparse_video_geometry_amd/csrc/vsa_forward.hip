@@ -140,9 +140,9 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   } while (0)
 
   VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
-  if (G.coarse == VSA_COARSE_MEAN_LOGMASS) {
+  if (G.coarse == VSA_COARSE_MEAN_LOGMASS || G.coarse == VSA_COARSE_WEIGHTED_LOGMASS) {
     VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
-    VSA_STEP("logmass", vsa_launch_logmass(G, k, kbar, anchor, bias, st));
+    VSA_STEP("logmass", vsa_launch_logmass(G, k, v, kbar, vbar, anchor, bias, st));
   }
   VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, st));
   if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));

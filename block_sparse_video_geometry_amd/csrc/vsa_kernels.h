@@ -13,9 +13,10 @@ void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void*
 // Mean video query per (batch, head) (log-mass anchor).
 void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipStream_t st);
 
-// Log-mass bias per video key tile.
-void vsa_launch_logmass(const VsaGeom& g, const void* k, const float* kbar, const float* anchor,
-                        float* bias, hipStream_t st);
+// Log-mass bias per video key tile; in the weighted mode also the weighted key / value
+// summaries, written over kbar and vbar.
+void vsa_launch_logmass(const VsaGeom& g, const void* k, const void* v, float* kbar, float* vbar,
+                        const float* anchor, float* bias, hipStream_t st);
 
 // Coarse branch: S = scale qbar kbar^T + b for the sparse rows against the video tiles
 // (written to scores, with the per-block tau sums), the row softmax, and

@@ -44,7 +44,8 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   if (o.sink != VSA_SINK_EXACT_KV && o.sink != VSA_SINK_EXACT_KV_AND_ROWS)
     return VSA_ERR_UNSUPPORTED;
   if (o.select != VSA_SELECT_TOPK && o.select != VSA_SELECT_TAU) return VSA_ERR_UNSUPPORTED;
-  if (o.coarse != VSA_COARSE_MEAN && o.coarse != VSA_COARSE_MEAN_LOGMASS)
+  if (o.coarse != VSA_COARSE_MEAN && o.coarse != VSA_COARSE_MEAN_LOGMASS &&
+      o.coarse != VSA_COARSE_WEIGHTED_LOGMASS)
     return VSA_ERR_UNSUPPORTED;
   if (o.select == VSA_SELECT_TOPK && !(keep_percent > 0.0f && keep_percent <= 100.0f))
     return VSA_ERR_UNSUPPORTED;

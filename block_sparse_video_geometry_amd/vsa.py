@@ -22,7 +22,7 @@ VSA_ERR_NO_MEMORY = -5
 VSA_SEG_TEXT, VSA_SEG_REF_IMAGE, VSA_SEG_REF_AUDIO, VSA_SEG_OTHER_PREFIX, VSA_SEG_VIDEO = range(5)
 VSA_SINK_EXACT_KV, VSA_SINK_EXACT_KV_AND_ROWS = 1, 2
 VSA_SELECT_TOPK, VSA_SELECT_TAU = 0, 1
-VSA_COARSE_MEAN, VSA_COARSE_MEAN_LOGMASS = 0, 1
+VSA_COARSE_MEAN, VSA_COARSE_MEAN_LOGMASS, VSA_COARSE_WEIGHTED_LOGMASS = 0, 1, 2
 
 HEAD_DIM = 128
 

@@ -106,8 +106,16 @@ typedef enum { VSA_SELECT_TOPK = 0, VSA_SELECT_TAU = 1 } vsa_select;
 /* Coarse logits: MEAN is s * qbar . kbar; MEAN_LOGMASS adds the per video
  * tile bias b_j = log(mean_{t in j} exp(s q_a . (k_t - kbar_j))) with q_a the
  * mean video query of the (batch, head) ("Que cambia Spark-Attn",
- * Spark-Reweight).  s = 1/sqrt(128). */
-typedef enum { VSA_COARSE_MEAN = 0, VSA_COARSE_MEAN_LOGMASS = 1 } vsa_coarse;
+ * Spark-Reweight).  WEIGHTED_LOGMASS (same item: weighted summaries in place of
+ * the means) replaces kbar_j and vbar_j by the anchor's attention over the
+ * tile, ktil_j = sum_t w_t k_t and vtil_j = sum_t w_t v_t with
+ * w_t = softmax_{t in j}(s q_a . k_t), and takes
+ * b_j = log(mean_t exp(s q_a . k_t)) - s q_a . ktil_j.  s = 1/sqrt(128). */
+typedef enum {
+  VSA_COARSE_MEAN = 0,
+  VSA_COARSE_MEAN_LOGMASS = 1,
+  VSA_COARSE_WEIGHTED_LOGMASS = 2
+} vsa_coarse;
 
 typedef struct {
   int32_t sink;    /* vsa_sink */

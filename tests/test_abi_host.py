@@ -68,6 +68,7 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, sink=3), -2),
     (dict(segs=GOOD, select=2), -2),
     (dict(segs=GOOD, coarse=5), -2),
+    (dict(segs=GOOD, coarse=2), 0),                                   # weighted summaries
     (dict(segs=GOOD, heads=0), -1),
     (dict(segs=GOOD, batch=0), -1),
     (dict(segs=[(i * 4, 4, 0) for i in range(17)] + [(68, 1024, 4)]), -2),   # > 16 prefix spans

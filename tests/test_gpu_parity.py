@@ -16,7 +16,8 @@ import parity as PAR
 from oracle import vsa_oracle as O
 from workloads.synth import (WORKLOADS, Workload, make_inputs, scaled_down, SEG_TEXT,
                              SEG_REF_IMAGE, SEG_REF_AUDIO, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS,
-                             SELECT_TOPK, SELECT_TAU, COARSE_MEAN, COARSE_MEAN_LOGMASS)
+                             SELECT_TOPK, SELECT_TAU, COARSE_MEAN, COARSE_MEAN_LOGMASS,
+                             COARSE_WEIGHTED_LOGMASS)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +57,9 @@ SMALL_CASES = [
     scaled_down(WORKLOADS["full_tau_1.5"], heads=2, grid=FULL_SMALL_GRID, name="tau15_small"),
     scaled_down(WORKLOADS["full_tau_2.0"], heads=2, grid=FULL_SMALL_GRID, name="tau2_small"),
     scaled_down(WORKLOADS["full_logmass"], heads=2, grid=FULL_SMALL_GRID, name="logmass_small"),
+    scaled_down(WORKLOADS["full_weighted"], heads=2, grid=FULL_SMALL_GRID, name="weighted_small"),
+    Workload("weighted_tau", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 40)), (8, 16, 16), 0.0,
+             SINK_EXACT_KV, SELECT_TAU, COARSE_WEIGHTED_LOGMASS, 1.0, seed=84, recipe="offset"),
     # ragged prefix tiles, video span first, exact_kv rows, odd head count
     Workload("ragged_video_first", 3, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 64), (SEG_REF_AUDIO, 30)),
              (8, 12, 16), 20.0, SINK_EXACT_KV, seed=71, recipe="scaled", video_first=True),
@@ -146,7 +150,7 @@ def _inputs_for_seed(name):
 
 
 FULL_CASES = ["full", "full_smooth_20", "full_smooth_100", "full_tau_1.0", "full_tau_1.5",
-              "full_tau_2.0", "full_logmass"]
+              "full_tau_2.0", "full_logmass", "full_weighted"]
 
 
 @pytest.mark.parametrize("name", FULL_CASES)
@@ -154,7 +158,8 @@ def test_parity_full_size_sampled(name):
     w = WORKLOADS[name]
     # workloads that share a seed share their inputs
     src = {"full_smooth_100": "full_smooth_20", "full_tau_1.5": "full_tau_1.0",
-           "full_tau_2.0": "full_tau_1.0", "full_logmass": "full_tau_1.0"}.get(name, name)
+           "full_tau_2.0": "full_tau_1.0", "full_logmass": "full_tau_1.0",
+           "full_weighted": "full_tau_1.0"}.get(name, name)
     x = _inputs_for_seed(src)
     plan, ws, o, _ = run_gpu(w, x)
     gpu = PAR.gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar",

@@ -105,6 +105,10 @@ WORKLOADS = {
     "full_logmass": Workload("full_logmass", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
                              SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, COARSE_MEAN_LOGMASS,
                              seed=1005, recipe="offset"),
+    # the log-mass workload with weighted key / value summaries in place of the means
+    "full_weighted": Workload("full_weighted", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
+                              SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, COARSE_WEIGHTED_LOGMASS,
+                              seed=1005, recipe="offset"),
 }
 
 
