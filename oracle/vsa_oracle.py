@@ -35,7 +35,9 @@ Method, in the pages' order:
   4. selection: top-k video key tiles per query tile at a keep fraction
      ([FH3] "The mechanism"; [BSA-es] top-k item), or a per-head threshold
      mean + tau * std ([BSA-es] Sol-Attn item); prefix tiles never pruned
-     ([R2V-fr] items 1-2; [R2V-en] "The Solution").
+     ([R2V-fr] items 1-2; [R2V-en] "The Solution"), unless sink_conditioning
+     is off, where they compete like video tiles ([FH3] "The inputs that
+     matter").
   5. fine branch: exact attention over the listed tiles ([BSA-es] first
      paragraph; [SPK-es] "Que cambia Spark-Attn"); conditioning query rows
      run dense under exact_kv_and_rows ([FH3] "The inputs that matter",
@@ -69,6 +71,14 @@ the design notes):
     row whose list ends up empty has a zero fine output;
   * log-mass bias b_j = log(mean_t exp(l_t - p_j)) with l_t = s q_a . k_t,
     p_j = s q_a . kbar_j and q_a the mean of all video queries;
+  * sink_conditioning off ([FH3] only says it is the cheapest setting and that
+    conditioning is then not protected): the prefix tiles lose their
+    exemption and join the candidate key tiles.  The coarse branch, the
+    log-mass bias and the selection then run over all Tq tiles in tile-id
+    order (a partial prefix tile is summarised over its valid tokens), every
+    query tile is a sparse row, k = ceil(keep * Tq / 100 - 1e-9) clamped to
+    [1, Tq], ties go to the lowest tile id, and the anchor stays the mean of
+    the video queries;
   * weighted summaries (the page does not give the weights): the anchor's own
     attention over the tile, w_t = softmax_t(l_t); ktil_j = sum_t w_t k_t,
     vtil_j = sum_t w_t v_t; the bias keeps the same anchor identity,
@@ -86,7 +96,7 @@ TILE_TOKENS = TILE_EDGE ** 3       # 64
 HEAD_DIM = 128
 
 SEG_TEXT, SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_OTHER_PREFIX, SEG_VIDEO = 0, 1, 2, 3, 4
-SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 1, 2
+SINK_OFF, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 0, 1, 2
 SELECT_TOPK, SELECT_TAU = 0, 1
 COARSE_MEAN, COARSE_MEAN_LOGMASS, COARSE_WEIGHTED_LOGMASS = 0, 1, 2
 
@@ -162,13 +172,28 @@ def map_geometry(segments, T: int, H: int, W: int) -> Geometry:
 
 
 def keep_count(keep_percent: float, n_video: int) -> int:
-    """Number k of video key tiles kept per query tile at a keep percent.
+    """Number k of candidate key tiles kept per query tile at a keep percent.
 
     [FH3] "The inputs that matter": video_keep_percent; the plain reading of
-    a percent of Vt that is not an integer is to round up.
+    a percent of the candidates (Vt, or Tq with sink off) that is not an
+    integer is to round up.
     """
     k = math.ceil(keep_percent * n_video / 100.0 - 1e-9)
     return max(1, min(n_video, k))
+
+
+def key_candidates(geom: Geometry, sink: int) -> list:
+    """Tile ids that compete in the coarse branch and the selection.
+
+    [FH3] "The inputs that matter", sink_conditioning: exact_kv and
+    exact_kv_and_rows protect the conditioning keys, so only video tiles
+    compete; off protects nothing, so every tile competes.
+    """
+    if sink == SINK_OFF:
+        return list(range(geom.n_tiles))
+    if sink in (SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS):
+        return list(range(geom.n_prefix, geom.n_tiles))
+    raise ValueError("unsupported sink mode")
 
 
 def row_classes(geom: Geometry, sink: int):
@@ -180,7 +205,7 @@ def row_classes(geom: Geometry, sink: int):
     """
     prefix = list(range(geom.n_prefix))
     video = list(range(geom.n_prefix, geom.n_tiles))
-    if sink == SINK_EXACT_KV:
+    if sink in (SINK_OFF, SINK_EXACT_KV):
         return prefix + video, []
     if sink == SINK_EXACT_KV_AND_ROWS:
         return video, prefix
@@ -201,22 +226,23 @@ def pool_tiles(X: np.ndarray, tiles) -> np.ndarray:
     return np.stack([X[t].mean(axis=0) for t in tiles])
 
 
-def logmass_bias(Q: np.ndarray, K: np.ndarray, geom: Geometry, scale: float):
-    """Per video key tile log-mass bias, anchored at the mean video query.
+def logmass_bias(Q: np.ndarray, K: np.ndarray, geom: Geometry, scale: float, cand=None):
+    """Per candidate key tile log-mass bias, anchored at the mean video query.
 
     [SPK-es] "Que cambia Spark-Attn", Spark-Reweight: mean pooling puts
     exp(E[x]) in place of E[exp(x)]; a bias restores the missing mass, and the
     score uses the mean of the video queries as a per-head anchor.
       q_a = mean of Q over all valid video tokens
       l_t = s q_a . k_t,  p_j = s q_a . kbar_j
-      b_j = log( mean_{t in j} exp(l_t - p_j) )
-    Returns (b [Vt], q_a [D]).
+      b_j = log( mean_{t in j} exp(l_t - p_j) )   (mean over the valid tokens)
+    cand: candidate tile ids (default: the video tiles).
+    Returns (b [len(cand)], q_a [D]).
     """
-    vt = geom.tiles[geom.n_prefix:]
-    video_tokens = np.concatenate(vt)
+    video_tokens = np.concatenate(geom.tiles[geom.n_prefix:])
     q_a = Q[video_tokens].mean(axis=0)
-    b = np.empty(len(vt))
-    for j, toks in enumerate(vt):
+    ct = geom.tiles[geom.n_prefix:] if cand is None else [geom.tiles[t] for t in cand]
+    b = np.empty(len(ct))
+    for j, toks in enumerate(ct):
         kbar = K[toks].mean(axis=0)
         p = scale * (q_a @ kbar)
         ell = scale * (K[toks] @ q_a)
@@ -224,8 +250,9 @@ def logmass_bias(Q: np.ndarray, K: np.ndarray, geom: Geometry, scale: float):
     return b, q_a
 
 
-def weighted_summaries(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry, scale: float):
-    """Weighted key / value summaries of the video tiles plus the log-mass bias.
+def weighted_summaries(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry, scale: float,
+                       cand=None):
+    """Weighted key / value summaries of the candidate tiles plus the log-mass bias.
 
     [SPK-es] "Que cambia Spark-Attn", Spark-Reweight: weighted summaries replace
     the mean-pooled key / value summary, with the log-mass bias on top and the
@@ -235,14 +262,16 @@ def weighted_summaries(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geomet
       l_t = s q_a . k_t,  w_t = exp(l_t) / sum_{t' in j} exp(l_t')
       ktil_j = sum_t w_t k_t,  vtil_j = sum_t w_t v_t
       b_j = log( mean_{t in j} exp(l_t) ) - s q_a . ktil_j
-    so that exp(s q_a . ktil_j + b_j) is mean_t exp(l_t), as for the plain bias.
-    Returns (ktil [Vt, D], vtil [Vt, D], b [Vt], q_a [D]).
+    so that exp(s q_a . ktil_j + b_j) is mean_t exp(l_t), as for the plain bias
+    (sums and means over the tile's valid tokens).
+    cand: candidate tile ids (default: the video tiles).
+    Returns (ktil [n, D], vtil [n, D], b [n], q_a [D]) with n = len(cand).
     """
-    vt = geom.tiles[geom.n_prefix:]
-    q_a = Q[np.concatenate(vt)].mean(axis=0)
+    q_a = Q[np.concatenate(geom.tiles[geom.n_prefix:])].mean(axis=0)
+    ct = geom.tiles[geom.n_prefix:] if cand is None else [geom.tiles[t] for t in cand]
     D = K.shape[1]
-    ktil, vtil, b = np.empty((len(vt), D)), np.empty((len(vt), D)), np.empty(len(vt))
-    for j, toks in enumerate(vt):
+    ktil, vtil, b = np.empty((len(ct), D)), np.empty((len(ct), D)), np.empty(len(ct))
+    for j, toks in enumerate(ct):
         ell = scale * (K[toks] @ q_a)
         m = ell.max()
         e = np.exp(ell - m)
@@ -257,7 +286,7 @@ def coarse_branch(Qbar: np.ndarray, Kbar: np.ndarray, Vbar: np.ndarray,
                   bias: np.ndarray, scale: float):
     """Coarse scores, softmax and output for a set of query tiles.
 
-    S_ij = s qbar_i . kbar_j + b_j over video key tiles j; P = row softmax;
+    S_ij = s qbar_i . kbar_j + b_j over the candidate key tiles j; P = row softmax;
     O_c,i = sum_j P_ij vbar_j.  Returns (S, O_c).
     """
     S = scale * (Qbar @ Kbar.T) + bias[None, :]
@@ -271,8 +300,8 @@ def coarse_branch(Qbar: np.ndarray, Kbar: np.ndarray, Vbar: np.ndarray,
 # 4. selection
 # --------------------------------------------------------------------------
 def select_topk(S_row: np.ndarray, k: int) -> np.ndarray:
-    """The k largest logits; equal logits go to the lowest tile index.
-    Returns the kept video tile indices in ascending order."""
+    """The k largest logits; equal logits go to the lowest candidate index.
+    Returns the kept candidate indices in ascending order."""
     order = sorted(range(len(S_row)), key=lambda j: (-S_row[j], j))
     return np.array(sorted(order[:k]), dtype=np.int64)
 
@@ -292,11 +321,14 @@ def select_tau(S_row: np.ndarray, thr: float) -> np.ndarray:
     return np.nonzero(S_row > thr)[0].astype(np.int64)
 
 
-def row_list(geom: Geometry, video_sel) -> np.ndarray:
-    """Key tiles of one sparse row: every prefix tile (never pruned) then the
-    kept video tiles, both ascending, as tile ids."""
-    return np.concatenate([np.arange(geom.n_prefix, dtype=np.int64),
-                           geom.n_prefix + np.asarray(video_sel, dtype=np.int64)])
+def row_list(geom: Geometry, video_sel, sink: int = SINK_EXACT_KV) -> np.ndarray:
+    """Key tiles of one sparse row, as ascending tile ids.  With the prefix
+    protected: every prefix tile (never pruned) then the kept video tiles;
+    with sink off: the kept candidates, which are tile ids themselves."""
+    sel = np.asarray(video_sel, dtype=np.int64)
+    if sink == SINK_OFF:
+        return sel
+    return np.concatenate([np.arange(geom.n_prefix, dtype=np.int64), geom.n_prefix + sel])
 
 
 # --------------------------------------------------------------------------
@@ -337,15 +369,16 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
     if rows is None:
         rows = list(range(geom.n_tiles))
     rows_set = set(int(r) for r in rows)
-    vt = geom.tiles[geom.n_prefix:]
-    Kbar = pool_tiles(K, vt)
-    Vbar = pool_tiles(V, vt)
+    cand = key_candidates(geom, sink)
+    ct = [geom.tiles[t] for t in cand]
+    Kbar = pool_tiles(K, ct)
+    Vbar = pool_tiles(V, ct)
     if coarse == COARSE_MEAN_LOGMASS:
-        bias, q_a = logmass_bias(Q, K, geom, scale)
+        bias, q_a = logmass_bias(Q, K, geom, scale, cand)
     elif coarse == COARSE_WEIGHTED_LOGMASS:
-        Kbar, Vbar, bias, q_a = weighted_summaries(Q, K, V, geom, scale)
+        Kbar, Vbar, bias, q_a = weighted_summaries(Q, K, V, geom, scale, cand)
     elif coarse == COARSE_MEAN:
-        bias, q_a = np.zeros(len(vt)), None
+        bias, q_a = np.zeros(len(ct)), None
     else:
         raise ValueError("unsupported coarse mode")
 
@@ -353,9 +386,9 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
     need = sparse if select == SELECT_TAU else [i for i in sparse if i in rows_set]
     need_idx = {i: n for n, i in enumerate(need)}
     Qbar = pool_tiles(Q, [geom.tiles[i] for i in need]) if need else np.zeros((0, Q.shape[1]))
-    S, Oc = coarse_branch(Qbar, Kbar, Vbar, bias, scale) if need else (np.zeros((0, len(vt))), None)
+    S, Oc = coarse_branch(Qbar, Kbar, Vbar, bias, scale) if need else (np.zeros((0, len(ct))), None)
     thr = tau_threshold(S, tau) if select == SELECT_TAU else None
-    k = keep_count(keep_percent, geom.n_video) if select == SELECT_TOPK else None
+    k = keep_count(keep_percent, len(cand)) if select == SELECT_TOPK else None
 
     O = np.full_like(Q, np.nan)
     lists = {}
@@ -371,7 +404,7 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
                 sel = select_topk(srow, k)
             else:
                 sel = select_tau(srow, thr)
-            lst = row_list(geom, sel)
+            lst = row_list(geom, sel, sink)
             if list_override is not None and i in list_override:
                 lst = np.asarray(list_override[i], dtype=np.int64)
         lists[i] = lst
@@ -381,7 +414,7 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
         O[toks] = of
     inter = None
     if want_intermediates:
-        inter = dict(Kbar=Kbar, Vbar=Vbar, bias=bias, anchor=q_a, sparse_rows=need,
+        inter = dict(Kbar=Kbar, Vbar=Vbar, bias=bias, anchor=q_a, sparse_rows=need, cand=cand,
                      Qbar=Qbar, S=S, Oc=Oc, thr=thr, k=k, lists=lists)
     return O, inter
 

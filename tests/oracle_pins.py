@@ -25,7 +25,7 @@ import torch
 
 from oracle import vsa_oracle as O
 from workloads.synth import (Workload, make_inputs, f32_to_bf16_bits, SEG_TEXT,
-                             SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_VIDEO, SINK_EXACT_KV,
+                             SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_VIDEO, SINK_OFF, SINK_EXACT_KV,
                              SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, SELECT_TAU,
                              COARSE_MEAN, COARSE_MEAN_LOGMASS, COARSE_WEIGHTED_LOGMASS)
 
@@ -470,6 +470,138 @@ def check_prefix_permutation():
     assert np.abs(o2 - o[:, idx]).max() < 1e-12
 
 
+# ---------------------------------------------------------------- P-10 sink off
+# [FH3] "The inputs that matter", sink_conditioning: off protects no conditioning
+# tile, so the prefix tiles compete with the video tiles in the coarse branch and
+# the selection.  The pins rebuild every step from independent pieces: the tiles
+# from slicing and a reshape of the grid, the pooled logits from a matmul, the
+# selection by brute force over all k-subsets, the attention from torch's sdpa.
+SINK_OFF_W = Workload("off", 2, SMALL.prefix, SMALL.grid, 30.0, SINK_OFF, seed=71, recipe="scaled")
+# partial prefix tiles of 64 + 1 and 30 tokens
+SINK_OFF_PARTIAL = Workload("off_part", 1, ((SEG_TEXT, 65), (SEG_REF_AUDIO, 30)), (4, 8, 8), 20.0,
+                            SINK_OFF, seed=72, recipe="offset")
+
+
+def _all_tiles(w: Workload):
+    """Token ids of every tile in tile-id order: prefix chunks, then video cubes."""
+    return prefix_chunks(w) + [c for c in video_cube_tokens(w)]
+
+
+def _pool_all(X, w: Workload):
+    pre, vid = independent_pool(X, w)
+    return np.concatenate([pre, vid])
+
+
+def check_sink_off_dense(w: Workload):
+    """keep 100% with sink off keeps all Tq tiles (not Vt of them): with no gate the
+    output is dense attention over every token."""
+    x = make_inputs(w, with_gate=False)
+    out, _ = O.forward(x, w.segments(), w.grid, 100.0, SINK_OFF)
+    for h in range(w.heads):
+        ref = torch_sdpa(as_f64(x["q"][0, :, h]), as_f64(x["k"][0, :, h]), as_f64(x["v"][0, :, h]))
+        err = np.abs(out[0, :, h] - ref).max()
+        assert err < 1e-12, f"sink off dense h{h}: {err}"
+
+
+def check_sink_off_selection(w: Workload, k: int):
+    """Selection and output with sink off, rebuilt from independent pieces; k is the
+    expected keep count over all Tq tiles, given as a literal."""
+    x = make_inputs(w, with_gate=True)
+    tiles = _all_tiles(w)
+    Tq, P = len(tiles), len(prefix_chunks(w))
+    out, inter = O.forward(x, w.segments(), w.grid, w.keep, SINK_OFF, want_intermediates=True)
+    kept_pre = dropped_pre = 0
+    for h in range(w.heads):
+        Q, K, V, G = (as_f64(x[n][0, :, h]) for n in "qkvg")
+        qall, kall, vall = _pool_all(Q, w), _pool_all(K, w), _pool_all(V, w)
+        S = qall @ kall.T / math.sqrt(D)
+        oc = torch_sdpa(qall, kall, vall)
+        it = inter[(0, h)]
+        assert it["sparse_rows"] == list(range(Tq)), "sink off: every query tile is a sparse row"
+        assert it["S"].shape == S.shape, f"coarse logits shape {it['S'].shape} != {S.shape}"
+        assert np.abs(it["S"] - S).max() < 1e-12
+        assert np.abs(it["Oc"] - oc).max() < 1e-12
+        for i in range(Tq):
+            pick = brute_topk(list(S[i]), k)
+            assert list(it["lists"][i]) == pick, f"h{h} row {i}: {list(it['lists'][i])} != {pick}"
+            keys = np.concatenate([tiles[t] for t in pick])
+            ref = torch_sdpa(Q[tiles[i]], K[keys], V[keys]) + G[tiles[i]] * oc[i][None, :]
+            assert np.abs(out[0, tiles[i], h] - ref).max() < 1e-12, f"h{h} row {i} output"
+            n_pre = sum(1 for t in pick if t < P)
+            kept_pre += n_pre
+            dropped_pre += P - n_pre
+    assert kept_pre > 0 and dropped_pre > 0, "prefix tiles must both win and lose somewhere"
+
+
+def check_sink_off_tau(w: Workload, tau: float):
+    """Tau mode with sink off: the threshold's moments run over every (query tile, tile)
+    logit, prefix tiles included, and a row keeps the tiles above it (Python's exact
+    statistics module for the moments)."""
+    x = make_inputs(w, with_gate=False)
+    tiles = _all_tiles(w)
+    _, inter = O.forward(x, w.segments(), w.grid, 0.0, SINK_OFF, select=SELECT_TAU, tau=tau,
+                         want_intermediates=True)
+    for h in range(w.heads):
+        Q, K = as_f64(x["q"][0, :, h]), as_f64(x["k"][0, :, h])
+        S = _pool_all(Q, w) @ _pool_all(K, w).T / math.sqrt(D)
+        thr = statistics.fmean(S.ravel()) + tau * statistics.pstdev(S.ravel().tolist())
+        it = inter[(0, h)]
+        assert abs(it["thr"] - thr) < 1e-12
+        for i in range(len(tiles)):
+            want = [j for j in range(len(tiles)) if S[i, j] > thr]
+            assert list(it["lists"][i]) == want, f"h{h} row {i}"
+
+
+def check_sink_off_logmass():
+    """Log-mass bias and weighted summaries over partial prefix tiles (sink off): the
+    means run over a tile's valid tokens only, so a one-token tile has b = 0 and its
+    weighted summary is that token; every tile's biased pooled exponential equals
+    the mean token exponential summed directly; the anchor is the mean of the video
+    queries alone."""
+    w = SINK_OFF_PARTIAL
+    x = make_inputs(w)
+    geom = geom_of(w)
+    tiles = _all_tiles(w)
+    assert [len(t) for t in tiles[:3]] == [64, 1, 30]
+    s = 1.0 / math.sqrt(D)
+    Q, K, V = (as_f64(x[n][0, :, 0]) for n in "qkv")
+    q_a = Q[np.concatenate(video_cube_tokens(w))].mean(axis=0)
+    kmean = _pool_all(K, w)
+    cand = list(range(len(tiles)))
+    b, qa = O.logmass_bias(Q, K, geom, s, cand)
+    assert np.abs(qa - q_a).max() < 1e-14
+    assert len(b) == len(tiles)
+    assert abs(b[1]) < 1e-15, f"one-token tile bias {b[1]}"
+    for j, toks in enumerate(tiles):
+        lhs = math.exp(s * float(q_a @ kmean[j]) + b[j])
+        rhs = math.fsum(math.exp(s * float(q_a @ K[t])) for t in toks) / len(toks)
+        assert abs(lhs - rhs) <= 1e-12 * rhs, (j, lhs, rhs)
+    kt, vt, bw, _ = O.weighted_summaries(Q, K, V, geom, s, cand)
+    assert np.abs(kt[1] - K[tiles[1][0]]).max() < 1e-15 and np.abs(vt[1] - V[tiles[1][0]]).max() < 1e-15
+    assert abs(bw[1]) < 1e-15
+    for j, toks in enumerate(tiles):
+        v_ref = torch_sdpa(q_a[None, :], K[toks], V[toks])[0]
+        assert np.abs(vt[j] - v_ref).max() < 1e-12 * (1 + np.abs(v_ref).max()), j
+    # the forward uses these over all Tq tiles
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, SINK_OFF, coarse=COARSE_MEAN_LOGMASS,
+                         want_intermediates=True)
+    S_ref = _pool_all(Q, w) @ kmean.T * s + b[None, :]
+    assert np.abs(inter[(0, 0)]["S"] - S_ref).max() < 1e-12
+
+
+def check_sink_off_no_prefix():
+    """With no conditioning segment there is nothing to protect: sink off and
+    exact_kv give the same output."""
+    w = Workload("nopre", 2, (), (4, 8, 12), 25.0, SINK_OFF, seed=73, recipe="scaled")
+    x = make_inputs(w)
+    o_off, _ = O.forward(x, w.segments(), w.grid, w.keep, SINK_OFF)
+    o_kv, _ = O.forward(x, w.segments(), w.grid, w.keep, SINK_EXACT_KV)
+    assert np.array_equal(o_off, o_kv)
+    o_off, _ = O.forward(x, w.segments(), w.grid, 0.0, SINK_OFF, select=SELECT_TAU, tau=0.5)
+    o_kv, _ = O.forward(x, w.segments(), w.grid, 0.0, SINK_EXACT_KV, select=SELECT_TAU, tau=0.5)
+    assert np.array_equal(o_off, o_kv)
+
+
 ALL_CHECKS = [
     ("geometry", lambda: (check_geometry(SMALL), check_geometry(SMALL_VIDEO_FIRST),
                           check_geometry(GEOM_3D))),
@@ -491,4 +623,9 @@ ALL_CHECKS = [
     ("combine", lambda: check_combine(SMALL)),
     ("metamorphic", lambda: check_metamorphic(SMALL_VIDEO_FIRST)),
     ("prefix_permutation", check_prefix_permutation),
+    ("sink_off_dense", lambda: (check_sink_off_dense(SINK_OFF_W), check_sink_off_dense(SINK_OFF_PARTIAL))),
+    ("sink_off_selection", lambda: check_sink_off_selection(SINK_OFF_W, 3)),
+    ("sink_off_tau", lambda: (check_sink_off_tau(SINK_OFF_W, 1.0), check_sink_off_tau(SINK_OFF_PARTIAL, 0.5))),
+    ("sink_off_logmass", check_sink_off_logmass),
+    ("sink_off_no_prefix", check_sink_off_no_prefix),
 ]

@@ -3,8 +3,9 @@
 Selections: per (batch, head, sparse query tile) let S(k) and S(k+1) be the
 oracle's k-th and (k+1)-th largest coarse logits.  Where S(k) - S(k+1) > GAP
 the GPU list must equal the oracle's.  Elsewhere the GPU list must be a
-valid top-k within GAP (size P + k, every prefix tile, every kept logit
->= S(k) - GAP, every dropped logit <= S(k+1) + GAP); the oracle then adopts
+valid top-k within GAP (size P + k, every protected prefix tile, every kept
+logit >= S(k) - GAP, every dropped logit <= S(k+1) + GAP; with sink off no
+tile is protected and P is 0 here); the oracle then adopts
 the GPU's list for that row before the outputs are compared.  Tau mode: the
 GPU must agree wherever |S - thr| > GAP and its choice is adopted elsewhere.
 
@@ -51,7 +52,9 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
     geom = O.map_geometry(w.segments(), *w.grid)
     sparse, dense = O.row_classes(geom, w.sink)
     n_dense = len(dense)
-    P = geom.n_prefix
+    P = 0 if w.sink == O.SINK_OFF else geom.n_prefix   # protected (always listed) tiles
+    cand = O.key_candidates(geom, w.sink)
+    c0, nc = cand[0], len(cand)                        # candidates are tile ids c0 .. c0 + nc - 1
     B, N, H, D = x["q"].shape
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
@@ -93,9 +96,9 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
             glist = gpu["lists"][b, h, s, :cnt].astype(np.int64)
             olist = it["lists"][i]
             assert list(glist[:P]) == list(range(P)), f"(b{b},h{h},tile {i}) prefix tiles missing"
-            gvid = glist[P:] - P
+            gvid = glist[P:] - c0
             assert np.all(np.diff(gvid) > 0), f"(b{b},h{h},tile {i}) list not ascending"
-            assert gvid.size == 0 or (gvid.min() >= 0 and gvid.max() < geom.n_video)
+            assert gvid.size == 0 or (gvid.min() >= 0 and gvid.max() < nc)
             if w.select == O.SELECT_TOPK:
                 k = it["k"]
                 assert cnt == P + k, f"(b{b},h{h},tile {i}) count {cnt} != {P + k}"
@@ -107,7 +110,7 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
                         f"(b{b},h{h},tile {i}) selection differs at gap {sk - sk1:.3g}"
                     rep["exact_rows"] += 1
                 else:
-                    sel = np.zeros(geom.n_video, bool)
+                    sel = np.zeros(nc, bool)
                     sel[gvid] = True
                     assert np.all(srow_ref[sel] >= sk - gap), f"(b{b},h{h},tile {i}) weak pick"
                     assert np.all(srow_ref[~sel] <= sk1 + gap), f"(b{b},h{h},tile {i}) weak drop"
@@ -115,7 +118,7 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
                     rep["adopted_rows"] += 1
             else:
                 thr = it["thr"]
-                sel = np.zeros(geom.n_video, bool)
+                sel = np.zeros(nc, bool)
                 sel[gvid] = True
                 clear = np.abs(srow_ref - thr) > gap
                 assert np.array_equal(sel[clear], (srow_ref > thr)[clear]), \

@@ -14,7 +14,8 @@ from oracle import vsa_oracle as O
 
 _orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
                                       "logmass_bias", "coarse_branch", "tau_threshold",
-                                      "keep_count", "pool_tiles", "fine_row", "weighted_summaries")}
+                                      "keep_count", "pool_tiles", "fine_row", "weighted_summaries",
+                                      "key_candidates")}
 
 
 def _geom_swapped_axes(segments, T, H, W):
@@ -45,13 +46,31 @@ def _topk_smallest(S_row, k):
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
-def _bias_flipped(Q, K, geom, scale):
-    b, qa = _orig["logmass_bias"](Q, K, geom, scale)
+def _bias_flipped(Q, K, geom, scale, cand=None):
+    b, qa = _orig["logmass_bias"](Q, K, geom, scale, cand)
     return -b, qa
 
 
-def _bias_no_anchor(Q, K, geom, scale):
-    return np.zeros(geom.n_video), np.zeros(Q.shape[1])
+def _bias_no_anchor(Q, K, geom, scale, cand=None):
+    return np.zeros(geom.n_video if cand is None else len(cand)), np.zeros(Q.shape[1])
+
+
+def _bias_mean_over_64(Q, K, geom, scale, cand=None):
+    """The mean inside the log divided by 64 instead of the tile's valid token count."""
+    b, qa = _orig["logmass_bias"](Q, K, geom, scale, cand)
+    ids = range(geom.n_prefix, geom.n_tiles) if cand is None else cand
+    return np.array([bj + math.log(len(geom.tiles[t]) / 64.0) for bj, t in zip(b, ids)]), qa
+
+
+def _off_video_only(geom, sink):
+    return list(range(geom.n_prefix, geom.n_tiles))
+
+
+def _row_list_always_pinned(geom, sel, sink=1):
+    sel = np.asarray(sel, dtype=np.int64)
+    if sink == O.SINK_OFF:
+        return np.unique(np.concatenate([np.arange(geom.n_prefix, dtype=np.int64), sel]))
+    return _orig["row_list"](geom, sel, sink)
 
 
 def _coarse_no_bias(Qbar, Kbar, Vbar, bias, scale):
@@ -64,24 +83,24 @@ def _tau_variance(S, tau):
     return mu + tau * float(np.mean((vals - mu) ** 2))
 
 
-def _weighted_plain_means(Q, K, V, geom, scale):
-    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
-    tiles = geom.tiles[geom.n_prefix:]
+def _weighted_plain_means(Q, K, V, geom, scale, cand=None):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale, cand)
+    tiles = geom.tiles[geom.n_prefix:] if cand is None else [geom.tiles[t] for t in cand]
     return (np.stack([K[t].mean(axis=0) for t in tiles]), np.stack([V[t].mean(axis=0) for t in tiles]),
             b, qa)
 
 
-def _weighted_unnormalized(Q, K, V, geom, scale):
-    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
-    tiles = geom.tiles[geom.n_prefix:]
+def _weighted_unnormalized(Q, K, V, geom, scale, cand=None):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale, cand)
+    tiles = geom.tiles[geom.n_prefix:] if cand is None else [geom.tiles[t] for t in cand]
     ell = [scale * (K[t] @ qa) for t in tiles]
     e = [np.exp(l - l.max()) for l in ell]
     return np.stack([ei @ K[t] for ei, t in zip(e, tiles)]), np.stack([ei @ V[t] for ei, t in zip(e, tiles)]), b, qa
 
 
-def _weighted_bias_vs_mean(Q, K, V, geom, scale):
-    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale)
-    tiles = geom.tiles[geom.n_prefix:]
+def _weighted_bias_vs_mean(Q, K, V, geom, scale, cand=None):
+    kt, vt, b, qa = _orig["weighted_summaries"](Q, K, V, geom, scale, cand)
+    tiles = geom.tiles[geom.n_prefix:] if cand is None else [geom.tiles[t] for t in cand]
     b2 = np.array([b[j] + scale * (qa @ kt[j]) - scale * (qa @ K[t].mean(axis=0)) for j, t in enumerate(tiles)])
     return kt, vt, b2, qa
 
@@ -96,8 +115,8 @@ MUTATIONS = [
     ("tile_token_order", "map_geometry", _geom_token_order, "geometry"),
     ("ties_to_highest", "select_topk", _topk_high_ties, "topk_ties"),
     ("topk_smallest", "select_topk", _topk_smallest, "topk_bruteforce"),
-    ("prefix_dropped", "row_list", lambda geom, sel: geom.n_prefix + np.asarray(sel, dtype=np.int64),
-     "prefix_exempt"),
+    ("prefix_dropped", "row_list",
+     lambda geom, sel, sink=1: geom.n_prefix + np.asarray(sel, dtype=np.int64), "prefix_exempt"),
     ("bias_sign", "logmass_bias", _bias_flipped, "logmass"),
     ("bias_no_anchor", "logmass_bias", _bias_no_anchor, "logmass"),
     ("coarse_ignores_bias", "coarse_branch", _coarse_no_bias, "coarse_logmass"),
@@ -108,6 +127,10 @@ MUTATIONS = [
     ("weighted_plain_means", "weighted_summaries", _weighted_plain_means, "weighted_summaries"),
     ("weighted_unnormalized", "weighted_summaries", _weighted_unnormalized, "weighted_summaries"),
     ("weighted_bias_vs_mean", "weighted_summaries", _weighted_bias_vs_mean, "weighted_summaries"),
+    ("off_video_only", "key_candidates", _off_video_only, "sink_off_selection"),
+    ("off_video_only_tau", "key_candidates", _off_video_only, "sink_off_tau"),
+    ("off_prefix_pinned", "row_list", _row_list_always_pinned, "sink_off_selection"),
+    ("bias_mean_over_64", "logmass_bias", _bias_mean_over_64, "sink_off_logmass"),
 ]
 
 

@@ -34,7 +34,7 @@ HEAD_DIM = 128
 
 # segment kinds, same numbering as the C ABI
 SEG_TEXT, SEG_REF_IMAGE, SEG_REF_AUDIO, SEG_OTHER_PREFIX, SEG_VIDEO = 0, 1, 2, 3, 4
-SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 1, 2
+SINK_OFF, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS = 0, 1, 2
 SELECT_TOPK, SELECT_TAU = 0, 1
 COARSE_MEAN, COARSE_MEAN_LOGMASS, COARSE_WEIGHTED_LOGMASS = 0, 1, 2
 
