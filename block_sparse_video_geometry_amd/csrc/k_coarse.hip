@@ -7,7 +7,9 @@
 // branch attends over mean-pooled summaries.
 //
 // S_ij = s qbar_i . kbar_j + b_j for every sparse query tile i and every
-// video key tile j; P = softmax_j(S); O_c,i = sum_j P_ij vbar_j.  All fp32
+// candidate key tile j (the video tiles; every tile when sink_conditioning is
+// off, "BSAI FastH3 Native VSA (recipe)", "The inputs that matter");
+// P = softmax_j(S); O_c,i = sum_j P_ij vbar_j.  All fp32
 // (the ranking must hold the oracle's order wherever its logit gap > 1e-4;
 // bf16 inputs to this dot product would not), on the fp32 MFMAs: two dense
 // contractions per head, ~4.6 GFLOP at 32 heads x 564 tiles, fused in one
@@ -18,12 +20,12 @@
 namespace {
 
 constexpr int CROWS = VSA_COARSE_ROWS;  // 64 sparse rows per workgroup, 16 per wave
-constexpr int CCH = 64;                 // video tiles per LDS chunk
+constexpr int CCH = 64;                 // candidate tiles per LDS chunk
 constexpr int LW = VSA_HEAD_DIM + 4;    // padded LDS row (floats)
 constexpr float LOG2E_F = 1.4426950408889634f;
 
 // One workgroup per (64 sparse rows, head, batch); wave w owns rows 16 w .. 16 w + 15.
-// Per chunk of 64 video tiles (K-bar, V-bar and the bias staged in LDS, the next chunk's
+// Per chunk of 64 candidate tiles (K-bar, V-bar and the bias staged in LDS, the next chunk's
 // loads in flight meanwhile):
 //   S^T = K-bar Q-bar^T on fp32 MFMAs (v_mfma_f32_16x16x4_f32).  MFMA step t of a
 //     16-tile block contracts dims k(t, g) = 16 (t >> 2) + 4 g + (t & 3) for lane group g,
@@ -58,9 +60,9 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
 #pragma unroll
     for (int m = 0; m < 8; ++m) qf[m] = live ? qp[4 * m + lg] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float* kb = kbar + bh * g.Vt * VSA_HEAD_DIM;
-  const float* vb = vbar + bh * g.Vt * VSA_HEAD_DIM;
-  const float* bb = bias + bh * g.Vt;
+  const float* kb = kbar + bh * g.Kc * VSA_HEAD_DIM;
+  const float* vb = vbar + bh * g.Kc * VSA_HEAD_DIM;
+  const float* bb = bias + bh * g.Kc;
 
   // chunk staging: thread tid moves rows (tid >> 5) + 8 r, 16-byte column tid & 31
   f32x4 kr[8], vr[8];
@@ -70,12 +72,12 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
     for (int r = 0; r < 8; ++r) {
       const int j = j0 + (tid >> 5) + 8 * r;
       kr[r] = vr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j < g.Vt) {
+      if (j < g.Kc) {
         kr[r] = reinterpret_cast<const f32x4*>(kb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
         vr[r] = reinterpret_cast<const f32x4*>(vb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
       }
     }
-    br = (tid < CCH && j0 + tid < g.Vt) ? bb[j0 + tid] : 0.f;
+    br = (tid < CCH && j0 + tid < g.Kc) ? bb[j0 + tid] : 0.f;
   };
   auto stash = [&]() {
 #pragma unroll
@@ -91,14 +93,14 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   double ssum = 0.0, ssq = 0.0;
-  const bool vec_out = (g.Vt & 3) == 0;  // 16-byte score stores stay aligned
+  const bool vec_out = (g.Kc & 3) == 0;  // 16-byte score stores stay aligned
 
   fetch(0);
-  for (int j0 = 0; j0 < g.Vt; j0 += CCH) {
+  for (int j0 = 0; j0 < g.Kc; j0 += CCH) {
     __syncthreads();  // the previous chunk's LDS reads are done
     stash();
     __syncthreads();
-    if (j0 + CCH < g.Vt) fetch(j0 + CCH);
+    if (j0 + CCH < g.Kc) fetch(j0 + CCH);
 
     f32x4 st[4];
 #pragma unroll
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sv[i] = st[cb][i] * g.scale + bs[jl + i];
-        const bool valid = j0 + jl + i < g.Vt;
+        const bool valid = j0 + jl + i < g.Kc;
         if (live && valid) {
           ssum += (double)sv[i];
           ssq += (double)sv[i] * (double)sv[i];
@@ -131,13 +133,13 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
         cm = fmaxf(cm, st[cb][i]);
       }
       if (live) {
-        float* dst = scores + (bh * g.Qs + row) * g.Vt + j0 + jl;
-        if (vec_out && j0 + jl + 3 < g.Vt) {
+        float* dst = scores + (bh * g.Qs + row) * g.Kc + j0 + jl;
+        if (vec_out && j0 + jl + 3 < g.Kc) {
           *reinterpret_cast<f32x4*>(dst) = sv;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (j0 + jl + i < g.Vt) dst[i] = sv[i];
+            if (j0 + jl + i < g.Kc) dst[i] = sv[i];
         }
       }
     }
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
   }
 }
 
-// thr = mu + tau * sigma (population) over all Qs * Vt logits of a (batch, head).
+// thr = mu + tau * sigma (population) over all Qs * Kc logits of a (batch, head).
 __global__ void vsa_tau_kernel(VsaGeom g, const double* __restrict__ statp, float* __restrict__ thr) {
   const size_t bh = (size_t)blockIdx.y * g.heads + blockIdx.x;
   if (threadIdx.x != 0) return;
@@ -213,7 +215,7 @@ __global__ void vsa_tau_kernel(VsaGeom g, const double* __restrict__ statp, floa
     a += statp[(bh * g.coarse_blocks + i) * 2 + 0];
     q += statp[(bh * g.coarse_blocks + i) * 2 + 1];
   }
-  const double n = (double)g.Qs * (double)g.Vt;
+  const double n = (double)g.Qs * (double)g.Kc;
   const double mu = a / n;
   double var = q / n - mu * mu;
   if (var < 0.0) var = 0.0;

@@ -8,10 +8,14 @@
 // exp(E[x]) in for E[exp(x)]; a bias per tile, scored with the mean video
 // query as the anchor, restores the missing mass.  The same item's weighted
 // summaries replace the means by the anchor's attention over each tile.
+// K and V summaries and biases cover the candidate key tiles [kc0, kc0 + Kc):
+// the video tiles, or every tile when sink_conditioning is off ("BSAI FastH3
+// Native VSA (recipe)", "The inputs that matter"); a partial prefix tile is
+// summarised over its valid tokens.
 //
 // HBM-bound: each (tile, head) slice of Q, K, V is read once; one wave per
 // (tile, head), 16 lanes per token (16 x 16 B = one 256-byte head row), four
-// tokens per load instruction; a video tile's 48 loads (Q, K, V) are all in flight at once.
+// tokens per load instruction; a candidate tile's 48 loads (Q, K, V) are all in flight at once.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -20,16 +24,22 @@ namespace {
 // This wave's 64 tile rows of one head: lane group grp = lane/16 owns rows 4p + grp, lane
 // chunk c = lane%16 owns dims 8c..8c+7.  tile_load only issues the loads, so a wave can
 // have the Q, K and V rows of a tile in flight at once; tile_sum reduces them over the
-// four groups (every lane holds its chunk's sums).
+// four groups (every lane holds its chunk's sums).  VIDEO: t is a video tile, whose 64
+// rows are all valid, so the loads need no padding test.
+template <bool VIDEO>
 __device__ __forceinline__ void tile_load(const VsaGeom& g, const u32x4* __restrict__ X, int b, int h,
                                           int t, int grp, int c, u32x4 buf[16]) {
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    const int tok = tile_token(g, t, 4 * p + grp);
-    if (tok >= 0)
-      buf[p] = X[row_offset(g, b, tok, h) / 8 + c];
-    else
-      buf[p] = u32x4{0u, 0u, 0u, 0u};
+    if (VIDEO) {
+      buf[p] = X[row_offset(g, b, video_token(g, t, 4 * p + grp), h) / 8 + c];
+    } else {
+      const int tok = tile_token(g, t, 4 * p + grp);
+      if (tok >= 0)
+        buf[p] = X[row_offset(g, b, tok, h) / 8 + c];
+      else
+        buf[p] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 __device__ __forceinline__ void tile_sum(const u32x4 buf[16], float acc[8]) {
@@ -53,6 +63,38 @@ __device__ __forceinline__ void store8(float* dst, const float v[8], float mul) 
   d4[1] = f32x4{v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul};
 }
 
+// Q-bar of tile t, and K-bar / V-bar when KV (t is a candidate key tile).
+template <bool VIDEO, bool KV>
+__device__ __forceinline__ void pool_tile(const VsaGeom& g, const u32x4* __restrict__ q,
+                                          const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                          float* __restrict__ qbar, float* __restrict__ kbar,
+                                          float* __restrict__ vbar, float* __restrict__ bias, int b,
+                                          int h, int t, int lane) {
+  const int grp = lane >> 4, c = lane & 15;
+  const size_t bh = (size_t)b * g.heads + h;
+  const float inv = VIDEO ? 1.0f / VSA_TILE_TOKENS : 1.0f / (float)tile_valid(g, t);
+  float acc[8];
+  u32x4 bq[16];
+  tile_load<VIDEO>(g, q, b, h, t, grp, c, bq);
+  if (!KV) {
+    tile_sum(bq, acc);
+    if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+    return;
+  }
+  // candidate key tile: all 48 loads in flight before the first sum
+  u32x4 bk[16], bv[16];
+  tile_load<VIDEO>(g, k, b, h, t, grp, c, bk);
+  tile_load<VIDEO>(g, v, b, h, t, grp, c, bv);
+  const int j = t - g.kc0;
+  tile_sum(bq, acc);
+  if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  tile_sum(bk, acc);
+  if (grp == 0) store8(kbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  tile_sum(bv, acc);
+  if (grp == 0) store8(vbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  if (g.coarse == VSA_COARSE_MEAN && lane == 0) bias[bh * g.Kc + j] = 0.0f;
+}
+
 __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* __restrict__ q,
                                                        const u32x4* __restrict__ k,
                                                        const u32x4* __restrict__ v,
@@ -67,29 +109,12 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* _
   const int h = blockIdx.x * 4 + wave;
   const int b = blockIdx.z;
   if (h >= g.heads) return;
-  const int grp = lane >> 4, c = lane & 15;
-  const size_t bh = (size_t)b * g.heads + h;
-  const float inv = 1.0f / (float)tile_valid(g, t);
-  float acc[8];
-  u32x4 bq[16];
-  tile_load(g, q, b, h, t, grp, c, bq);
-  if (t < g.P) {
-    tile_sum(bq, acc);
-    if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
-    return;
-  }
-  // video tile: all 48 loads in flight before the first sum
-  u32x4 bk[16], bv[16];
-  tile_load(g, k, b, h, t, grp, c, bk);
-  tile_load(g, v, b, h, t, grp, c, bv);
-  const int j = t - g.P;
-  tile_sum(bq, acc);
-  if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
-  tile_sum(bk, acc);
-  if (grp == 0) store8(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
-  tile_sum(bv, acc);
-  if (grp == 0) store8(vbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
-  if (g.coarse == VSA_COARSE_MEAN && lane == 0) bias[bh * g.Vt + j] = 0.0f;
+  if (t >= g.P)  // video tiles are always candidates
+    pool_tile<true, true>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
+  else if (t >= g.kc0)  // prefix candidate (sink off)
+    pool_tile<false, true>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
+  else
+    pool_tile<false, false>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
 }
 
 // q_a = mean of the video tiles' qbar (every video tile holds 64 tokens, so
@@ -112,31 +137,33 @@ __global__ __launch_bounds__(1024) void vsa_anchor_kernel(VsaGeom g, const float
   }
 }
 
-// b_j = log(mean_t exp(s q_a . (k_t - kbar_j))), max-shifted.  One wave per
-// (video tile, head).  WEIGHTED (Spark-Reweight's weighted summaries, read as the
+// b_j = log(mean_t exp(s q_a . (k_t - kbar_j))), max-shifted, means and sums over the
+// tile's valid tokens.  One wave per (candidate tile, head).  WEIGHTED (Spark-Reweight's weighted summaries, read as the
 // anchor's attention over the tile): with the centred logits l'_t = s q_a . (k_t - kbar_j)
 // and w_t = softmax_t(l'_t), the kernel also writes
 //   ktil_j = kbar_j + sum_t w_t (k_t - kbar_j),  vtil_j = sum_t w_t v_t
 // over kbar_j and vbar_j, and the bias b_j = log(mean_t exp(l'_t)) - sum_t w_t l'_t, which is
 // log(mean_t exp(s q_a . k_t)) - s q_a . ktil_j.
-template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4* __restrict__ k,
+// PARTIAL: the launch covers prefix candidate tiles (sink off), which may hold padding
+// rows; a video tile always holds 64 tokens, so its launch skips the masking.
+template <bool WEIGHTED, bool PARTIAL>
+__global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, int t_first, const u32x4* __restrict__ k,
                                                           const u32x4* __restrict__ v,
                                                           float* __restrict__ kbar,
                                                           float* __restrict__ vbar,
                                                           const float* __restrict__ anchor,
                                                           float* __restrict__ bias) {
-  const int j = blockIdx.y;
+  const int t = t_first + blockIdx.y;
+  const int j = t - g.kc0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * 4 + wave;
   const int b = blockIdx.z;
   if (h >= g.heads) return;
   const int grp = lane >> 4, c = lane & 15;
   const size_t bh = (size_t)b * g.heads + h;
-  const int t = g.P + j;
   float qa[8], kb[8];
   const f32x4* a4 = reinterpret_cast<const f32x4*>(anchor + bh * VSA_HEAD_DIM + 8 * c);
-  const f32x4* k4 = reinterpret_cast<const f32x4*>(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c);
+  const f32x4* k4 = reinterpret_cast<const f32x4*>(kbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     qa[i] = a4[0][i];
@@ -144,11 +171,21 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
     kb[i] = k4[0][i];
     kb[4 + i] = k4[1][i];
   }
-  // rows 4 p + grp of the tile, dims 8 c .. 8 c + 7
+  // rows 4 p + grp of the tile, dims 8 c .. 8 c + 7.  A padding row of a partial prefix
+  // tile reloads row 0 (always valid) and takes no part: ok bit p clear, weight 0.
   u32x4 buf[16], vbuf[16];
+  unsigned ok = 0xffffu;
+  const int tok0 = PARTIAL ? tile_token(g, t, 0) : 0;
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    const long long ro = row_offset(g, b, tile_token(g, t, 4 * p + grp), h) / 8 + c;
+    int tok = PARTIAL ? tile_token(g, t, 4 * p + grp) : video_token(g, t, 4 * p + grp);
+    if (PARTIAL) {
+      if (tok < 0) {
+        ok &= ~(1u << p);
+        tok = tok0;
+      }
+    }
+    const long long ro = row_offset(g, b, tok, h) / 8 + c;
     buf[p] = k[ro];
     if (WEIGHTED) vbuf[p] = v[ro];
   }
@@ -165,22 +202,24 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
     for (int m = 1; m < 16; m <<= 1) s += __shfl_xor(s, m);
     ell[p] = s * g.scale;
   }
-  float mx = ell[0];
+  float mx = -INFINITY;
 #pragma unroll
-  for (int p = 1; p < 16; ++p) mx = fmaxf(mx, ell[p]);
+  for (int p = 0; p < 16; ++p)
+    if (!PARTIAL || (ok & (1u << p))) mx = fmaxf(mx, ell[p]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   float e[16], se = 0.f;
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    e[p] = expf(ell[p] - mx);
+    e[p] = (!PARTIAL || (ok & (1u << p))) ? expf(ell[p] - mx) : 0.f;  // row 0 is always valid
     se += e[p];
   }
   se += __shfl_xor(se, 16);
   se += __shfl_xor(se, 32);
-  const float lme = mx + logf(se * (1.0f / VSA_TILE_TOKENS));  // log mean exp of the l'_t
+  const float nvalid = PARTIAL ? (float)tile_valid(g, t) : (float)VSA_TILE_TOKENS;
+  const float lme = mx + logf(se / nvalid);  // log mean exp of the l'_t
   if (!WEIGHTED) {
-    if (lane == 0) bias[bh * g.Vt + j] = lme;
+    if (lane == 0) bias[bh * g.Kc + j] = lme;
     return;
   }
   // weighted sums over this lane's rows, then over the four row groups
@@ -212,10 +251,10 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, const u32x4
     float kt[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) kt[i] = kb[i] + ak[i] * inv;
-    store8(kbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, kt, 1.0f);
-    store8(vbar + (bh * g.Vt + j) * VSA_HEAD_DIM + 8 * c, av, inv);
+    store8(kbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c, kt, 1.0f);
+    store8(vbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c, av, inv);
   }
-  if (lane == 0) bias[bh * g.Vt + j] = lme - ew * inv;
+  if (lane == 0) bias[bh * g.Kc + j] = lme - ew * inv;
 }
 
 }  // namespace
@@ -231,13 +270,27 @@ void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipSt
   hipLaunchKernelGGL(vsa_anchor_kernel, dim3(g.heads, g.batch), dim3(1024), 0, st, g, qbar, anchor);
 }
 
+namespace {
+template <bool WEIGHTED>
+void launch_logmass(const VsaGeom& g, const void* k, const void* v, float* kbar, float* vbar,
+                    const float* anchor, float* bias, hipStream_t st) {
+  const dim3 block(256);
+  // prefix candidates (sink off only), then the video tiles
+  if (g.kc0 < g.P) {
+    dim3 grid((g.heads + 3) / 4, g.P - g.kc0, g.batch);
+    hipLaunchKernelGGL((vsa_logmass_kernel<WEIGHTED, true>), grid, block, 0, st, g, g.kc0, (const u32x4*)k,
+                       (const u32x4*)v, kbar, vbar, anchor, bias);
+  }
+  dim3 grid((g.heads + 3) / 4, g.Vt, g.batch);
+  hipLaunchKernelGGL((vsa_logmass_kernel<WEIGHTED, false>), grid, block, 0, st, g, g.P, (const u32x4*)k,
+                     (const u32x4*)v, kbar, vbar, anchor, bias);
+}
+}  // namespace
+
 void vsa_launch_logmass(const VsaGeom& g, const void* k, const void* v, float* kbar, float* vbar,
                         const float* anchor, float* bias, hipStream_t st) {
-  dim3 grid((g.heads + 3) / 4, g.Vt, g.batch);
   if (g.coarse == VSA_COARSE_WEIGHTED_LOGMASS)
-    hipLaunchKernelGGL(vsa_logmass_kernel<true>, grid, dim3(256), 0, st, g, (const u32x4*)k, (const u32x4*)v,
-                       kbar, vbar, anchor, bias);
+    launch_logmass<true>(g, k, v, kbar, vbar, anchor, bias, st);
   else
-    hipLaunchKernelGGL(vsa_logmass_kernel<false>, grid, dim3(256), 0, st, g, (const u32x4*)k, (const u32x4*)v,
-                       kbar, vbar, anchor, bias);
+    launch_logmass<false>(g, k, v, kbar, vbar, anchor, bias, st);
 }

@@ -7,15 +7,18 @@
 // a fixed share of key blocks; Sol-Attn keeps blocks above a per-head
 // threshold in standard deviations.  "Ref2VA VSA : noeud d'attention sparse
 // pour le Ref2VA H3", items 1-2: the conditioning tiles are never pruned; top-k
-// applies to video key tiles only.
+// applies to video key tiles only.  "BSAI FastH3 Native VSA (recipe)", "The
+// inputs that matter": with sink_conditioning off nothing is protected, and
+// every tile is a candidate.
 //
-// One wave per row.  The Vt logits of the row sit in registers as order-
-// preserving 32-bit keys (lane l, slot e holds video tile 64 e + l, so slot-
-// major order is index order).  TOPK: an MSB-first bitwise search finds the
-// k-th largest key T in 32 ballot rounds; every key > T is kept, and the keys
-// equal to T are kept lowest index first until k are kept.  TAU: keep
-// S > thr.  Kept tiles are compacted in ascending order with ballot + mbcnt
-// after the P prefix tile ids.  Integer output, no atomics: deterministic.
+// One wave per row.  The Kc candidate logits of the row (tiles kc0 .. kc0 +
+// Kc - 1) sit in registers as order-preserving 32-bit keys (lane l, slot e
+// holds candidate 64 e + l, so slot-major order is index order).  TOPK: an
+// MSB-first bitwise search finds the k-th largest key T in 32 ballot rounds;
+// every key > T is kept, and the keys equal to T are kept lowest index first
+// until k are kept.  TAU: keep S > thr.  Kept tiles are compacted in
+// ascending order with ballot + mbcnt after the npin protected prefix tile ids
+// (P, or none with sink off).  Integer output, no atomics: deterministic.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -42,16 +45,16 @@ __global__ __launch_bounds__(256) void vsa_select_kernel(VsaGeom g, const float*
   const int s = blockIdx.x * 4 + wave;
   if (s >= g.Qs) return;
   const size_t bh = (size_t)blockIdx.z * g.heads + blockIdx.y;
-  const float* S = scores + (bh * g.Qs + s) * g.Vt;
+  const float* S = scores + (bh * g.Qs + s) * g.Kc;
   int* L = lists + (bh * g.Qs + s) * g.cap;
 
   unsigned int key[NPL];  // padding slots hold 0, below every real key
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     const int j = e * 64 + lane;
-    key[e] = j < g.Vt ? order_key(S[j]) : 0u;
+    key[e] = j < g.Kc ? order_key(S[j]) : 0u;
   }
-  for (int t = lane; t < g.P; t += 64) L[t] = t;
+  for (int t = lane; t < g.npin; t += 64) L[t] = t;
 
   unsigned int T;
   int need_eq;  // keys equal to T still to keep (TOPK); unused for TAU
@@ -83,10 +86,10 @@ __global__ __launch_bounds__(256) void vsa_select_kernel(VsaGeom g, const float*
     eq_seen += __popcll(beq);
     const bool take = gt || eq_take;
     const unsigned long long bt = __ballot(take);
-    if (take) L[g.P + base + lanes_below(bt)] = g.P + e * 64 + lane;
+    if (take) L[g.npin + base + lanes_below(bt)] = g.kc0 + e * 64 + lane;
     base += __popcll(bt);
   }
-  if (lane == 0) counts[bh * g.Qs + s] = g.P + base;
+  if (lane == 0) counts[bh * g.Qs + s] = g.npin + base;
 }
 
 template <int NPL>
@@ -102,7 +105,7 @@ void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, 
                        int* counts, hipStream_t st) {
   if (g.Qs == 0) return;
   // slots per lane; exact up to 16, so no all-padding slot joins the 32 ballot rounds
-  const int npl = (g.Vt + 63) / 64;
+  const int npl = (g.Kc + 63) / 64;
   switch (npl) {
     case 1: launch_npl<1>(g, scores, thr, lists, counts, st); break;
     case 2: launch_npl<2>(g, scores, thr, lists, counts, st); break;

@@ -37,12 +37,7 @@ __device__ __forceinline__ int tile_valid(const VsaGeom& g, int t) {
 // Prefix tile: 64 consecutive tokens of its segment.  Video tile j = t - P:
 // (tt, th, tw) raster over the (T/4, H/4, W/4) grid, row r = (dt, dh, dw)
 // raster, token vstart + ((4tt+dt) H + 4th+dh) W + 4tw+dw.
-__device__ __forceinline__ int tile_token(const VsaGeom& g, int t, int r) {
-  if (t < g.P) {
-    const int s = prefix_seg(g, t);
-    const int off = (t - g.pre_tile0[s]) * VSA_TILE_TOKENS + r;
-    return off < g.pre_len[s] ? g.pre_start[s] + off : -1;
-  }
+__device__ __forceinline__ int video_token(const VsaGeom& g, int t, int r) {
   const int j = t - g.P;
   const int tw = j % g.tw_n;
   const int rest = j / g.tw_n;
@@ -50,6 +45,14 @@ __device__ __forceinline__ int tile_token(const VsaGeom& g, int t, int r) {
   const int tt = rest / g.th_n;
   const int dt = r >> 4, dh = (r >> 2) & 3, dw = r & 3;
   return g.vstart + ((4 * tt + dt) * g.H + 4 * th + dh) * g.W + 4 * tw + dw;
+}
+__device__ __forceinline__ int tile_token(const VsaGeom& g, int t, int r) {
+  if (t < g.P) {
+    const int s = prefix_seg(g, t);
+    const int off = (t - g.pre_tile0[s]) * VSA_TILE_TOKENS + r;
+    return off < g.pre_len[s] ? g.pre_start[s] + off : -1;
+  }
+  return video_token(g, t, r);
 }
 
 // Element offset of (batch b, token tok, head h, dim 0) in a [B, N, heads, 128] tensor.

@@ -216,7 +216,7 @@ extern "C" int vsa_read_stats(const vsa_plan* plan, const void* workspace, void*
   int64_t pairs = BH * G.n_dense * (int64_t)G.Tq, kept = 0;
   for (size_t i = 0; i < n; ++i) {
     pairs += cnt[i];
-    kept += cnt[i] - G.P;
+    kept += cnt[i] - G.npin;
   }
   out->executed_pairs = pairs;
   out->dense_pairs = BH * (int64_t)G.Tq * G.Tq;

@@ -7,7 +7,7 @@
 #include "vsa.h"
 
 #define VSA_MAX_PREFIX_SEGS 16
-#define VSA_MAX_VIDEO_TILES 4096
+#define VSA_MAX_VIDEO_TILES 4096  // also the most candidate key tiles (selector: 64 per lane)
 #define VSA_MAX_LIST 2048        // key tiles in one sparse row's list (staged in LDS by the fine kernel)
 #define VSA_HEAD_DIM 128
 #define VSA_TILE_TOKENS 64
@@ -24,6 +24,9 @@ struct VsaGeom {
   int32_t T, H, W;                         // video latent grid
   int32_t tw_n, th_n;                      // W/4, H/4
   int32_t P, Vt, Tq;
+  int32_t npin;                            // tiles listed in every sparse row: P, or 0 with sink off
+  int32_t kc0, Kc;                         // candidate key tiles [kc0, kc0 + Kc): the video tiles,
+                                           // or every tile with sink off
   int32_t N, heads, batch;
   int32_t n_dense;                         // dense query tiles per (batch, head): 0 or P
   int32_t Qs;                              // sparse query tiles per (batch, head): Tq - n_dense

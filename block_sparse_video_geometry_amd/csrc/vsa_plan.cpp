@@ -41,7 +41,7 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
 
   vsa_options o{VSA_SINK_EXACT_KV, VSA_SELECT_TOPK, VSA_COARSE_MEAN, 0.0f};
   if (opts != nullptr) o = *opts;
-  if (o.sink != VSA_SINK_EXACT_KV && o.sink != VSA_SINK_EXACT_KV_AND_ROWS)
+  if (o.sink != VSA_SINK_OFF && o.sink != VSA_SINK_EXACT_KV && o.sink != VSA_SINK_EXACT_KV_AND_ROWS)
     return VSA_ERR_UNSUPPORTED;
   if (o.select != VSA_SELECT_TOPK && o.select != VSA_SELECT_TAU) return VSA_ERR_UNSUPPORTED;
   if (o.coarse != VSA_COARSE_MEAN && o.coarse != VSA_COARSE_MEAN_LOGMASS &&
@@ -114,19 +114,28 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     delete p;
     return VSA_ERR_UNSUPPORTED;
   }
+  // candidates: the video tiles, or with sink off every tile ("BSAI FastH3 Native VSA
+  // (recipe)", "The inputs that matter": off protects no conditioning tile)
+  g.npin = (o.sink == VSA_SINK_OFF) ? 0 : g.P;
+  g.kc0 = g.npin;
+  g.Kc = g.Tq - g.kc0;
+  if (g.Kc > VSA_MAX_VIDEO_TILES) {
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
   g.N = (int32_t)N;
   g.heads = heads;
   g.batch = batch;
   g.n_dense = (o.sink == VSA_SINK_EXACT_KV_AND_ROWS) ? g.P : 0;
   g.Qs = g.Tq - g.n_dense;
-  // k = ceil(keep * Vt / 100), clamped to [1, Vt]
+  // k = ceil(keep * Kc / 100), clamped to [1, Kc]
   if (o.select == VSA_SELECT_TOPK) {
-    int k = (int)std::ceil((double)keep_percent * g.Vt / 100.0 - 1e-9);
-    g.k = std::max(1, std::min(g.Vt, k));
-    g.cap = g.P + g.k;
+    int k = (int)std::ceil((double)keep_percent * g.Kc / 100.0 - 1e-9);
+    g.k = std::max(1, std::min(g.Kc, k));
+    g.cap = g.npin + g.k;
   } else {
     g.k = 0;
-    g.cap = g.P + g.Vt;
+    g.cap = g.npin + g.Kc;
   }
   if (g.cap > VSA_MAX_LIST) {
     delete p;
@@ -150,11 +159,11 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     return at;
   };
   L.qbar = take(BH * g.Tq * VSA_HEAD_DIM * 4);
-  L.kbar = take(BH * g.Vt * VSA_HEAD_DIM * 4);
-  L.vbar = take(BH * g.Vt * VSA_HEAD_DIM * 4);
-  L.bias = take(BH * g.Vt * 4);
+  L.kbar = take(BH * g.Kc * VSA_HEAD_DIM * 4);
+  L.vbar = take(BH * g.Kc * VSA_HEAD_DIM * 4);
+  L.bias = take(BH * g.Kc * 4);
   L.anchor = take(BH * VSA_HEAD_DIM * 4);
-  L.scores = take(BH * (size_t)g.Qs * g.Vt * 4);
+  L.scores = take(BH * (size_t)g.Qs * g.Kc * 4);
   L.ocoarse = take(BH * (size_t)g.Qs * VSA_HEAD_DIM * 4);
   L.thr = take(BH * 4);
   L.lists = take(BH * (size_t)g.Qs * g.cap * 4);
@@ -191,6 +200,8 @@ extern "C" int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out) {
   out->list_capacity = g.cap;
   out->options = plan->opts;
   out->keep_percent = plan->keep;
+  out->first_candidate = g.kc0;
+  out->n_candidates = g.Kc;
   return VSA_OK;
 }
 

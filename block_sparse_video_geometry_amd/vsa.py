@@ -20,7 +20,7 @@ VSA_ERR_HIP = -4
 VSA_ERR_NO_MEMORY = -5
 
 VSA_SEG_TEXT, VSA_SEG_REF_IMAGE, VSA_SEG_REF_AUDIO, VSA_SEG_OTHER_PREFIX, VSA_SEG_VIDEO = range(5)
-VSA_SINK_EXACT_KV, VSA_SINK_EXACT_KV_AND_ROWS = 1, 2
+VSA_SINK_OFF, VSA_SINK_EXACT_KV, VSA_SINK_EXACT_KV_AND_ROWS = 0, 1, 2
 VSA_SELECT_TOPK, VSA_SELECT_TAU = 0, 1
 VSA_COARSE_MEAN, VSA_COARSE_MEAN_LOGMASS, VSA_COARSE_WEIGHTED_LOGMASS = 0, 1, 2
 
@@ -43,7 +43,8 @@ class vsa_plan_desc(C.Structure):
                 ("n_video_tiles", C.c_int32), ("n_tiles", C.c_int32), ("k", C.c_int32),
                 ("n_dense_rows", C.c_int32), ("n_sparse_rows", C.c_int32),
                 ("list_capacity", C.c_int32), ("options", vsa_options),
-                ("keep_percent", C.c_float)]
+                ("keep_percent", C.c_float), ("first_candidate", C.c_int32),
+                ("n_candidates", C.c_int32)]
 
 
 class vsa_stats(C.Structure):
@@ -260,15 +261,15 @@ def debug_tensor(plan: Plan, workspace, field: str):
     """View of one intermediate in the workspace (see vsa_debug in include/vsa.h)."""
     import torch
     d = plan.desc
-    B, H, Tq, Vt, Qs, cap = (d.batch, d.heads, d.n_tiles, d.n_video_tiles, d.n_sparse_rows,
+    B, H, Tq, Kc, Qs, cap = (d.batch, d.heads, d.n_tiles, d.n_candidates, d.n_sparse_rows,
                              d.list_capacity)
     spec = {
         "qbar": (torch.float32, (B, H, Tq, HEAD_DIM)),
-        "kbar": (torch.float32, (B, H, Vt, HEAD_DIM)),
-        "vbar": (torch.float32, (B, H, Vt, HEAD_DIM)),
-        "bias": (torch.float32, (B, H, Vt)),
+        "kbar": (torch.float32, (B, H, Kc, HEAD_DIM)),
+        "vbar": (torch.float32, (B, H, Kc, HEAD_DIM)),
+        "bias": (torch.float32, (B, H, Kc)),
         "anchor": (torch.float32, (B, H, HEAD_DIM)),
-        "scores": (torch.float32, (B, H, Qs, Vt)),
+        "scores": (torch.float32, (B, H, Qs, Kc)),
         "ocoarse": (torch.float32, (B, H, Qs, HEAD_DIM)),
         "thr": (torch.float32, (B, H)),
         "lists": (torch.int32, (B, H, Qs, cap)),

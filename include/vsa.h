@@ -61,10 +61,11 @@ typedef enum {
   VSA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad spans, negative sizes, aliasing */
   VSA_ERR_UNSUPPORTED = -2,      /* outside what the kernels implement: head_dim != 128,
                                     grid dims not multiples of 4, not exactly one video span,
-                                    keep outside (0, 100], > 4096 video tiles, > 65535
-                                    tiles in all, > 16 prefix
+                                    keep outside (0, 100], > 4096 video tiles or candidate
+                                    key tiles, > 65535 tiles in all, > 16 prefix
                                     segments, a sparse row list longer than 2048 tiles
-                                    (P + k, or P + Vt in TAU mode), N * heads * head_dim
+                                    (P + k, or P + Vt in TAU mode; k, or Tq, with sink
+                                    off), N * heads * head_dim
                                     >= 2^30 (one batch item's Q, K or V is addressed
                                     with 32-bit byte offsets), unknown mode, device
                                     not gfx950.  The caller
@@ -93,17 +94,25 @@ typedef struct {
 /* sink_conditioning ("BSAI FastH3 Native VSA (recipe)", "The inputs that
  * matter"): EXACT_KV keeps every prefix key tile in every query tile's list;
  * EXACT_KV_AND_ROWS also runs prefix query tiles dense (all key tiles, no
- * coarse term). */
-typedef enum { VSA_SINK_EXACT_KV = 1, VSA_SINK_EXACT_KV_AND_ROWS = 2 } vsa_sink;
+ * coarse term).  OFF protects nothing: the prefix tiles become candidate key
+ * tiles like the video tiles (coarse branch, bias and selection run over all
+ * Tq tiles, a partial prefix tile summarised over its valid tokens) and every
+ * query tile is a sparse row. */
+typedef enum {
+  VSA_SINK_OFF = 0,
+  VSA_SINK_EXACT_KV = 1,
+  VSA_SINK_EXACT_KV_AND_ROWS = 2
+} vsa_sink;
 
-/* Video key tile selection: TOPK keeps the k = ceil(keep * Vt / 100) largest
- * coarse logits of each sparse query tile (ties to the lowest video tile
- * index); TAU keeps every video tile whose logit exceeds mean + tau * std of
- * all the (sparse query tile, video key tile) logits of its (batch, head)
+/* Candidate key tile selection (the Kc candidates are the video tiles, or
+ * every tile with VSA_SINK_OFF): TOPK keeps the k = ceil(keep * Kc / 100)
+ * largest coarse logits of each sparse query tile (ties to the lowest tile
+ * index); TAU keeps every candidate whose logit exceeds mean + tau * std of
+ * all the (sparse query tile, candidate) logits of its (batch, head)
  * (Sol-Attn, "un nodo, tres backends"). */
 typedef enum { VSA_SELECT_TOPK = 0, VSA_SELECT_TAU = 1 } vsa_select;
 
-/* Coarse logits: MEAN is s * qbar . kbar; MEAN_LOGMASS adds the per video
+/* Coarse logits: MEAN is s * qbar . kbar; MEAN_LOGMASS adds the per candidate
  * tile bias b_j = log(mean_{t in j} exp(s q_a . (k_t - kbar_j))) with q_a the
  * mean video query of the (batch, head) ("Que cambia Spark-Attn",
  * Spark-Reweight).  WEIGHTED_LOGMASS (same item: weighted summaries in place of
@@ -133,12 +142,14 @@ typedef struct {
   int32_t n_prefix_tiles;  /* P */
   int32_t n_video_tiles;   /* Vt */
   int32_t n_tiles;         /* Tq = P + Vt */
-  int32_t k;               /* video tiles kept per sparse row (TOPK); 0 in TAU mode */
+  int32_t k;               /* candidate tiles kept per sparse row (TOPK); 0 in TAU mode */
   int32_t n_dense_rows;    /* query tiles per (batch, head) that run dense */
   int32_t n_sparse_rows;   /* query tiles per (batch, head) that select (Qs) */
   int32_t list_capacity;   /* entries reserved per sparse row in the list buffer */
   vsa_options options;
   float keep_percent;
+  int32_t first_candidate; /* candidate key tiles are [first_candidate, first_candidate + */
+  int32_t n_candidates;    /* n_candidates): P and Vt, or 0 and Tq with VSA_SINK_OFF */
 } vsa_plan_desc;
 
 /* Counters of one forward ("BSAI FastH3 Native VSA (recipe)", "Where it goes
@@ -148,7 +159,8 @@ typedef struct {
   int64_t dense_pairs;      /* pairs a dense run would execute: batch * heads * Tq * Tq */
   int64_t sparse_rows;      /* sparse query tiles, all (batch, head) */
   int64_t dense_rows;       /* dense query tiles, all (batch, head) */
-  int64_t kept_video_tiles; /* video key tiles kept over all sparse rows */
+  int64_t kept_video_tiles; /* candidate tiles kept over all sparse rows (video tiles
+                               unless VSA_SINK_OFF) */
   int32_t k;                /* as in vsa_plan_desc */
   int32_t reserved;
 } vsa_stats;
@@ -156,14 +168,15 @@ typedef struct {
 /* Byte offsets into the workspace of the intermediates of the last forward
  * that used it (all row-major, fp32 unless noted):
  *   qbar  [batch, heads, Tq, 128]   mean of the valid Q tokens of each tile
- *   kbar  [batch, heads, Vt, 128]   mean K of each video tile
- *   vbar  [batch, heads, Vt, 128]   mean V of each video tile
- *   bias  [batch, heads, Vt]        log-mass bias (zeros in MEAN mode)
- *   anchor[batch, heads, 128]       mean video query (LOGMASS mode only)
- *   scores[batch, heads, Qs, Vt]    coarse logits of the sparse rows
+ *   kbar  [batch, heads, Kc, 128]   K summary of each candidate tile (Kc = n_candidates)
+ *   vbar  [batch, heads, Kc, 128]   V summary of each candidate tile
+ *   bias  [batch, heads, Kc]        log-mass bias (zeros in MEAN mode)
+ *   anchor[batch, heads, 128]       mean video query (LOGMASS modes only)
+ *   scores[batch, heads, Qs, Kc]    coarse logits of the sparse rows
  *   ocoarse[batch, heads, Qs, 128]  coarse output of the sparse rows
  *   thr   [batch, heads]            TAU threshold (TAU mode only)
- *   lists [batch, heads, Qs, list_capacity] int32 tile ids (prefix ascending, then video ascending)
+ *   lists [batch, heads, Qs, list_capacity] int32 tile ids, ascending (the protected
+ *                                   prefix tiles, then the kept candidates)
  *   counts[batch, heads, Qs]        int32 valid entries of each list
  * Sparse row s of a (batch, head) is query tile s + n_dense_rows. */
 typedef struct {

@@ -66,6 +66,10 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, keep=0.0, select=1, tau=1.0), 0),                # keep unused in tau mode
     (dict(segs=GOOD, select=1, tau=float("inf")), -2),
     (dict(segs=GOOD, sink=3), -2),
+    (dict(segs=GOOD, sink=-1), -2),
+    (dict(segs=GOOD, sink=0), 0),                                     # sink_conditioning off
+    (dict(segs=[(0, 64, 0), (64, 4 * 256 * 256, 4)], T=4, H=256, W=256), 0),          # 4096 video tiles
+    (dict(segs=[(0, 64, 0), (64, 4 * 256 * 256, 4)], T=4, H=256, W=256, sink=0), -2),  # 4097 candidates
     (dict(segs=GOOD, select=2), -2),
     (dict(segs=GOOD, coarse=5), -2),
     (dict(segs=GOOD, coarse=2), 0),                                   # weighted summaries
@@ -95,17 +99,20 @@ def test_plan_shapes_match_oracle_geometry(name):
                             coarse=w.coarse, tau=w.tau)
     geom = O.map_geometry(w.segments(), *w.grid)
     sparse, dense = O.row_classes(geom, w.sink)
+    cand = O.key_candidates(geom, w.sink)
+    pinned = 0 if w.sink == O.SINK_OFF else geom.n_prefix
     d = p.desc
     assert d.n_prefix_tiles == geom.n_prefix
     assert d.n_video_tiles == geom.n_video
     assert d.n_tiles == geom.n_tiles
     assert d.n_dense_rows == len(dense) and d.n_sparse_rows == len(sparse)
     assert d.n_tokens == w.n_tokens
+    assert (d.first_candidate, d.n_candidates) == (cand[0], len(cand))
     if w.select == V.VSA_SELECT_TOPK:
-        assert d.k == O.keep_count(w.keep, geom.n_video)
-        assert d.list_capacity == geom.n_prefix + d.k
+        assert d.k == O.keep_count(w.keep, len(cand))
+        assert d.list_capacity == pinned + d.k
     else:
-        assert d.list_capacity == geom.n_tiles
+        assert d.list_capacity == pinned + len(cand)
 
 
 def test_workspace_layout():
@@ -114,7 +121,7 @@ def test_workspace_layout():
                             select=w.select, tau=w.tau)
     dbg = p.debug
     d = p.desc
-    B, H, Tq, Vt, Qs, cap = 1, d.heads, d.n_tiles, d.n_video_tiles, d.n_sparse_rows, d.list_capacity
+    B, H, Tq, Vt, Qs, cap = 1, d.heads, d.n_tiles, d.n_candidates, d.n_sparse_rows, d.list_capacity
     sizes = {"qbar": B * H * Tq * 512, "kbar": B * H * Vt * 512, "vbar": B * H * Vt * 512,
              "bias": B * H * Vt * 4, "anchor": B * H * 512, "scores": B * H * Qs * Vt * 4,
              "ocoarse": B * H * Qs * 512, "thr": B * H * 4, "lists": B * H * Qs * cap * 4,

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 import parity as PAR
 from oracle import vsa_oracle as O
 from workloads.synth import (WORKLOADS, Workload, make_inputs, scaled_down, SEG_TEXT,
-                             SEG_REF_IMAGE, SEG_REF_AUDIO, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS,
+                             SEG_REF_IMAGE, SEG_REF_AUDIO, SINK_OFF, SINK_EXACT_KV, SINK_EXACT_KV_AND_ROWS,
                              SELECT_TOPK, SELECT_TAU, COARSE_MEAN, COARSE_MEAN_LOGMASS,
                              COARSE_WEIGHTED_LOGMASS)
 
@@ -83,6 +83,17 @@ SMALL_CASES = [
              seed=82, recipe="scaled"),
     Workload("odd_video_grid_tau", 2, ((SEG_TEXT, 70),), (12, 20, 28), 0.0, SINK_EXACT_KV,
              SELECT_TAU, COARSE_MEAN_LOGMASS, 1.0, seed=83, recipe="offset"),
+    # sink_conditioning off: prefix tiles compete (168 candidates: three selector slots per
+    # lane, three 64-tile chunks of the coarse kernel)
+    scaled_down(WORKLOADS["full_sink_off"], heads=3, grid=FULL_SMALL_GRID, name="sink_off_small"),
+    Workload("sink_off_ragged", 3, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 64), (SEG_REF_AUDIO, 30)),
+             (8, 12, 16), 20.0, SINK_OFF, seed=85, recipe="scaled", video_first=True),
+    # partial prefix tiles of 1 and 30 tokens in the log-mass and weighted summaries
+    Workload("sink_off_logmass", 2, ((SEG_TEXT, 65), (SEG_REF_AUDIO, 30)), (8, 16, 16), 15.0,
+             SINK_OFF, SELECT_TOPK, COARSE_MEAN_LOGMASS, seed=86, recipe="offset"),
+    Workload("sink_off_weighted_tau", 2, ((SEG_TEXT, 65), (SEG_REF_AUDIO, 30)), (8, 16, 16), 0.0,
+             SINK_OFF, SELECT_TAU, COARSE_WEIGHTED_LOGMASS, 1.0, seed=87, recipe="offset"),
+    Workload("sink_off_keep_all", 2, ((SEG_TEXT, 40),), (4, 8, 12), 100.0, SINK_OFF, seed=88),
 ]
 
 
@@ -124,6 +135,20 @@ def test_deterministic_and_stats():
     assert 0 < st["executed_pairs"] < st["dense_pairs"]
 
 
+def test_stats_sink_off():
+    """sink off: every query tile keeps k = ceil(keep Tq / 100) tiles and nothing else."""
+    V = _lib()
+    w = scaled_down(WORKLOADS["full_sink_off"], heads=2, grid=FULL_SMALL_GRID, name="det_off")
+    x = make_inputs(w)
+    plan, ws, o, _ = run_gpu(w, x)
+    st = V.vsa_read_stats(plan, ws)
+    d = plan.desc
+    assert (d.first_candidate, d.n_candidates, d.n_dense_rows) == (0, d.n_tiles, 0)
+    assert d.k == int(np.ceil(w.keep * d.n_tiles / 100 - 1e-9))
+    assert st["executed_pairs"] == w.heads * d.n_tiles * d.k
+    assert st["kept_video_tiles"] == w.heads * d.n_tiles * d.k
+
+
 def test_abi_errors_on_device():
     V = _lib()
     w = WORKLOADS["tiny"]
@@ -150,7 +175,7 @@ def _inputs_for_seed(name):
 
 
 FULL_CASES = ["full", "full_smooth_20", "full_smooth_100", "full_tau_1.0", "full_tau_1.5",
-              "full_tau_2.0", "full_logmass", "full_weighted"]
+              "full_tau_2.0", "full_logmass", "full_weighted", "full_sink_off"]
 
 
 @pytest.mark.parametrize("name", FULL_CASES)
@@ -159,21 +184,22 @@ def test_parity_full_size_sampled(name):
     # workloads that share a seed share their inputs
     src = {"full_smooth_100": "full_smooth_20", "full_tau_1.5": "full_tau_1.0",
            "full_tau_2.0": "full_tau_1.0", "full_logmass": "full_tau_1.0",
-           "full_weighted": "full_tau_1.0"}.get(name, name)
+           "full_weighted": "full_tau_1.0", "full_sink_off": "full"}.get(name, name)
     x = _inputs_for_seed(src)
     plan, ws, o, _ = run_gpu(w, x)
     gpu = PAR.gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar",
                                                           "vbar", "bias", "ocoarse", "thr"))
     d = plan.desc
     P, Tq = d.n_prefix_tiles, d.n_tiles
+    pinned = 0 if w.sink == SINK_OFF else P
     # properties over every row
     cnt = gpu["counts"]
     if w.select == SELECT_TOPK:
-        assert np.all(cnt == P + d.k)
+        assert np.all(cnt == pinned + d.k)
     else:
-        assert np.all((cnt >= P) & (cnt <= Tq))
+        assert np.all((cnt >= pinned) & (cnt <= pinned + d.n_candidates))
     lists = gpu["lists"]
-    assert np.all(lists[..., :P] == np.arange(P))
+    assert np.all(lists[..., :pinned] == np.arange(pinned))
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     heads = [(0, 0), (0, int(rng.integers(1, w.heads)))]
     rows = sorted(set([0, P - 1, P, Tq - 1] + [int(r) for r in rng.integers(0, Tq, size=4)]))

@@ -109,6 +109,9 @@ WORKLOADS = {
     "full_weighted": Workload("full_weighted", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
                               SINK_EXACT_KV_AND_ROWS, SELECT_TOPK, COARSE_WEIGHTED_LOGMASS,
                               seed=1005, recipe="offset"),
+    # the full workload's inputs with sink_conditioning off: prefix tiles compete
+    "full_sink_off": Workload("full_sink_off", 32, _FULL_PREFIX, _FULL_GRID, 10.0, SINK_OFF,
+                              seed=1003, recipe="scaled"),
 }
 
 
