@@ -41,7 +41,9 @@ Method, in the pages' order:
   5. fine branch: exact attention over the listed tiles ([BSA-es] first
      paragraph; [SPK-es] "Que cambia Spark-Attn"); conditioning query rows
      run dense under exact_kv_and_rows ([FH3] "The inputs that matter",
-     sink_conditioning).
+     sink_conditioning); optionally plus the extra_tokens best-scoring
+     single key tokens outside the listed tiles ([BSA-es], schedule
+     paragraph: extra_tokens).
   6. gated combine O = O_fine + G * O_coarse with G the to_gate_compress
      output ([R2V-fr] item 3; [R2V-en] "Technical Architecture"; [BSA-es]
      VSA item).
@@ -79,6 +81,14 @@ the design notes):
     query tile is a sparse row, k = ceil(keep * Tq / 100 - 1e-9) clamped to
     [1, Tq], ties go to the lowest tile id, and the anchor stays the mean of
     the video queries;
+  * extra_tokens E ([BSA-es] only says the best-scoring tokens beyond the
+    selected blocks are added, to stay closer to dense): per sparse query
+    tile i, every valid key token t outside the tiles of i's list is scored
+    with the same pooled query as the coarse branch, z_t = s qbar_i . k_t (no
+    bias: the bias is a tile's, not a token's); the E largest, ties to the
+    lowest packed token index, join the key set of every query of tile i
+    (all of them if fewer than E remain).  Dense rows take none (they already
+    see every token).  The coarse branch and its output are unchanged;
   * weighted summaries (the page does not give the weights): the anchor's own
     attention over the tile, w_t = softmax_t(l_t); ktil_j = sum_t w_t k_t,
     vtil_j = sum_t w_t v_t; the bias keeps the same anchor identity,
@@ -334,16 +344,40 @@ def row_list(geom: Geometry, video_sel, sink: int = SINK_EXACT_KV) -> np.ndarray
 # --------------------------------------------------------------------------
 # 5. fine branch
 # --------------------------------------------------------------------------
+def extra_tokens_for_row(qbar_i: np.ndarray, K: np.ndarray, geom: Geometry, key_tiles,
+                         n_extra: int, scale: float) -> np.ndarray:
+    """The n_extra best-scoring key tokens outside the listed tiles of one sparse row.
+
+    [BSA-es], schedule paragraph: extra_tokens adds the top-scoring tokens
+    beyond the selected blocks.  z_t = s qbar_i . k_t over every valid token t
+    not in a listed tile; the largest z first, equal z to the lower token index.
+    Returns the chosen packed token indices in ascending order.
+    """
+    if n_extra <= 0:
+        return np.zeros(0, dtype=np.int64)
+    listed = set(int(t) for t in key_tiles)
+    elig = [geom.tiles[t] for t in range(geom.n_tiles) if t not in listed]
+    if not elig:
+        return np.zeros(0, dtype=np.int64)
+    toks = np.concatenate(elig)
+    z = scale * (K[toks] @ qbar_i)
+    order = sorted(range(len(toks)), key=lambda a: (-z[a], toks[a]))
+    return np.sort(toks[order[:n_extra]])
+
+
 def fine_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry,
-             qtile: int, key_tiles, scale: float) -> np.ndarray:
+             qtile: int, key_tiles, scale: float, extra=None) -> np.ndarray:
     """Exact softmax attention of the valid queries of one query tile over the
-    valid tokens of the listed key tiles.  Returns [n_valid, D].  An empty
-    list (possible only with no prefix and nothing above the tau threshold)
-    attends to nothing and gives zeros."""
+    valid tokens of the listed key tiles, plus the extra tokens if given.
+    Returns [n_valid, D].  An empty key set (possible only with no prefix
+    and nothing above the tau threshold) attends to nothing and gives zeros."""
     rows = geom.tiles[qtile]
-    if len(key_tiles) == 0:
+    parts = [geom.tiles[t] for t in key_tiles]
+    if extra is not None and len(extra):
+        parts.append(np.asarray(extra, dtype=np.int64))
+    if not parts:
         return np.zeros((len(rows), Q.shape[1]))
-    keys = np.concatenate([geom.tiles[t] for t in key_tiles])
+    keys = np.concatenate(parts)
     z = scale * (Q[rows] @ K[keys].T)
     z = z - z.max(axis=1, keepdims=True)
     e = np.exp(z)
@@ -355,14 +389,16 @@ def fine_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry,
 # --------------------------------------------------------------------------
 def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
                  select: int, coarse: int, tau: float, rows=None,
-                 list_override=None, want_intermediates=False):
+                 list_override=None, want_intermediates=False, extra_tokens: int = 0,
+                 extra_override=None):
     """Run the method for one (batch, head).
 
     Q, K, V, G: float64 [N, D] (G may be None).  rows: query tile ids to
     produce (None = all).  list_override: {query tile id: tile id array} to
     replace the selection of some sparse rows (used when several selections
-    are correct).  Returns (O [N, D] with NaN outside the produced rows,
-    intermediates dict or None).
+    are correct); extra_override does the same for the extra tokens.
+    Returns (O [N, D] with NaN outside the produced rows, intermediates dict
+    or None).
     """
     scale = softmax_scale(Q.shape[1])
     sparse, dense = row_classes(geom, sink)
@@ -391,7 +427,7 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
     k = keep_count(keep_percent, len(cand)) if select == SELECT_TOPK else None
 
     O = np.full_like(Q, np.nan)
-    lists = {}
+    lists, extras = {}, {}
     dense_set = set(dense)
     all_tiles = np.arange(geom.n_tiles, dtype=np.int64)
     for i in sorted(rows_set):
@@ -408,20 +444,27 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
             if list_override is not None and i in list_override:
                 lst = np.asarray(list_override[i], dtype=np.int64)
         lists[i] = lst
-        of = fine_row(Q, K, V, geom, i, lst, scale)
+        ex = None
+        if i not in dense_set and extra_tokens > 0:
+            ex = extra_tokens_for_row(Qbar[need_idx[i]], K, geom, lst, extra_tokens, scale)
+            if extra_override is not None and i in extra_override:
+                ex = np.asarray(extra_override[i], dtype=np.int64)
+            extras[i] = ex
+        of = fine_row(Q, K, V, geom, i, lst, scale, ex)
         if i not in dense_set and G is not None:
             of = of + G[toks] * Oc[need_idx[i]][None, :]
         O[toks] = of
     inter = None
     if want_intermediates:
         inter = dict(Kbar=Kbar, Vbar=Vbar, bias=bias, anchor=q_a, sparse_rows=need, cand=cand,
-                     Qbar=Qbar, S=S, Oc=Oc, thr=thr, k=k, lists=lists)
+                     Qbar=Qbar, S=S, Oc=Oc, thr=thr, k=k, lists=lists, extras=extras)
     return O, inter
 
 
 def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
             select: int = SELECT_TOPK, coarse: int = COARSE_MEAN, tau: float = 0.0,
-            heads=None, rows=None, list_override=None, want_intermediates=False):
+            heads=None, rows=None, list_override=None, want_intermediates=False,
+            extra_tokens: int = 0):
     """Oracle forward on bf16 bit arrays q, k, v, g ([B, N, H, D] uint16; g
     may be None).  Returns (O float64 [B, N, H, D] (NaN where not produced),
     {(b, h): intermediates}).  heads: iterable of (b, h) to run (None = all).
@@ -446,6 +489,7 @@ def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
         lo = None if list_override is None else list_override.get((b, h))
         O[b, :, h, :], it = forward_head(Qh, Kh, Vh, Gh, geom, keep_percent, sink, select,
                                          coarse, tau, rows=rows, list_override=lo,
-                                         want_intermediates=want_intermediates)
+                                         want_intermediates=want_intermediates,
+                                         extra_tokens=extra_tokens)
         inter[(b, h)] = it
     return O, inter

@@ -602,6 +602,101 @@ def check_sink_off_no_prefix():
     assert np.array_equal(o_off, o_kv)
 
 
+# ---------------------------------------------------------------- P-11 extra tokens
+# [BSA-es], schedule paragraph: extra_tokens adds the best-scoring single tokens
+# beyond the selected blocks.  Reading: scored with the row's pooled query, like the
+# coarse branch, over the valid tokens outside the listed tiles; ties to the lower
+# token index.
+EXTRA_W = Workload("extra", 2, ((SEG_TEXT, 100), (SEG_REF_AUDIO, 30)), (4, 8, 12), 25.0,
+                   SINK_EXACT_KV, seed=91, recipe="scaled")
+
+
+def check_extra_dense():
+    """With more extra tokens than there are tokens, every sparse row sees every token:
+    no gate gives plain dense attention, for top-k and for tau."""
+    w = EXTRA_W
+    x = make_inputs(w, with_gate=False)
+    for sel, tau in ((SELECT_TOPK, 0.0), (SELECT_TAU, 1.5)):
+        out, _ = O.forward(x, w.segments(), w.grid, w.keep, w.sink, select=sel, tau=tau,
+                           extra_tokens=10 ** 6)
+        for h in range(w.heads):
+            ref = torch_sdpa(as_f64(x["q"][0, :, h]), as_f64(x["k"][0, :, h]), as_f64(x["v"][0, :, h]))
+            assert np.abs(out[0, :, h] - ref).max() < 1e-12, (sel, h)
+
+
+def _check_extra_choice(w: Workload, x, n_extra: int, sink: int):
+    tiles = _all_tiles(w)
+    out, inter = O.forward(x, w.segments(), w.grid, w.keep, sink, want_intermediates=True,
+                           extra_tokens=n_extra)
+    sparse, dense = O.row_classes(geom_of(w), sink)
+    ties = 0
+    for h in range(w.heads):
+        Q, K, V, G = (as_f64(x[n][0, :, h]) for n in "qkvg")
+        qall = _pool_all(Q, w)
+        it = inter[(0, h)]
+        assert set(it["extras"]) == set(sparse)
+        for i in sparse:
+            listed = np.concatenate([tiles[t] for t in it["lists"][i]]) if len(it["lists"][i]) else \
+                np.zeros(0, np.int64)
+            elig = np.setdiff1d(np.arange(w.n_tokens), listed)
+            X = np.asarray(it["extras"][i])
+            assert len(X) == min(n_extra, len(elig)), (h, i, len(X))
+            assert np.all(np.diff(X) > 0) and np.isin(X, elig).all(), (h, i)
+            z = K[elig] @ qall[i] / math.sqrt(D)
+            chosen = np.isin(elig, X)
+            if chosen.any() and (~chosen).any():
+                zmin, zmax = z[chosen].min(), z[~chosen].max()
+                assert zmin >= zmax, (h, i, zmin, zmax)
+                if zmin == zmax:  # a tie at the boundary goes to the lower token
+                    assert elig[chosen][z[chosen] == zmin].max() < elig[~chosen][z[~chosen] == zmax].min()
+                    ties += 1
+            keys = np.concatenate([listed, X]).astype(np.int64)
+            ref = torch_sdpa(Q[tiles[i]], K[keys], V[keys])
+            got = out[0, tiles[i], h] - G[tiles[i]] * it["Oc"][it["sparse_rows"].index(i)][None, :]
+            assert np.abs(got - ref).max() < 1e-12, (h, i)
+        for i in dense:
+            assert i not in it["extras"]
+    return ties
+
+
+def check_extra_choice():
+    """The chosen extra tokens are the best-scoring eligible ones (independent pooling,
+    a matmul and comparisons, not a sort), none in a listed tile, and the output is
+    torch's sdpa over the listed tokens plus them; dense rows take none."""
+    w = EXTRA_W
+    x = make_inputs(w, with_gate=True)
+    _check_extra_choice(w, x, 20, SINK_EXACT_KV)
+    _check_extra_choice(w, x, 7, SINK_OFF)
+    _check_extra_choice(w, x, 64, SINK_EXACT_KV_AND_ROWS)
+
+
+def check_extra_ties():
+    """One token of every video tile holds the same key, aligned with the mean query so it
+    out-scores every other token: its copies outside the listed tiles tie for every row,
+    and the lower token indices must win."""
+    w = Workload("extra_tie", 1, EXTRA_W.prefix, EXTRA_W.grid, EXTRA_W.keep, SINK_EXACT_KV,
+                 seed=92, recipe="offset")
+    x = make_inputs(w)
+    geom = geom_of(w)
+    mu = as_f64(x["q"][0, :, 0]).mean(axis=0)
+    key = f32_to_bf16_bits((3.0 * math.sqrt(D) * mu / np.linalg.norm(mu)).astype(np.float32))
+    k = x["k"].copy()
+    for t in range(geom.n_prefix, geom.n_tiles):
+        k[0, geom.tiles[t][5], 0] = key
+    x = dict(x, k=k)
+    ties = _check_extra_choice(w, x, 3, SINK_EXACT_KV)
+    assert ties == len(geom.tiles), f"expected a boundary tie on every row, got {ties}"
+
+
+def check_extra_zero():
+    """extra_tokens = 0 is the plain method."""
+    w = EXTRA_W
+    x = make_inputs(w)
+    a, _ = O.forward(x, w.segments(), w.grid, w.keep, w.sink, extra_tokens=0)
+    b, _ = O.forward(x, w.segments(), w.grid, w.keep, w.sink)
+    assert np.array_equal(a, b)
+
+
 ALL_CHECKS = [
     ("geometry", lambda: (check_geometry(SMALL), check_geometry(SMALL_VIDEO_FIRST),
                           check_geometry(GEOM_3D))),
@@ -628,4 +723,8 @@ ALL_CHECKS = [
     ("sink_off_tau", lambda: (check_sink_off_tau(SINK_OFF_W, 1.0), check_sink_off_tau(SINK_OFF_PARTIAL, 0.5))),
     ("sink_off_logmass", check_sink_off_logmass),
     ("sink_off_no_prefix", check_sink_off_no_prefix),
+    ("extra_dense", check_extra_dense),
+    ("extra_choice", check_extra_choice),
+    ("extra_ties", check_extra_ties),
+    ("extra_zero", check_extra_zero),
 ]

@@ -15,7 +15,7 @@ from oracle import vsa_oracle as O
 _orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
                                       "logmass_bias", "coarse_branch", "tau_threshold",
                                       "keep_count", "pool_tiles", "fine_row", "weighted_summaries",
-                                      "key_candidates")}
+                                      "key_candidates", "extra_tokens_for_row")}
 
 
 def _geom_swapped_axes(segments, T, H, W):
@@ -105,8 +105,24 @@ def _weighted_bias_vs_mean(Q, K, V, geom, scale, cand=None):
     return kt, vt, b2, qa
 
 
-def _fine_k_for_v(Q, K, V, geom, qtile, key_tiles, scale):
-    return _orig["fine_row"](Q, K, K, geom, qtile, key_tiles, scale)
+def _fine_k_for_v(Q, K, V, geom, qtile, key_tiles, scale, extra=None):
+    return _orig["fine_row"](Q, K, K, geom, qtile, key_tiles, scale, extra)
+
+
+def _extra_ignores_list(qbar_i, K, geom, key_tiles, n_extra, scale):
+    return _orig["extra_tokens_for_row"](qbar_i, K, geom, [], n_extra, scale)
+
+
+def _extra_lowest(qbar_i, K, geom, key_tiles, n_extra, scale):
+    return _orig["extra_tokens_for_row"](-qbar_i, K, geom, key_tiles, n_extra, scale)
+
+
+def _extra_ties_high(qbar_i, K, geom, key_tiles, n_extra, scale):
+    listed = set(int(t) for t in key_tiles)
+    toks = np.concatenate([geom.tiles[t] for t in range(geom.n_tiles) if t not in listed])
+    z = scale * (K[toks] @ qbar_i)
+    order = sorted(range(len(toks)), key=lambda a: (-z[a], -toks[a]))
+    return np.sort(toks[order[:n_extra]])
 
 
 MUTATIONS = [
@@ -131,6 +147,10 @@ MUTATIONS = [
     ("off_video_only_tau", "key_candidates", _off_video_only, "sink_off_tau"),
     ("off_prefix_pinned", "row_list", _row_list_always_pinned, "sink_off_selection"),
     ("bias_mean_over_64", "logmass_bias", _bias_mean_over_64, "sink_off_logmass"),
+    ("extra_ignores_list", "extra_tokens_for_row", _extra_ignores_list, "extra_dense"),
+    ("extra_ignores_list_choice", "extra_tokens_for_row", _extra_ignores_list, "extra_choice"),
+    ("extra_lowest", "extra_tokens_for_row", _extra_lowest, "extra_choice"),
+    ("extra_ties_high", "extra_tokens_for_row", _extra_ties_high, "extra_ties"),
 ]
 
 
