@@ -361,7 +361,7 @@ def extra_tokens_for_row(qbar_i: np.ndarray, K: np.ndarray, geom: Geometry, key_
         return np.zeros(0, dtype=np.int64)
     toks = np.concatenate(elig)
     z = scale * (K[toks] @ qbar_i)
-    order = sorted(range(len(toks)), key=lambda a: (-z[a], toks[a]))
+    order = np.lexsort((toks, -z))   # by -z, then by token
     return np.sort(toks[order[:n_extra]])
 
 
