@@ -133,7 +133,7 @@ def main():
     o = torch.empty_like(q)
     plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128,
                                w.keep if w.keep > 0 else 100.0, sink=w.sink, select=w.select,
-                               coarse=w.coarse, tau=w.tau)
+                               coarse=w.coarse, tau=w.tau, extra_tokens=w.extra)
     ws = V.alloc_workspace(plan)
     timer = V.Timer()
     stream = torch.cuda.current_stream()

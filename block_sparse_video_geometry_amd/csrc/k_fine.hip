@@ -41,6 +41,13 @@
 // Rows are ordered head-major, dense rows first, and mapped XCD-aware: the
 // hardware deals workgroup i to XCD i % 8, so XCD x receives a contiguous
 // range of heads and its L2 sees few heads' K/V at a time.
+//
+// Extra tokens ("ComfyUI Agrega Nodo Central de Atencion Dispersa...", schedule
+// paragraph): a sparse row's extra key tokens, staged by the extra-token kernels
+// as 64 consecutive rows (padding zero) with the token stride of K and V, run as
+// the row's first tile.  Only the loads of that first tile (K and V rows 0-31 in
+// the prologue, V rows 32-63 in the first iteration) use the staging buffers'
+// resources; the rest of the pipeline is unchanged.
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -126,7 +133,8 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     VsaGeom g, const char* __restrict__ kptr, const char* __restrict__ vptr,
     const u32x4* __restrict__ q, const unsigned short* __restrict__ gate,
     const float* __restrict__ ocoarse, const int* __restrict__ lists,
-    const int* __restrict__ counts, unsigned short* __restrict__ o, int per_xcd) {
+    const int* __restrict__ counts, unsigned short* __restrict__ o, int per_xcd,
+    const char* __restrict__ kxptr, const char* __restrict__ vxptr, const int* __restrict__ xcnt) {
   // a K tile and a V tile; separate arrays so LDS reads of one are never taken as aliasing
   // DMA writes in flight to the other.  About 33 KB in all, so four workgroups share a CU.
   __shared__ __attribute__((aligned(16))) char klds[TILE_BYTES];
@@ -195,12 +203,24 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   for (int m = 0; m < 4; ++m) koff[m] = gi * rowbytes + ((pos ^ (gi | (m << 2))) << 4);
 #pragma unroll
   for (int m = 0; m < 2; ++m) voff[m] = gi * rowbytes + ((pos ^ ((2 * gi + 8 * m) & 15)) << 4);
+  // a sparse row's staged extra tokens (nx of them, none when the option is off) run first
+  int nx = 0;
+  if (!dense && g.extra > 0) nx = __builtin_amdgcn_readfirstlane(xcnt[(size_t)bh * g.Qs + srow]);
+  const int hx = nx > 0 ? 1 : 0;
   const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
   const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(kptr + bh_off), 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(vptr + bh_off), 0, nrec, 0x00020000);
+  // the first tile's resources: the staging buffers ([batch, Qs, 64, heads, 128]) when the
+  // row has extra tokens
+  const long long bhx_off = ((long long)b * g.Qs * VSA_MAX_EXTRA * g.heads + h) * (VSA_HEAD_DIM * 2);
+  const int nrec_x = (int)((unsigned)(g.Qs * VSA_MAX_EXTRA - 1) * rowbytes + VSA_HEAD_DIM * 2);
+  const __amdgpu_buffer_rsrc_t krs0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(hx ? kxptr + bhx_off : kptr + bh_off), 0, hx ? nrec_x : nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(hx ? vxptr + bhx_off : vptr + bh_off), 0, hx ? nrec_x : nrec, 0x00020000);
 
   lds_char* kbuf = (lds_char*)klds;
   lds_char* vbuf = (lds_char*)vlds;
@@ -221,12 +241,12 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   // Tile descriptors, 64 at a time: lane l describes tile 64 batch + l of the list.
   // off = byte offset of the tile's first token row in the (b, h) plane;
   // flags = video | nvalid << 1.
-  const int my_n = nlist;
+  const int my_n = nlist + hx;
   unsigned d_off = 0, d_flags = 0;
   auto describe = [&](int batch) {
     const int j = batch * 64 + lane;
     int t = 0;
-    if (j < my_n) t = dense ? j : lst_lds[j];
+    if (j < my_n && j >= hx) t = dense ? j : lst_lds[j - hx];
     int tok0, video, nvalid;
     if (t >= g.P) {
       const int jv = t - g.P;
@@ -251,6 +271,10 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     }
     d_off = (unsigned)tok0 * rowbytes;
     d_flags = (unsigned)video | ((unsigned)nvalid << 1);
+    if (j < hx) {  // the staged extra tokens: nx consecutive rows of the row's staging tile
+      d_off = (unsigned)srow * VSA_MAX_EXTRA * rowbytes;
+      d_flags = (unsigned)nx << 1;
+    }
   };
   // Row group n (key rows 4n .. 4n+3) of a tile starts at off + (n >> 2) * stp + (n & 3) * stl:
   // a video tile steps dt and dh, a prefix tile 16 and 4 tokens.
@@ -258,12 +282,14 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     stp = (flags & 1) ? plane : 16 * rowbytes;
     stl = (flags & 1) ? line : 4 * rowbytes;
   };
-  auto kdma = [&](int n, unsigned off, unsigned stp, unsigned stl) {
-    bdma16(krs, koff[(n >> 1) & 3], off + (n >> 2) * stp + (n & 3) * stl, kbuf_u + 1024 * n);
+  auto kdma_r = [&](__amdgpu_buffer_rsrc_t rs, int n, unsigned off, unsigned stp, unsigned stl) {
+    bdma16(rs, koff[(n >> 1) & 3], off + (n >> 2) * stp + (n & 3) * stl, kbuf_u + 1024 * n);
   };
-  auto vdma = [&](int n, unsigned off, unsigned stp, unsigned stl) {
-    bdma16(vrs, voff[(n >> 1) & 1], off + (n >> 2) * stp + (n & 3) * stl, vbuf_u + 1024 * n);
+  auto vdma_r = [&](__amdgpu_buffer_rsrc_t rs, int n, unsigned off, unsigned stp, unsigned stl) {
+    bdma16(rs, voff[(n >> 1) & 1], off + (n >> 2) * stp + (n & 3) * stl, vbuf_u + 1024 * n);
   };
+  auto kdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { kdma_r(krs, n, off, stp, stl); };
+  auto vdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { vdma_r(vrs, n, off, stp, stl); };
 
   f32x4 oacc[8][4];
 #pragma unroll
@@ -334,7 +360,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     unsigned stp, stl;
     steps(c_flags, stp, stl);
 #pragma unroll
-    for (int n = 0; n < 16; ++n) kdma(n, c_off, stp, stl);
+    for (int n = 0; n < 16; ++n) kdma_r(krs0, n, c_off, stp, stl);
   }
   // Q, the epilogue's copies and K(0) landed.  A wait the compiler sees, on every path to
   // the loop, so it does not wait (whole queue) for the Q loads again inside the loop.
@@ -376,7 +402,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 #pragma unroll
     for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) vdma(n, c_off, stp, stl);
+    for (int n = 0; n < 8; ++n) vdma_r(vrs0, n, c_off, stp, stl);
     if ((int)(c_flags >> 1) < VSA_TILE_TOKENS) mask(scur, (int)(c_flags >> 1));
     // the first tile sets the running max
 #pragma unroll
@@ -390,6 +416,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     }
   }
 
+  __amdgpu_buffer_rsrc_t vrs_c = vrs0;  // V(j)'s resource: the first tile's, then the plain one
   for (int j = 0; j < my_n; ++j) {
     unsigned nn_off = NO_TILE, nn_flags = 0;
     if (j + 2 < my_n) {
@@ -454,7 +481,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
         if (s < 8)
-          vdma(8 + s, c_off, c_stp, c_stl);  // V(j) rows 32-63
+          vdma_r(vrs_c, 8 + s, c_off, c_stp, c_stl);  // V(j) rows 32-63
         else
           kdma(s - 8, nn_off, nn_stp, nn_stl);  // K(j+2) rows 0-31 (read by steps 0-7)
         __builtin_amdgcn_sched_barrier(0);
@@ -563,6 +590,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     c_flags = n_flags;
     n_off = nn_off;
     n_flags = nn_flags;
+    vrs_c = vrs;
     if (j + 1 < my_n && (int)(c_flags >> 1) < VSA_TILE_TOKENS) mask(scur, (int)(c_flags >> 1));
   }
   // the loads issued past the end of the list (out of range, writing zeros) must land
@@ -647,10 +675,10 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
                      const float* ocoarse, const int* lists, const int* counts, void* o,
-                     hipStream_t st) {
+                     const void* kx, const void* vx, const int* xcnt, hipStream_t st) {
   const int total = g.batch * g.heads * g.Tq;
   const int per_xcd = (total + 7) / 8;
   hipLaunchKernelGGL(vsa_fine_kernel, dim3(8 * per_xcd), dim3(64), (size_t)g.cap * sizeof(int), st, g, (const char*)k,
                      (const char*)v, (const u32x4*)q, (const unsigned short*)gate, ocoarse, lists,
-                     counts, (unsigned short*)o, per_xcd);
+                     counts, (unsigned short*)o, per_xcd, (const char*)kx, (const char*)vx, xcnt);
 }

@@ -128,6 +128,10 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   int* lists = reinterpret_cast<int*>(ws + L.lists);
   int* counts = reinterpret_cast<int*>(ws + L.counts);
   double* statp = reinterpret_cast<double*>(ws + L.statp);
+  int* xtok = reinterpret_cast<int*>(ws + L.xtok);
+  int* xcnt = reinterpret_cast<int*>(ws + L.xcnt);
+  void* kx = ws + L.kx;
+  void* vx = ws + L.vx;
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   int rc = VSA_OK;
@@ -147,7 +151,8 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, st));
   if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
   VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
-  VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, st));
+  if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, st));
+  VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, kx, vx, xcnt, st));
 #undef VSA_STEP
   return VSA_OK;
 }
@@ -203,20 +208,27 @@ extern "C" int vsa_read_stats(const vsa_plan* plan, const void* workspace, void*
   if (plan == nullptr || workspace == nullptr || out == nullptr) return VSA_ERR_INVALID_ARGUMENT;
   const VsaGeom& G = plan->g;
   const size_t n = (size_t)G.batch * G.heads * G.Qs;
-  std::vector<int> cnt(n);
+  std::vector<int> cnt(n), xc(G.extra > 0 ? n : 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (n > 0) {
     const char* ws = static_cast<const char*>(workspace);
     if (hipMemcpyAsync(cnt.data(), ws + plan->ws.counts, n * sizeof(int), hipMemcpyDeviceToHost,
                        st) != hipSuccess)
       return VSA_ERR_HIP;
+    if (G.extra > 0 && hipMemcpyAsync(xc.data(), ws + plan->ws.xcnt, n * sizeof(int), hipMemcpyDeviceToHost,
+                                      st) != hipSuccess)
+      return VSA_ERR_HIP;
   }
   if (hipStreamSynchronize(st) != hipSuccess) return VSA_ERR_HIP;
   const int64_t BH = (int64_t)G.batch * G.heads;
-  int64_t pairs = BH * G.n_dense * (int64_t)G.Tq, kept = 0;
+  int64_t pairs = BH * G.n_dense * (int64_t)G.Tq, kept = 0, extra = 0;
   for (size_t i = 0; i < n; ++i) {
     pairs += cnt[i];
     kept += cnt[i] - G.npin;
+  }
+  for (size_t i = 0; i < xc.size(); ++i) {
+    pairs += xc[i] > 0 ? 1 : 0;  // the staged extra-token tile
+    extra += xc[i];
   }
   out->executed_pairs = pairs;
   out->dense_pairs = BH * (int64_t)G.Tq * G.Tq;
@@ -225,6 +237,7 @@ extern "C" int vsa_read_stats(const vsa_plan* plan, const void* workspace, void*
   out->kept_video_tiles = kept;
   out->k = G.k;
   out->reserved = 0;
+  out->extra_tokens = extra;
   return VSA_OK;
 }
 

@@ -12,6 +12,7 @@
 #define VSA_HEAD_DIM 128
 #define VSA_TILE_TOKENS 64
 #define VSA_COARSE_ROWS 64   // sparse rows per workgroup of the coarse kernel
+#define VSA_MAX_EXTRA 64     // extra tokens per sparse row (one staged tile)
 
 // Geometry and options of one plan, passed to every kernel by value.  Tile ids:
 // prefix tiles [0, P) in packed order, video tiles [P, P + Vt) raster (tt, th, tw).
@@ -32,6 +33,7 @@ struct VsaGeom {
   int32_t Qs;                              // sparse query tiles per (batch, head): Tq - n_dense
   int32_t cap;                             // list capacity per sparse row
   int32_t k;                               // TOPK keep count
+  int32_t extra;                           // extra tokens per sparse row (0: off)
   int32_t sink, select, coarse;
   float tau;
   float scale;                             // softmax scale 1/sqrt(128)
@@ -40,6 +42,7 @@ struct VsaGeom {
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
+  size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
   size_t total;
 };
 

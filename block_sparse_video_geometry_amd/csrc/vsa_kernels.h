@@ -31,7 +31,13 @@ void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream
 void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, int* lists,
                        int* counts, hipStream_t st);
 
-// Block-sparse fine attention + gated combine, output in packed order.
+// Extra tokens per sparse row (best pooled-query scores outside the listed tiles): ids
+// ascending and counts, and their K / V rows staged [batch, Qs, 64, heads, 128].
+void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
+                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, hipStream_t st);
+
+// Block-sparse fine attention + gated combine, output in packed order; a sparse row's
+// staged extra tokens (kx, vx, xcnt; unused when the option is off) run as its first tile.
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
                      const float* ocoarse, const int* lists, const int* counts, void* o,
-                     hipStream_t st);
+                     const void* kx, const void* vx, const int* xcnt, hipStream_t st);

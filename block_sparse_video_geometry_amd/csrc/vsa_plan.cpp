@@ -50,6 +50,8 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   if (o.select == VSA_SELECT_TOPK && !(keep_percent > 0.0f && keep_percent <= 100.0f))
     return VSA_ERR_UNSUPPORTED;
   if (o.select == VSA_SELECT_TAU && !std::isfinite(o.tau)) return VSA_ERR_UNSUPPORTED;
+  if (o.extra_tokens < 0) return VSA_ERR_INVALID_ARGUMENT;
+  if (o.extra_tokens > VSA_MAX_EXTRA) return VSA_ERR_UNSUPPORTED;
 
   // spans: sort by start, must partition [0, N)
   std::vector<Seg> s;
@@ -141,6 +143,12 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     delete p;
     return VSA_ERR_UNSUPPORTED;
   }
+  g.extra = o.extra_tokens;
+  // the fine kernel addresses a (b, h) plane of the extra-token staging with 32-bit offsets
+  if (g.extra > 0 && (int64_t)g.Qs * VSA_MAX_EXTRA * heads * VSA_HEAD_DIM * 2 >= ((int64_t)1 << 31)) {
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
   g.sink = o.sink;
   g.select = o.select;
   g.coarse = o.coarse;
@@ -169,6 +177,11 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   L.lists = take(BH * (size_t)g.Qs * g.cap * 4);
   L.counts = take(BH * (size_t)g.Qs * 4);
   L.statp = take(BH * (size_t)g.coarse_blocks * 2 * 8);
+  const size_t xrows = g.extra > 0 ? (size_t)batch * g.Qs * VSA_MAX_EXTRA : 0;
+  L.xtok = take(g.extra > 0 ? BH * (size_t)g.Qs * VSA_MAX_EXTRA * 4 : 0);
+  L.xcnt = take(g.extra > 0 ? BH * (size_t)g.Qs * 4 : 0);
+  L.kx = take(xrows * heads * VSA_HEAD_DIM * 2);
+  L.vx = take(xrows * heads * VSA_HEAD_DIM * 2);
   L.total = off;
 
   p->opts = o;
@@ -218,6 +231,8 @@ extern "C" int vsa_debug_views(const vsa_plan* plan, vsa_debug* out) {
   out->thr = L.thr;
   out->lists = L.lists;
   out->counts = L.counts;
+  out->xtok = L.xtok;
+  out->xcnt = L.xcnt;
   out->total_bytes = L.total;
   return VSA_OK;
 }

@@ -62,10 +62,11 @@ class LayerDriver:
     def __init__(self, segments, batch: int, video_T: int, video_H: int, video_W: int, heads: int,
                  keep_percent: float, sink: int = _v.VSA_SINK_EXACT_KV, select: int = _v.VSA_SELECT_TOPK,
                  coarse: int = _v.VSA_COARSE_MEAN, tau: float = 0.0, schedule: Schedule = Schedule(),
-                 device: str = "cuda"):
+                 device: str = "cuda", extra_tokens: int = 0):
         self.schedule = schedule
         self.sparse_plan = _v.vsa_plan_geometry(segments, batch, video_T, video_H, video_W, heads, _v.HEAD_DIM,
-                                                keep_percent, sink=sink, select=select, coarse=coarse, tau=tau)
+                                                keep_percent, sink=sink, select=select, coarse=coarse, tau=tau,
+                                                extra_tokens=extra_tokens)
         self.dense_plan = _v.vsa_plan_geometry(segments, batch, video_T, video_H, video_W, heads, _v.HEAD_DIM,
                                                100.0, sink=sink)
         self.n_tokens = int(self.sparse_plan.desc.n_tokens)

@@ -34,7 +34,7 @@ class vsa_segment(C.Structure):
 
 class vsa_options(C.Structure):
     _fields_ = [("sink", C.c_int32), ("select", C.c_int32), ("coarse", C.c_int32),
-                ("tau", C.c_float)]
+                ("tau", C.c_float), ("extra_tokens", C.c_int32)]
 
 
 class vsa_plan_desc(C.Structure):
@@ -50,12 +50,14 @@ class vsa_plan_desc(C.Structure):
 class vsa_stats(C.Structure):
     _fields_ = [("executed_pairs", C.c_int64), ("dense_pairs", C.c_int64),
                 ("sparse_rows", C.c_int64), ("dense_rows", C.c_int64),
-                ("kept_video_tiles", C.c_int64), ("k", C.c_int32), ("reserved", C.c_int32)]
+                ("kept_video_tiles", C.c_int64), ("k", C.c_int32), ("reserved", C.c_int32),
+                ("extra_tokens", C.c_int64)]
 
 
 class vsa_debug(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("qbar", "kbar", "vbar", "bias", "anchor", "scores",
-                                           "ocoarse", "thr", "lists", "counts", "total_bytes")]
+                                           "ocoarse", "thr", "lists", "counts", "xtok", "xcnt",
+                                           "total_bytes")]
 
 
 class vsa_kernel_time(C.Structure):
@@ -144,13 +146,14 @@ class Plan:
 def vsa_plan_geometry(segments, batch: int, video_T: int, video_H: int, video_W: int,
                       heads: int, head_dim: int = HEAD_DIM, keep_percent: float = 10.0,
                       sink: int = VSA_SINK_EXACT_KV, select: int = VSA_SELECT_TOPK,
-                      coarse: int = VSA_COARSE_MEAN, tau: float = 0.0, use_options: bool = True) -> Plan:
+                      coarse: int = VSA_COARSE_MEAN, tau: float = 0.0, use_options: bool = True,
+                      extra_tokens: int = 0) -> Plan:
     """segments: iterable of (start, length, kind).  Raises VsaError on a bad layout."""
     segs = list(segments)
     arr = (vsa_segment * max(1, len(segs)))()
     for i, (s, n, kd) in enumerate(segs):
         arr[i] = vsa_segment(int(s), int(n), int(kd), 0)
-    opts = vsa_options(int(sink), int(select), int(coarse), float(tau))
+    opts = vsa_options(int(sink), int(select), int(coarse), float(tau), int(extra_tokens))
     out = C.c_void_p()
     rc = _lib.vsa_plan_geometry(arr, len(segs), int(batch), int(video_T), int(video_H), int(video_W),
                                 int(heads), int(head_dim), float(keep_percent),
@@ -274,6 +277,8 @@ def debug_tensor(plan: Plan, workspace, field: str):
         "thr": (torch.float32, (B, H)),
         "lists": (torch.int32, (B, H, Qs, cap)),
         "counts": (torch.int32, (B, H, Qs)),
+        "xtok": (torch.int32, (B, H, Qs, 64)),
+        "xcnt": (torch.int32, (B, H, Qs)),
     }[field]
     dtype, shape = spec
     off = getattr(plan.debug, field)

@@ -131,6 +131,14 @@ typedef struct {
   int32_t select;  /* vsa_select */
   int32_t coarse;  /* vsa_coarse */
   float tau;       /* TAU mode threshold in standard deviations */
+  /* extra_tokens ("ComfyUI Agrega Nodo Central de Atencion Dispersa y Compilador
+   * Comfy", schedule paragraph: the best-scoring tokens beyond the selected blocks
+   * are added): 0 (off) .. 64.  Each sparse query tile i also attends to the
+   * extra_tokens valid key tokens outside its listed tiles with the largest
+   * s * qbar_i . k_t (ties to the lower packed token index; all of them if fewer
+   * remain).  Dense rows take none.  > 64 is VSA_ERR_UNSUPPORTED, < 0
+   * VSA_ERR_INVALID_ARGUMENT. */
+  int32_t extra_tokens;
 } vsa_options;
 
 typedef struct vsa_plan vsa_plan; /* opaque, host-only, immutable after creation */
@@ -163,6 +171,8 @@ typedef struct {
                                unless VSA_SINK_OFF) */
   int32_t k;                /* as in vsa_plan_desc */
   int32_t reserved;
+  int64_t extra_tokens;     /* extra tokens attended over all sparse rows (executed_pairs
+                               counts each row's staged extra tile as one pair) */
 } vsa_stats;
 
 /* Byte offsets into the workspace of the intermediates of the last forward
@@ -178,9 +188,12 @@ typedef struct {
  *   lists [batch, heads, Qs, list_capacity] int32 tile ids, ascending (the protected
  *                                   prefix tiles, then the kept candidates)
  *   counts[batch, heads, Qs]        int32 valid entries of each list
+ *   xtok  [batch, heads, Qs, 64]    int32 extra token ids, ascending (extra_tokens > 0)
+ *   xcnt  [batch, heads, Qs]        int32 extra tokens of each sparse row
  * Sparse row s of a (batch, head) is query tile s + n_dense_rows. */
 typedef struct {
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts;
+  size_t xtok, xcnt;
   size_t total_bytes;
 } vsa_debug;
 
@@ -190,7 +203,7 @@ typedef struct {
  * start inside), exactly one of kind VSA_SEG_VIDEO with length
  * video_T * video_H * video_W, each dim a multiple of 4, at most 16 prefix
  * spans.  keep_percent in (0, 100] is used in TOPK mode.  opts may be NULL
- * ({EXACT_KV, TOPK, MEAN}).  On success *out owns a new plan (free with
+ * ({EXACT_KV, TOPK, MEAN, tau 0, extra_tokens 0}).  On success *out owns a new plan (free with
  * vsa_plan_destroy); on error *out is NULL.  Host only, no device work. */
 int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch, int video_T, int video_H,
                       int video_W, int heads, int head_dim, float keep_percent,
@@ -204,7 +217,8 @@ int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out);
 
 /* Enqueue the whole forward on `stream`: geometry gather + mean pooling,
  * [anchor + log-mass bias], coarse logits, coarse softmax + O_coarse,
- * [tau statistics], selection, block-sparse fine attention with the gated
+ * [tau statistics], selection, [extra-token scoring and staging],
+ * block-sparse fine attention with the gated
  * combine O = O_fine + G * O_coarse written in packed order.
  * q, k, v, o: [batch, N, heads, 128] bf16 device buffers; g: same shape or
  * NULL (no coarse term in O).  o must not overlap q, k, v, g or the

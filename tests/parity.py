@@ -8,6 +8,9 @@ logit >= S(k) - GAP, every dropped logit <= S(k+1) + GAP; with sink off no
 tile is protected and P is 0 here); the oracle then adopts
 the GPU's list for that row before the outputs are compared.  Tau mode: the
 GPU must agree wherever |S - thr| > GAP and its choice is adopted elsewhere.
+Extra tokens: the same rule on the token scores z of the row's eligible tokens
+(given the row's list): exact where z(E) - z(E+1) > GAP, else a valid top-E
+within GAP, adopted.
 
 Outputs, over every valid element produced:
 |O_gpu - O_ref| <= 2e-2 + 2^-8 |O_ref| and ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2.
@@ -33,12 +36,14 @@ def bits_to_f64(b):
 
 
 def gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar", "vbar",
-                                              "bias", "ocoarse", "thr", "anchor")):
+                                              "bias", "ocoarse", "thr", "anchor", "xtok", "xcnt")):
     """Copy the output and the workspace intermediates to host numpy arrays."""
     import torch
     from block_sparse_video_geometry_amd import debug_tensor
     res = {"o": o.view(torch.int16).cpu().numpy().view(np.uint16)}
     for f in fields:
+        if f in ("xtok", "xcnt") and plan.desc.options.extra_tokens == 0:
+            continue
         res[f] = debug_tensor(plan, ws, f).cpu().numpy()
     return res
 
@@ -58,7 +63,9 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
     B, N, H, D = x["q"].shape
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
-    rep = dict(rows=0, exact_rows=0, adopted_rows=0, max_abs=0.0, max_excess=0.0, err2=0.0, ref2=0.0,
+    E = getattr(w, "extra", 0)
+    rep = dict(rows=0, exact_rows=0, adopted_rows=0, extra_exact=0, extra_adopted=0, max_abs=0.0,
+               max_excess=0.0, err2=0.0, ref2=0.0,
                max_s_err=0.0, max_pool_err=0.0, max_oc_err=0.0, max_bias_err=0.0, s_mag=1.0,
                bias_mag=1.0)
     g_all = x.get("g")
@@ -66,7 +73,7 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
         Q, K, V = (bits_to_f64(x[n][b, :, h]) for n in "qkv")
         G = bits_to_f64(g_all[b, :, h]) if g_all is not None else None
         _, it = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
-                               rows=rows, want_intermediates=True)
+                               rows=rows, want_intermediates=True, extra_tokens=E)
         need = it["sparse_rows"]
         S_ref = it["S"]
         if S_ref.size:
@@ -128,12 +135,42 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
                 else:
                     override[i] = glist
                     rep["adopted_rows"] += 1
-        if override:
-            Oref, _ = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
-                                     rows=rows, list_override=override)
-        else:
-            Oref, _ = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
-                                     rows=rows)
+        xover = {}
+        if E > 0:
+            # the oracle's extra tokens given the GPU's lists
+            _, it2 = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                                    rows=rows, list_override=override or None, want_intermediates=True,
+                                    extra_tokens=E)
+            scale = O.softmax_scale(D)
+            for n_i, i in enumerate(it2["sparse_rows"]):
+                if rows is not None and i not in set(rows):
+                    continue
+                s = i - n_dense
+                xc = int(gpu["xcnt"][b, h, s])
+                gx = gpu["xtok"][b, h, s, :xc].astype(np.int64)
+                ox = it2["extras"][i]
+                listed = [geom.tiles[t] for t in it2["lists"][i]]
+                listed = np.concatenate(listed) if listed else np.zeros(0, np.int64)
+                elig = np.setdiff1d(np.concatenate(geom.tiles), listed)
+                assert xc == min(E, len(elig)), f"(b{b},h{h},tile {i}) {xc} extra tokens, expected {min(E, len(elig))}"
+                assert np.all(np.diff(gx) > 0) and np.isin(gx, elig).all(), \
+                    f"(b{b},h{h},tile {i}) extra tokens not ascending or not eligible"
+                z = scale * (K[elig] @ it2["Qbar"][n_i])
+                zs = np.sort(z)[::-1]
+                ze = zs[xc - 1] if xc > 0 else np.inf
+                ze1 = zs[xc] if xc < len(zs) else -np.inf
+                if ze - ze1 > gap:
+                    assert np.array_equal(gx, ox), f"(b{b},h{h},tile {i}) extra tokens differ at gap {ze - ze1:.3g}"
+                    rep["extra_exact"] += 1
+                else:
+                    chosen = np.isin(elig, gx)
+                    assert np.all(z[chosen] >= ze - gap), f"(b{b},h{h},tile {i}) weak extra pick"
+                    assert np.all(z[~chosen] <= ze1 + gap), f"(b{b},h{h},tile {i}) weak extra drop"
+                    xover[i] = gx
+                    rep["extra_adopted"] += 1
+        Oref, _ = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                                 rows=rows, list_override=override or None, extra_tokens=E,
+                                 extra_override=xover or None)
         row_ids = range(geom.n_tiles) if rows is None else rows
         toks = np.concatenate([geom.tiles[i] for i in row_ids])
         og = bits_to_f64(gpu["o"][b, toks, h])

@@ -73,6 +73,9 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, select=2), -2),
     (dict(segs=GOOD, coarse=5), -2),
     (dict(segs=GOOD, coarse=2), 0),                                   # weighted summaries
+    (dict(segs=GOOD, extra_tokens=64), 0),                            # extra tokens: 0 .. 64
+    (dict(segs=GOOD, extra_tokens=65), -2),
+    (dict(segs=GOOD, extra_tokens=-1), -1),
     (dict(segs=GOOD, heads=0), -1),
     (dict(segs=GOOD, batch=0), -1),
     (dict(segs=[(i * 4, 4, 0) for i in range(17)] + [(68, 1024, 4)]), -2),   # > 16 prefix spans
@@ -115,10 +118,11 @@ def test_plan_shapes_match_oracle_geometry(name):
         assert d.list_capacity == pinned + len(cand)
 
 
-def test_workspace_layout():
+@pytest.mark.parametrize("extra", [0, 64])
+def test_workspace_layout(extra):
     w = WORKLOADS["full_tau_1.0"]
     p = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, 100.0, sink=w.sink,
-                            select=w.select, tau=w.tau)
+                            select=w.select, tau=w.tau, extra_tokens=extra)
     dbg = p.debug
     d = p.desc
     B, H, Tq, Vt, Qs, cap = 1, d.heads, d.n_tiles, d.n_candidates, d.n_sparse_rows, d.list_capacity
@@ -126,6 +130,8 @@ def test_workspace_layout():
              "bias": B * H * Vt * 4, "anchor": B * H * 512, "scores": B * H * Qs * Vt * 4,
              "ocoarse": B * H * Qs * 512, "thr": B * H * 4, "lists": B * H * Qs * cap * 4,
              "counts": B * H * Qs * 4}
+    if extra:
+        sizes.update(xtok=B * H * Qs * 64 * 4, xcnt=B * H * Qs * 4)
     spans = sorted((getattr(dbg, n), getattr(dbg, n) + s) for n, s in sizes.items())
     for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
         assert a1 <= b0

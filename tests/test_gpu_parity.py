@@ -34,9 +34,10 @@ def to_dev(bits):
 def run_gpu(w, x, use_gate=True):
     V = _lib()
     print(f"[gpu] {w.name} heads={w.heads} grid={w.grid} keep={w.keep} sink={w.sink} "
-          f"select={w.select} coarse={w.coarse} tau={w.tau}", flush=True)
+          f"select={w.select} coarse={w.coarse} tau={w.tau} extra={w.extra}", flush=True)
     plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128, w.keep if w.keep > 0 else 100.0,
-                               sink=w.sink, select=w.select, coarse=w.coarse, tau=w.tau)
+                               sink=w.sink, select=w.select, coarse=w.coarse, tau=w.tau,
+                               extra_tokens=w.extra)
     q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
     g = to_dev(x["g"]) if (use_gate and x.get("g") is not None) else None
     o = torch.empty_like(q)
@@ -94,6 +95,18 @@ SMALL_CASES = [
     Workload("sink_off_weighted_tau", 2, ((SEG_TEXT, 65), (SEG_REF_AUDIO, 30)), (8, 16, 16), 0.0,
              SINK_OFF, SELECT_TAU, COARSE_WEIGHTED_LOGMASS, 1.0, seed=87, recipe="offset"),
     Workload("sink_off_keep_all", 2, ((SEG_TEXT, 40),), (4, 8, 12), 100.0, SINK_OFF, seed=88),
+    # extra tokens: 64 per row on the full recipe (dense prefix rows take none), ragged
+    # prefix tiles with a video span first, sink off with tau, and keep 100% (no token
+    # left outside the lists: every count is 0)
+    scaled_down(WORKLOADS["full_extra64"], heads=2, grid=FULL_SMALL_GRID, name="extra64_small"),
+    Workload("extra_ragged", 3, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 64), (SEG_REF_AUDIO, 30)),
+             (8, 12, 16), 20.0, SINK_EXACT_KV, seed=89, recipe="scaled", video_first=True, extra=17),
+    Workload("extra_off_tau", 2, ((SEG_TEXT, 65), (SEG_REF_AUDIO, 30)), (8, 16, 16), 0.0,
+             SINK_OFF, SELECT_TAU, COARSE_MEAN_LOGMASS, 1.5, seed=90, recipe="offset", extra=40),
+    Workload("extra_keep_all", 2, ((SEG_TEXT, 40),), (4, 8, 12), 100.0, SINK_EXACT_KV, seed=91,
+             extra=64),
+    Workload("extra_one", 2, ((SEG_TEXT, 64),), (8, 8, 8), 5.0, SINK_EXACT_KV, seed=92,
+             recipe="smooth", extra=1),
 ]
 
 
@@ -104,6 +117,7 @@ def test_parity_small(w):
     gpu = PAR.gpu_results_to_numpy(plan, ws, o)
     rep = PAR.check_parity(w, x, gpu)
     print(f"[parity] {w.name}: rows={rep['rows']} exact={rep['exact_rows']} adopted={rep['adopted_rows']} "
+          f"extra exact={rep['extra_exact']} adopted={rep['extra_adopted']} "
           f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e} s_err={rep['max_s_err']:.2e}",
           flush=True)
 
@@ -133,6 +147,21 @@ def test_deterministic_and_stats():
     assert st["dense_pairs"] == w.heads * Tq * Tq
     assert st["kept_video_tiles"] == w.heads * Vt * kk
     assert 0 < st["executed_pairs"] < st["dense_pairs"]
+    assert st["extra_tokens"] == 0
+
+
+def test_stats_extra():
+    """Every sparse row with tokens left outside its list attends to exactly E of them,
+    as one more (staged) tile."""
+    V = _lib()
+    w = scaled_down(WORKLOADS["full_extra64"], heads=2, grid=FULL_SMALL_GRID, name="det_extra")
+    x = make_inputs(w)
+    plan, ws, o, _ = run_gpu(w, x)
+    st = V.vsa_read_stats(plan, ws)
+    d = plan.desc
+    P, Vt, Tq, kk = d.n_prefix_tiles, d.n_video_tiles, d.n_tiles, d.k
+    assert st["extra_tokens"] == w.heads * Vt * w.extra
+    assert st["executed_pairs"] == w.heads * (Vt * (P + kk + 1) + P * Tq)
 
 
 def test_stats_sink_off():
@@ -175,7 +204,7 @@ def _inputs_for_seed(name):
 
 
 FULL_CASES = ["full", "full_smooth_20", "full_smooth_100", "full_tau_1.0", "full_tau_1.5",
-              "full_tau_2.0", "full_logmass", "full_weighted", "full_sink_off"]
+              "full_tau_2.0", "full_logmass", "full_weighted", "full_sink_off", "full_extra64"]
 
 
 @pytest.mark.parametrize("name", FULL_CASES)
@@ -184,11 +213,11 @@ def test_parity_full_size_sampled(name):
     # workloads that share a seed share their inputs
     src = {"full_smooth_100": "full_smooth_20", "full_tau_1.5": "full_tau_1.0",
            "full_tau_2.0": "full_tau_1.0", "full_logmass": "full_tau_1.0",
-           "full_weighted": "full_tau_1.0", "full_sink_off": "full"}.get(name, name)
+           "full_weighted": "full_tau_1.0", "full_sink_off": "full", "full_extra64": "full"}.get(name, name)
     x = _inputs_for_seed(src)
     plan, ws, o, _ = run_gpu(w, x)
     gpu = PAR.gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar", "kbar",
-                                                          "vbar", "bias", "ocoarse", "thr"))
+                                                          "vbar", "bias", "ocoarse", "thr", "xtok", "xcnt"))
     d = plan.desc
     P, Tq = d.n_prefix_tiles, d.n_tiles
     pinned = 0 if w.sink == SINK_OFF else P

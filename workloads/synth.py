@@ -54,6 +54,7 @@ class Workload:
     recipe: str = "iid"
     batch: int = 1
     video_first: bool = False   # put the video span before the prefix (edge case)
+    extra: int = 0              # extra_tokens per sparse query tile (0: off)
 
     @property
     def n_video(self) -> int:
@@ -112,6 +113,9 @@ WORKLOADS = {
     # the full workload's inputs with sink_conditioning off: prefix tiles compete
     "full_sink_off": Workload("full_sink_off", 32, _FULL_PREFIX, _FULL_GRID, 10.0, SINK_OFF,
                               seed=1003, recipe="scaled"),
+    # the full workload's inputs plus 64 extra tokens per sparse query tile
+    "full_extra64": Workload("full_extra64", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
+                             SINK_EXACT_KV_AND_ROWS, seed=1003, recipe="scaled", extra=64),
 }
 
 
