@@ -237,6 +237,37 @@ def test_parity_full_size_sampled(name):
           f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e}", flush=True)
 
 
+# The plan's limits: 16 prefix segments (most of them partial tiles), a sparse row list at
+# its 2048-entry capacity (keep 100%: 8 prefix + 2040 video tiles), and 4096 video tiles
+# (the selector's 64-slots-per-lane path, 64 chunks of the coarse kernel).  Sampled rows.
+LIMIT_CASES = [
+    Workload("max_prefix_segs", 2,
+             tuple((k % 4, n) for k, n in enumerate([1, 7, 64, 65, 100, 3, 128, 30, 64, 9, 200, 17, 63, 2, 77, 40])),
+             (4, 8, 8), 25.0, SINK_EXACT_KV, seed=93, recipe="scaled"),
+    Workload("max_list", 1, ((SEG_TEXT, 300), (SEG_REF_AUDIO, 148)), (32, 60, 68), 100.0, SINK_EXACT_KV,
+             seed=94, recipe="scaled"),
+    Workload("max_video_tiles", 1, ((SEG_TEXT, 64),), (64, 64, 64), 1.0, SINK_EXACT_KV_AND_ROWS, seed=95,
+             recipe="scaled"),
+]
+
+
+@pytest.mark.parametrize("w", LIMIT_CASES, ids=[w.name for w in LIMIT_CASES])
+def test_parity_limits(w):
+    x = make_inputs(w)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    d = plan.desc
+    P, Tq = d.n_prefix_tiles, d.n_tiles
+    cnt = gpu["counts"]
+    assert np.all(cnt == P + d.k)
+    assert d.list_capacity <= 2048
+    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+    rows = sorted(set([0, P - 1, P, Tq - 1] + [int(r) for r in rng.integers(0, Tq, size=3)]))
+    rep = PAR.check_parity(w, x, gpu, heads=[(0, h) for h in range(w.heads)], rows=rows)
+    print(f"[parity-limit] {w.name}: P={P} Vt={d.n_video_tiles} cap={d.list_capacity} rows={rep['rows']} "
+          f"exact={rep['exact_rows']} adopted={rep['adopted_rows']} max_abs={rep['max_abs']:.3e}", flush=True)
+
+
 def test_parity_growing_logits():
     """Keys scaled up tile by tile (x1 for the prefix tile, up to x17 for the last video
     tile), so along every row's list the running max grows by far more than the lazy
