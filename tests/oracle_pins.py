@@ -149,7 +149,7 @@ def check_keep_counts():
 def check_dense_equivalence(w: Workload):
     """keep 100%, no gate: every list holds every tile, so the output is plain
     dense softmax attention over all tokens ([BSA-es]/[SPK-es]: sparse results
-    are judged against the dense run)."""
+    are compared with the dense run)."""
     x = make_inputs(w, with_gate=False)
     out, _ = O.forward(x, w.segments(), w.grid, 100.0, w.sink)
     for b in range(w.batch):
