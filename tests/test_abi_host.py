@@ -153,3 +153,63 @@ def test_forward_rejects_before_touching_the_gpu():
     assert rc == V.VSA_ERR_INVALID_ARGUMENT
     st = VB.vsa_stats()
     assert lib.vsa_read_stats(None, None, None, ctypes.byref(st)) == V.VSA_ERR_INVALID_ARGUMENT
+
+
+def _random_layout(rng):
+    """Random packed layouts: 0-5 prefix segments of 1-300 tokens and one video span, in a
+    random order; sometimes a gap, an overlap, a second video span or a bad grid."""
+    T, H, W = (int(rng.choice([4, 8, 12, 16])) for _ in range(3))
+    parts = [(int(rng.integers(0, 4)), int(rng.integers(1, 301))) for _ in range(int(rng.integers(0, 6)))]
+    parts.append((4, T * H * W))
+    rng.shuffle(parts)
+    segs, pos = [], 0
+    for kind, n in parts:
+        segs.append([pos, n, kind])
+        pos += n
+    flaw = int(rng.integers(0, 8))
+    if flaw == 0 and len(segs) > 1:
+        segs[1][0] += 1                      # gap
+    elif flaw == 1 and len(segs) > 1:
+        segs[1][0] -= 1                      # overlap
+    elif flaw == 2:
+        segs.append([pos, 64, 4])            # a second video span
+    elif flaw == 3:
+        T += 2                               # video grid not a multiple of 4 ...
+    elif flaw == 4:
+        H += 4                               # ... or not matching the span's length
+    order = rng.permutation(len(segs))
+    return [tuple(segs[i]) for i in order], (T, H, W)
+
+
+def test_plan_agrees_with_oracle_geometry_on_random_layouts():
+    """The C plan accepts exactly the layouts the oracle's geometry mapper accepts, and then
+    has the same prefix, video and total tile counts, k and list capacity."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    accepted = rejected = 0
+    for trial in range(400):
+        segs, grid = _random_layout(rng)
+        sink = int(rng.integers(0, 3))
+        keep = float(rng.choice([0.5, 10.0, 33.3, 100.0]))
+        try:
+            geom = O.map_geometry(segs, *grid)
+            ok = True
+        except ValueError:
+            ok = False
+        try:
+            p = V.vsa_plan_geometry(segs, 1, *grid, 2, 128, keep, sink=sink)
+        except V.VsaError as e:
+            assert not ok, f"plan rejected {segs} {grid}: {e}"
+            rejected += 1
+            continue
+        assert ok, f"plan accepted {segs} {grid}, the oracle does not"
+        accepted += 1
+        d = p.desc
+        cand = O.key_candidates(geom, sink)
+        k = O.keep_count(keep, len(cand))
+        pinned = 0 if sink == O.SINK_OFF else geom.n_prefix
+        assert (d.n_prefix_tiles, d.n_video_tiles, d.n_tiles) == (geom.n_prefix, geom.n_video, geom.n_tiles)
+        assert (d.first_candidate, d.n_candidates) == (cand[0], len(cand))
+        assert d.k == k and d.list_capacity == pinned + k
+        assert d.n_dense_rows == len(O.row_classes(geom, sink)[1])
+    assert accepted > 100 and rejected > 50
