@@ -10,7 +10,7 @@
 //
 // vsa_extra_select_kernel: one workgroup per (64 sparse rows, head, batch), wave
 // w owns rows 16 w .. 16 w + 15.  Every key tile of the head streams through LDS
-// in tile-id order (the next tile's loads in flight in registers meanwhile):
+// in tile-id order (the next two tiles' loads in flight in registers meanwhile):
 //   Z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split exactly
 //     into three bf16 terms hi + mid + lo, so the products are exact and only the
 //     fp32 accumulation rounds: the ranking then holds the fp32 order (a plain
@@ -24,7 +24,12 @@
 //     which also raises the threshold, and tests the tile's keys again.  The keys
 //     are unique, so every cut keeps exactly E.  With E = 64 a row is cut about
 //     (64 + 64 ln(tiles / 2)) / 64 times.
+//   Scoring: a key passes if its float score is >= the threshold's; only a score equal
+//     to it needs the full (score, token) key, and keys are built only for the few
+//     that enter.
 // At the end each row is cut to at most E, ranked by token and written ascending.
+// The kernel issues ~0.4k VALU instructions per tile per wave against 48 MFMAs, at
+// about one wave per SIMD, so it is bound by issue and latency rather than by the MFMAs.
 //
 // vsa_extra_gather_kernel: copies each row's extra K and V rows into staging
 // buffers laid out [batch, Qs, 64, heads, 128] (padding rows zero), i.e. with
