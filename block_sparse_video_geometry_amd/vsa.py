@@ -280,6 +280,8 @@ def debug_tensor(plan: Plan, workspace, field: str):
         "xtok": (torch.int32, (B, H, Qs, 64)),
         "xcnt": (torch.int32, (B, H, Qs)),
     }[field]
+    if field in ("xtok", "xcnt") and d.options.extra_tokens == 0:
+        raise ValueError(f"{field}: the plan has no extra tokens (extra_tokens = 0)")
     dtype, shape = spec
     off = getattr(plan.debug, field)
     n = 1

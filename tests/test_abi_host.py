@@ -213,3 +213,14 @@ def test_plan_agrees_with_oracle_geometry_on_random_layouts():
         assert d.k == k and d.list_capacity == pinned + k
         assert d.n_dense_rows == len(O.row_classes(geom, sink)[1])
     assert accepted > 100 and rejected > 50
+
+
+def test_extra_token_views_need_the_option():
+    torch = pytest.importorskip("torch")
+    p = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0)
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        V.debug_tensor(p, ws, "xtok")
+    p2 = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0, extra_tokens=8)
+    ws2 = torch.empty(p2.workspace_bytes, dtype=torch.uint8)
+    assert tuple(V.debug_tensor(p2, ws2, "xtok").shape) == (1, 2, p2.desc.n_sparse_rows, 64)
