@@ -55,6 +55,15 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// The bits of a where m is set and of b elsewhere: one v_bfi_b32, written as asm so that a
+// tree of these is not folded back into an indexed read of a register array (which the
+// compiler would place in scratch memory).
+__device__ __forceinline__ unsigned bit_pick(unsigned m, unsigned a, unsigned b) {
+  unsigned r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
 // x = hi + mid + lo exactly (each term the bf16 round-to-nearest of what is left).
 __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
   hi = (__bf16)x;
@@ -284,18 +293,19 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     // z >= thz is tested first; only a score equal to thz (rare) needs the exact key.
     float z[16];
     unsigned ge = 0u;
-    if (video) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        z[e] = acc[e >> 2][e & 3] * g.scale;
-        ge |= (unsigned)(z[e] >= thz) << e;
-      }
-    } else {  // a prefix tile may end early
+    for (int e = 0; e < 16; ++e) {
+      z[e] = acc[e >> 2][e & 3] * g.scale;
+      ge |= (unsigned)(z[e] >= thz) << e;
+    }
+    if (!video) {  // a prefix tile may end early: key 16 kb + 4 grp + i is valid iff below nv
+      unsigned vm = 0u;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        z[e] = acc[e >> 2][e & 3] * g.scale;
-        ge |= (unsigned)((z[e] >= thz) & (16 * (e >> 2) + 4 * grp + (e & 3) < nv)) << e;
+      for (int kb = 0; kb < 4; ++kb) {
+        const int nk = min(max(nv - 16 * kb - 4 * grp, 0), 4);
+        vm |= ((1u << nk) - 1u) << (4 * kb);
       }
+      ge &= vm;
     }
     if (!live || excl) ge = 0u;
     if (__ballot(ge != 0u) == 0ull) {  // nothing of this tile can enter any row
@@ -345,10 +355,24 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
       c3 = __shfl(c, ql + 48);
     }
     int at = nrow + (grp > 0 ? c0 : 0) + (grp > 1 ? c1 : 0) + (grp > 2 ? c2 : 0);
-    // keys are built only where a lane admits one (few per tile once the buffer is warm)
+    // the admitted keys, lowest e first: one pass per key of the lane that admits the most
+    // (few once the buffer is warm); key e's score picked by a select tree on e's bits
+    for (unsigned f = flag; __ballot(f != 0u) != 0ull;) {
+      if (f != 0u) {
+        const int e = __builtin_ctz(f);
+        f &= f - 1u;
+        const unsigned m0 = 0u - (e & 1), m1 = 0u - ((e >> 1) & 1), m2 = 0u - ((e >> 2) & 1),
+                       m3 = 0u - ((e >> 3) & 1);
+        unsigned l1[8], l2[4], l3[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (flag & (1u << e)) cbuf[rl][at++] = entry(z[e], tok_of(e));
+        for (int j = 0; j < 8; ++j) l1[j] = bit_pick(m0, __float_as_uint(z[2 * j + 1]), __float_as_uint(z[2 * j]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l2[j] = bit_pick(m1, l1[2 * j + 1], l1[2 * j]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) l3[j] = bit_pick(m2, l2[2 * j + 1], l2[2 * j]);
+        cbuf[rl][at++] = entry(__uint_as_float(bit_pick(m3, l3[1], l3[0])), tok_of(e));
+      }
+    }
     nrow += c0 + c1 + c2 + c3;
     walk_next(g, wc);
   };
