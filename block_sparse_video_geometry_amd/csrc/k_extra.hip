@@ -323,9 +323,11 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
       }
       return f;
     };
+    // a score equal to the row's threshold score anywhere in the lane (a superset of the
+    // candidate ties; admit() applies ge)
     bool tie = false;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) tie |= ((ge >> e) & 1u) && z[e] == thz;
+    for (int e = 0; e < 16; ++e) tie |= z[e] == thz;
     // counts over the four lanes of the row (lanes ql + 16 grp)
     unsigned flag = ge;
     if (__ballot(tie) != 0ull) flag = admit();  // a score tie with the threshold (rare)
@@ -347,7 +349,18 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
           thz = __uint_as_float((sk & 0x80000000u) ? (sk & 0x7fffffffu) : ~sk);
         }
       }
-      flag = admit();
+      // the keys again against the raised thresholds: the same float test, the exact key
+      // only on a tie
+      unsigned ge2 = 0u;
+      bool tie2 = false;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ge2 |= (unsigned)(z[e] >= thz) << e;
+        tie2 |= z[e] == thz;
+      }
+      ge &= ge2;
+      flag = ge;
+      if (__ballot(tie2) != 0ull) flag = admit();
       c = __popc(flag);
       c0 = __shfl(c, ql);
       c1 = __shfl(c, ql + 16);
