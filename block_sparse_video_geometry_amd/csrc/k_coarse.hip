@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   double ssum = 0.0, ssq = 0.0;
+  const bool tau_sums = g.select == VSA_SELECT_TAU;  // the fp64 sums only feed the tau threshold
   const bool vec_out = (g.Kc & 3) == 0;  // 16-byte score stores stay aligned
 
   fetch(0);
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
       for (int i = 0; i < 4; ++i) {
         sv[i] = st[cb][i] * g.scale + bs[jl + i];
         const bool valid = j0 + jl + i < g.Kc;
-        if (live && valid) {
+        if (tau_sums && live && valid) {
           ssum += (double)sv[i];
           ssq += (double)sv[i] * (double)sv[i];
         }
