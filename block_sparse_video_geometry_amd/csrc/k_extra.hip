@@ -55,6 +55,19 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// The value x of the four lanes (lane & 15) + 16 r, r = 0..3, in every one of them: out[r] from
+// 16-lane row r.  permlane16_swap(x, x) gives {x of row r & ~1, x of row r | 1}; a permlane32_swap
+// of each half of that gives rows 0 and 2, or 1 and 3.
+__device__ __forceinline__ void row_values4(int x, int out[4]) {
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  const auto e = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+  const auto o = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+  out[0] = (int)e[0];
+  out[1] = (int)o[0];
+  out[2] = (int)e[1];
+  out[3] = (int)o[1];
+}
+
 // The bits of a where m is set and of b elsewhere: one v_bfi_b32, written as asm so that a
 // tree of these is not folded back into an indexed read of a register array (which the
 // compiler would place in scratch memory).
@@ -233,11 +246,19 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     }
   };
   auto stash = [&](const u32x4 (&src)[4], unsigned vmask) {
+    if (vmask == 0xfu) {  // all four rows valid (every video tile)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = (tid >> 4) + 16 * m;
-      *reinterpret_cast<u32x4*>(ktile + 256 * row + 16 * ((tid & 15) ^ (row & 15))) =
-          ((vmask >> m) & 1u) ? src[m] : u32x4{0u, 0u, 0u, 0u};
+      for (int m = 0; m < 4; ++m) {
+        const int row = (tid >> 4) + 16 * m;
+        *reinterpret_cast<u32x4*>(ktile + 256 * row + 16 * ((tid & 15) ^ (row & 15))) = src[m];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = (tid >> 4) + 16 * m;
+        *reinterpret_cast<u32x4*>(ktile + 256 * row + 16 * ((tid & 15) ^ (row & 15))) =
+            ((vmask >> m) & 1u) ? src[m] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
@@ -332,7 +353,9 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     unsigned flag = ge;
     if (__ballot(tie) != 0ull) flag = admit();  // a score tie with the threshold (rare)
     int c = __popc(flag);
-    int c0 = __shfl(c, ql), c1 = __shfl(c, ql + 16), c2 = __shfl(c, ql + 32), c3 = __shfl(c, ql + 48);
+    int cr[4];
+    row_values4(c, cr);
+    int c0 = cr[0], c1 = cr[1], c2 = cr[2], c3 = cr[3];
     // a row whose buffer would overflow is cut back to its E best first (raising its
     // threshold), and its keys are tested again; after a cut E + 64 <= XCAP entries fit
     unsigned long long full = __ballot(nrow + c0 + c1 + c2 + c3 > XCAP) & 0xffffull;
@@ -362,10 +385,11 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
       flag = ge;
       if (__ballot(tie2) != 0ull) flag = admit();
       c = __popc(flag);
-      c0 = __shfl(c, ql);
-      c1 = __shfl(c, ql + 16);
-      c2 = __shfl(c, ql + 32);
-      c3 = __shfl(c, ql + 48);
+      row_values4(c, cr);
+      c0 = cr[0];
+      c1 = cr[1];
+      c2 = cr[2];
+      c3 = cr[3];
     }
     int at = nrow + (grp > 0 ? c0 : 0) + (grp > 1 ? c1 : 0) + (grp > 2 ? c2 : 0);
     // the admitted keys, lowest e first: one pass per key of the lane that admits the most
@@ -430,7 +454,10 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
   const size_t dst = ((((size_t)b * g.Qs + s) * VSA_MAX_EXTRA + e) * g.heads + h) * 16 + 4 * part;
   u32x4 ka[4], va[4];
   if (e < n) {
-    const long long src = row_offset(g, b, xtok[ro * VSA_MAX_EXTRA + e], h) / 8 + 4 * part;
+    // (a token id outside the sequence cannot come from the select kernel; clamped all the
+    // same, so that a read never leaves the (b, h) plane)
+    const int tok = min(max(xtok[ro * VSA_MAX_EXTRA + e], 0), g.N - 1);
+    const long long src = row_offset(g, b, tok, h) / 8 + 4 * part;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ka[i] = k[src + i];
