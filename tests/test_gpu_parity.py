@@ -107,6 +107,12 @@ SMALL_CASES = [
              extra=64),
     Workload("extra_one", 2, ((SEG_TEXT, 64),), (8, 8, 8), 5.0, SINK_EXACT_KV, seed=92,
              recipe="smooth", extra=1),
+    # batch 2 with the options: the batch offsets of the extra-token staging and of the
+    # sink-off candidate range and weighted summaries
+    Workload("extra_batch2", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 50)), (4, 8, 16), 25.0,
+             SINK_EXACT_KV_AND_ROWS, seed=93, recipe="scaled", batch=2, extra=33),
+    Workload("sink_off_batch2", 2, ((SEG_TEXT, 70), (SEG_REF_IMAGE, 64)), (4, 8, 16), 20.0,
+             SINK_OFF, SELECT_TOPK, COARSE_WEIGHTED_LOGMASS, seed=94, recipe="offset", batch=2),
 ]
 
 
