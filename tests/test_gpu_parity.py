@@ -245,7 +245,8 @@ def test_parity_full_size_sampled(name):
 
 # The plan's limits: 16 prefix segments (most of them partial tiles), a sparse row list at
 # its 2048-entry capacity (keep 100%: 8 prefix + 2040 video tiles), and 4096 video tiles
-# (the selector's 64-slots-per-lane path, 64 chunks of the coarse kernel).  Sampled rows.
+# (the selector's 64-slots-per-lane path, 64 chunks of the coarse kernel), also with 64
+# extra tokens.  Sampled rows.
 LIMIT_CASES = [
     Workload("max_prefix_segs", 2,
              tuple((k % 4, n) for k, n in enumerate([1, 7, 64, 65, 100, 3, 128, 30, 64, 9, 200, 17, 63, 2, 77, 40])),
@@ -254,6 +255,9 @@ LIMIT_CASES = [
              seed=94, recipe="scaled"),
     Workload("max_video_tiles", 1, ((SEG_TEXT, 64),), (64, 64, 64), 1.0, SINK_EXACT_KV_AND_ROWS, seed=95,
              recipe="scaled"),
+    # the same shape with 64 extra tokens: each row's scoring streams all 4,097 key tiles
+    Workload("max_video_tiles_extra", 1, ((SEG_TEXT, 64),), (64, 64, 64), 1.0, SINK_EXACT_KV_AND_ROWS,
+             seed=95, recipe="scaled", extra=64),
 ]
 
 
