@@ -24,8 +24,11 @@ constexpr int CCH = 64;                 // candidate tiles per LDS chunk
 constexpr int LW = VSA_HEAD_DIM + 4;    // padded LDS row (floats)
 constexpr float LOG2E_F = 1.4426950408889634f;
 
-// One workgroup per (64 sparse rows, head, batch); wave w owns rows 16 w .. 16 w + 15.
-// Per chunk of 64 candidate tiles (K-bar, V-bar and the bias staged in LDS, the next chunk's
+// One workgroup per (64 sparse rows, slice of the candidate tiles, head, batch); wave w owns
+// rows 16 w .. 16 w + 15.  With four or more 64-tile chunks the candidates are cut into
+// slices of whole chunks (so 288 row blocks at 32 heads do not leave two workgroups on a few
+// CUs and one on the rest); each slice writes its running max, sum and unnormalised O, and
+// vsa_coarse_merge_kernel combines them.  Per chunk of 64 candidate tiles (K-bar, V-bar and the bias staged in LDS, the next chunk's
 // loads in flight meanwhile):
 //   S^T = K-bar Q-bar^T on fp32 MFMAs (v_mfma_f32_16x16x4_f32).  MFMA step t of a
 //     16-tile block contracts dims k(t, g) = 16 (t >> 2) + 4 g + (t & 3) for lane group g,
@@ -43,14 +46,18 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
                                                          const float* __restrict__ bias,
                                                          float* __restrict__ scores,
                                                          float* __restrict__ ocoarse,
-                                                         double* __restrict__ statp) {
+                                                         double* __restrict__ statp,
+                                                         float* __restrict__ cpart) {
   __shared__ __attribute__((aligned(16))) float ks[CCH][LW];
   __shared__ __attribute__((aligned(16))) float vs[CCH][LW];
   __shared__ float bs[CCH];
   __shared__ double red[4][2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const size_t bh = (size_t)blockIdx.z * g.heads + blockIdx.y;
-  const int row = blockIdx.x * CROWS + 16 * wave + lr;  // the sparse row of this lane's values
+  const int rb = (int)blockIdx.x / g.csplit, slice = (int)blockIdx.x % g.csplit;
+  const int c_begin = slice * g.cchunks * CCH;                  // this slice's candidate tiles:
+  const int c_end = min(g.Kc, c_begin + g.cchunks * CCH);       // [c_begin, c_end)
+  const int row = rb * CROWS + 16 * wave + lr;  // the sparse row of this lane's values
   const bool live = row < g.Qs;
 
   // Q-bar operand: qf[m] = Q-bar[row][16 m + 4 lg .. +3] (zeros past the last row)
@@ -72,12 +79,12 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
     for (int r = 0; r < 8; ++r) {
       const int j = j0 + (tid >> 5) + 8 * r;
       kr[r] = vr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j < g.Kc) {
+      if (j < c_end) {
         kr[r] = reinterpret_cast<const f32x4*>(kb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
         vr[r] = reinterpret_cast<const f32x4*>(vb + (size_t)j * VSA_HEAD_DIM)[tid & 31];
       }
     }
-    br = (tid < CCH && j0 + tid < g.Kc) ? bb[j0 + tid] : 0.f;
+    br = (tid < CCH && j0 + tid < c_end) ? bb[j0 + tid] : 0.f;
   };
   auto stash = [&]() {
 #pragma unroll
@@ -96,12 +103,12 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
   const bool tau_sums = g.select == VSA_SELECT_TAU;  // the fp64 sums only feed the tau threshold
   const bool vec_out = (g.Kc & 3) == 0;  // 16-byte score stores stay aligned
 
-  fetch(0);
-  for (int j0 = 0; j0 < g.Kc; j0 += CCH) {
+  fetch(c_begin);
+  for (int j0 = c_begin; j0 < c_end; j0 += CCH) {
     __syncthreads();  // the previous chunk's LDS reads are done
     stash();
     __syncthreads();
-    if (j0 + CCH < g.Kc) fetch(j0 + CCH);
+    if (j0 + CCH < c_end) fetch(j0 + CCH);
 
     f32x4 st[4];
 #pragma unroll
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sv[i] = st[cb][i] * g.scale + bs[jl + i];
-        const bool valid = j0 + jl + i < g.Kc;
+        const bool valid = j0 + jl + i < c_end;
         if (tau_sums && live && valid) {
           ssum += (double)sv[i];
           ssq += (double)sv[i] * (double)sv[i];
@@ -135,12 +142,12 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
       }
       if (live) {
         float* dst = scores + (bh * g.Qs + row) * g.Kc + j0 + jl;
-        if (vec_out && j0 + jl + 3 < g.Kc) {
+        if (vec_out && j0 + jl + 3 < c_end) {
           *reinterpret_cast<f32x4*>(dst) = sv;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (j0 + jl + i < g.Kc) dst[i] = sv[i];
+            if (j0 + jl + i < c_end) dst[i] = sv[i];
         }
       }
     }
@@ -172,10 +179,21 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
         }
   }
 
-  // O_c = O / l: oacc[4 hh + q][i] = O[row][64 hh + 16 lg + 4 i + q]
+  // O_c = O / l: oacc[4 hh + q][i] = O[row][64 hh + 16 lg + 4 i + q]; with several slices
+  // the slice's max, sum and unnormalised O go to the merge instead
   const float lt = group_sum(lrow);
+  if (live && g.csplit > 1) {
+    float* prow = cpart + ((bh * g.Qs + row) * g.csplit + slice) * (VSA_HEAD_DIM + 4);
+    if (lg == 0) *reinterpret_cast<f32x4*>(prow) = f32x4{mrow, lt, 0.f, 0.f};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(prow + 4 + 64 * hh + 16 * lg + 4 * i) =
+            f32x4{oacc[4 * hh][i], oacc[4 * hh + 1][i], oacc[4 * hh + 2][i], oacc[4 * hh + 3][i]};
+  }
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (live) {
+  if (live && g.csplit == 1) {
     float* orow = ocoarse + (bh * g.Qs + row) * VSA_HEAD_DIM;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -207,6 +225,25 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
   }
 }
 
+// O_c of a row from its slices: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M the
+// largest slice max (log2 units).  One workgroup per (row, head, batch), one thread per dim.
+__global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_coarse_merge_kernel(VsaGeom g, const float* __restrict__ cpart,
+                                                                       float* __restrict__ ocoarse) {
+  const size_t ro = ((size_t)blockIdx.z * g.heads + blockIdx.y) * g.Qs + blockIdx.x;
+  const float* base = cpart + ro * g.csplit * (VSA_HEAD_DIM + 4);
+  const int d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < g.csplit; ++s) mx = fmaxf(mx, base[s * (VSA_HEAD_DIM + 4)]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < g.csplit; ++s) {
+    const float* ps = base + s * (VSA_HEAD_DIM + 4);
+    const float w = ps[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ps[0] - mx);
+    num += w * ps[4 + d];
+    den += w * ps[1];
+  }
+  ocoarse[ro * VSA_HEAD_DIM + d] = den > 0.f ? num / den : 0.f;
+}
+
 // thr = mu + tau * sigma (population) over all Qs * Kc logits of a (batch, head).
 __global__ void vsa_tau_kernel(VsaGeom g, const double* __restrict__ statp, float* __restrict__ thr) {
   const size_t bh = (size_t)blockIdx.y * g.heads + blockIdx.x;
@@ -226,11 +263,15 @@ __global__ void vsa_tau_kernel(VsaGeom g, const double* __restrict__ statp, floa
 }  // namespace
 
 void vsa_launch_coarse(const VsaGeom& g, const float* qbar, const float* kbar, const float* vbar,
-                       const float* bias, float* scores, float* ocoarse, double* statp, hipStream_t st) {
+                       const float* bias, float* scores, float* ocoarse, double* statp, float* cpart,
+                       hipStream_t st) {
   if (g.Qs == 0) return;
   dim3 grid(g.coarse_blocks, g.heads, g.batch);
   hipLaunchKernelGGL(vsa_coarse_kernel, grid, dim3(256), 0, st, g, qbar, kbar, vbar, bias, scores, ocoarse,
-                     statp);
+                     statp, cpart);
+  if (g.csplit > 1)
+    hipLaunchKernelGGL(vsa_coarse_merge_kernel, dim3(g.Qs, g.heads, g.batch), dim3(VSA_HEAD_DIM), 0, st, g,
+                       cpart, ocoarse);
 }
 
 void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream_t st) {

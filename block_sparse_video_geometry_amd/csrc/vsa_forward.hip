@@ -128,6 +128,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   int* lists = reinterpret_cast<int*>(ws + L.lists);
   int* counts = reinterpret_cast<int*>(ws + L.counts);
   double* statp = reinterpret_cast<double*>(ws + L.statp);
+  float* cpart = reinterpret_cast<float*>(ws + L.cpart);
   int* xtok = reinterpret_cast<int*>(ws + L.xtok);
   int* xcnt = reinterpret_cast<int*>(ws + L.xcnt);
   void* kx = ws + L.kx;
@@ -148,7 +149,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
     VSA_STEP("logmass", vsa_launch_logmass(G, k, v, kbar, vbar, anchor, bias, st));
   }
-  VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, st));
+  VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, cpart, st));
   if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
   VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
   if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, st));

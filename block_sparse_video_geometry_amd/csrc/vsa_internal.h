@@ -37,12 +37,16 @@ struct VsaGeom {
   int32_t sink, select, coarse;
   float tau;
   float scale;                             // softmax scale 1/sqrt(128)
-  int32_t coarse_blocks;                   // workgroups per (batch, head) of the score kernel
+  int32_t coarse_blocks;                   // workgroups per (batch, head) of the score kernel:
+                                           // row blocks x csplit
+  int32_t csplit;                          // candidate-tile slices per row block (1: no merge)
+  int32_t cchunks;                         // 64-tile chunks per slice
 };
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
   size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
+  size_t cpart;               // coarse partials per (row, slice): max, sum, 2 pad, O[128]
   size_t total;
 };
 

@@ -22,7 +22,8 @@ void vsa_launch_logmass(const VsaGeom& g, const void* k, const void* v, float* k
 // (written to scores, with the per-block tau sums), the row softmax, and
 // O_coarse = softmax(S) vbar, in one fused fp32-MFMA kernel.
 void vsa_launch_coarse(const VsaGeom& g, const float* qbar, const float* kbar, const float* vbar,
-                       const float* bias, float* scores, float* ocoarse, double* statp, hipStream_t st);
+                       const float* bias, float* scores, float* ocoarse, double* statp, float* cpart,
+                       hipStream_t st);
 
 // tau threshold mean + tau * std per (batch, head) from the partials.
 void vsa_launch_tau(const VsaGeom& g, const double* statp, float* thr, hipStream_t st);

@@ -154,7 +154,17 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   g.coarse = o.coarse;
   g.tau = o.tau;
   g.scale = (float)(1.0 / std::sqrt((double)VSA_HEAD_DIM));
-  g.coarse_blocks = (g.Qs + VSA_COARSE_ROWS - 1) / VSA_COARSE_ROWS;
+  // The coarse kernel runs 64 rows per workgroup; with few row blocks per head the
+  // candidate tiles are cut into slices of whole 64-tile chunks (each slice a workgroup,
+  // merged by a small kernel) so that the grid spreads evenly over the CUs.
+  {
+    const int row_blocks = (g.Qs + VSA_COARSE_ROWS - 1) / VSA_COARSE_ROWS;
+    const int nchunks = std::max(1, (g.Kc + 63) / 64);
+    const int target = nchunks >= 4 ? 3 : 1;
+    g.cchunks = (nchunks + target - 1) / target;
+    g.csplit = (nchunks + g.cchunks - 1) / g.cchunks;
+    g.coarse_blocks = row_blocks * g.csplit;
+  }
 
   // workspace layout
   const size_t BH = (size_t)batch * heads;
@@ -182,6 +192,7 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   L.xcnt = take(g.extra > 0 ? BH * (size_t)g.Qs * 4 : 0);
   L.kx = take(xrows * heads * VSA_HEAD_DIM * 2);
   L.vx = take(xrows * heads * VSA_HEAD_DIM * 2);
+  L.cpart = take(g.csplit > 1 ? BH * (size_t)g.Qs * g.csplit * (VSA_HEAD_DIM + 4) * 4 : 0);
   L.total = off;
 
   p->opts = o;

@@ -113,6 +113,10 @@ SMALL_CASES = [
              SINK_EXACT_KV_AND_ROWS, seed=93, recipe="scaled", batch=2, extra=33),
     Workload("sink_off_batch2", 2, ((SEG_TEXT, 70), (SEG_REF_IMAGE, 64)), (4, 8, 16), 20.0,
              SINK_OFF, SELECT_TOPK, COARSE_WEIGHTED_LOGMASS, seed=94, recipe="offset", batch=2),
+    # 210 candidate tiles (four 64-tile chunks): the coarse kernel cuts them into two slices
+    # per row block and merges the partial softmaxes; tau sums over both slices
+    Workload("coarse_slices_tau", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 40)), (8, 32, 52), 0.0,
+             SINK_OFF, SELECT_TAU, COARSE_WEIGHTED_LOGMASS, 1.5, seed=96, recipe="offset"),
 ]
 
 
