@@ -316,6 +316,16 @@ def select_topk(S_row: np.ndarray, k: int) -> np.ndarray:
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
+def tau_rows(geom: Geometry, sink: int) -> list:
+    """Query tiles whose coarse logits enter the tau moments: the sparse rows.
+
+    [BSA-es] Sol-Attn: the threshold is in sigmas of the score distribution,
+    and only rows that select have coarse scores.  Under exact_kv_and_rows the
+    conditioning query tiles run dense ([FH3] "The inputs that matter"), so
+    they score nothing and stay out of the moments."""
+    return row_classes(geom, sink)[0]
+
+
 def tau_threshold(S: np.ndarray, tau: float) -> float:
     """mu + tau * sigma over every logit of one (batch, head), population
     moments in two passes ([BSA-es] Sol-Attn: a per-head threshold in sigmas
@@ -390,13 +400,15 @@ def fine_row(Q: np.ndarray, K: np.ndarray, V: np.ndarray, geom: Geometry,
 def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
                  select: int, coarse: int, tau: float, rows=None,
                  list_override=None, want_intermediates=False, extra_tokens: int = 0,
-                 extra_override=None):
+                 extra_override=None, fine: bool = True):
     """Run the method for one (batch, head).
 
     Q, K, V, G: float64 [N, D] (G may be None).  rows: query tile ids to
     produce (None = all).  list_override: {query tile id: tile id array} to
     replace the selection of some sparse rows (used when several selections
     are correct); extra_override does the same for the extra tokens.
+    fine=False stops after the selection (lists only: no extra tokens, no
+    fine branch, O left NaN).
     Returns (O [N, D] with NaN outside the produced rows, intermediates dict
     or None).
     """
@@ -418,12 +430,18 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
     else:
         raise ValueError("unsupported coarse mode")
 
-    # the tau threshold needs every sparse row's logits; top-k only the rows asked for
+    # tau mode reports every sparse row's logits (tests read them); top-k only the rows asked for
     need = sparse if select == SELECT_TAU else [i for i in sparse if i in rows_set]
     need_idx = {i: n for n, i in enumerate(need)}
     Qbar = pool_tiles(Q, [geom.tiles[i] for i in need]) if need else np.zeros((0, Q.shape[1]))
     S, Oc = coarse_branch(Qbar, Kbar, Vbar, bias, scale) if need else (np.zeros((0, len(ct))), None)
-    thr = tau_threshold(S, tau) if select == SELECT_TAU else None
+    thr = None
+    if select == SELECT_TAU:
+        # the moments run over the logits of every row of the tau population, asked for or not
+        pop = tau_rows(geom, sink)
+        Qpop = pool_tiles(Q, [geom.tiles[i] for i in pop]) if pop else np.zeros((0, Q.shape[1]))
+        Spop = coarse_branch(Qpop, Kbar, Vbar, bias, scale)[0] if pop else np.zeros((0, len(ct)))
+        thr = tau_threshold(Spop, tau)
     k = keep_count(keep_percent, len(cand)) if select == SELECT_TOPK else None
 
     O = np.full_like(Q, np.nan)
@@ -444,6 +462,8 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
             if list_override is not None and i in list_override:
                 lst = np.asarray(list_override[i], dtype=np.int64)
         lists[i] = lst
+        if not fine:
+            continue
         ex = None
         if i not in dense_set and extra_tokens > 0:
             ex = extra_tokens_for_row(Qbar[need_idx[i]], K, geom, lst, extra_tokens, scale)
@@ -464,11 +484,11 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
 def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
             select: int = SELECT_TOPK, coarse: int = COARSE_MEAN, tau: float = 0.0,
             heads=None, rows=None, list_override=None, want_intermediates=False,
-            extra_tokens: int = 0):
+            extra_tokens: int = 0, fine: bool = True):
     """Oracle forward on bf16 bit arrays q, k, v, g ([B, N, H, D] uint16; g
     may be None).  Returns (O float64 [B, N, H, D] (NaN where not produced),
     {(b, h): intermediates}).  heads: iterable of (b, h) to run (None = all).
-    list_override: {(b, h): {query tile: tile ids}}."""
+    list_override: {(b, h): {query tile: tile ids}}.  fine=False: selection only."""
     q, k, v, g = inputs["q"], inputs["k"], inputs["v"], inputs.get("g")
     B, N, H, D = q.shape
     T, Hh, W = grid
@@ -490,6 +510,6 @@ def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
         O[b, :, h, :], it = forward_head(Qh, Kh, Vh, Gh, geom, keep_percent, sink, select,
                                          coarse, tau, rows=rows, list_override=lo,
                                          want_intermediates=want_intermediates,
-                                         extra_tokens=extra_tokens)
+                                         extra_tokens=extra_tokens, fine=fine)
         inter[(b, h)] = it
     return O, inter

@@ -298,6 +298,42 @@ def check_tau_limits(w: Workload):
             assert len(lst) == geom.n_prefix + expect_video
 
 
+def check_tau_dense_rows(tau: float = 0.7):
+    """Tau mode under exact_kv_and_rows ([BSA-es] Sol-Attn item; [FH3] "The inputs that
+    matter"): the conditioning query tiles run dense, so the moments run over the video
+    rows x video tiles logits only (Python's exact statistics module on independently
+    pooled tiles).  Each video row lists every prefix tile, then the video tiles above
+    the threshold; each prefix row lists every tile and its output is dense attention
+    over all tokens with no coarse term, although a gate is given."""
+    w = Workload("tau_rows", 2, SMALL.prefix, (8, 8, 12), 0.0, SINK_EXACT_KV_AND_ROWS,
+                 SELECT_TAU, seed=13, recipe="offset")
+    x = make_inputs(w, with_gate=True)
+    P = len(prefix_chunks(w))
+    assert P >= 2
+    cubes = video_cube_tokens(w)
+    Vt = len(cubes)
+    out, inter = O.forward(x, w.segments(), w.grid, 0.0, SINK_EXACT_KV_AND_ROWS, select=SELECT_TAU,
+                           tau=tau, want_intermediates=True)
+    kept = 0
+    for h in range(w.heads):
+        Q, K, V = (as_f64(x[n][0, :, h]) for n in "qkv")
+        _, qv = independent_pool(Q, w)
+        _, kv = independent_pool(K, w)
+        S = qv @ kv.T / math.sqrt(D)                      # video rows x video tiles
+        thr = statistics.fmean(S.ravel()) + tau * statistics.pstdev(S.ravel().tolist())
+        it = inter[(0, h)]
+        assert abs(it["thr"] - thr) < 1e-12, f"h{h}: thr {it['thr']} != {thr}"
+        for j in range(Vt):
+            want = list(range(P)) + [P + c for c in range(Vt) if S[j, c] > thr]
+            assert list(it["lists"][P + j]) == want, f"h{h} video row {j}"
+            kept += len(want) - P
+        dense = torch_sdpa(Q, K, V)
+        for i, toks in enumerate(prefix_chunks(w)):
+            assert list(it["lists"][i]) == list(range(P + Vt)), f"h{h} prefix row {i} not dense"
+            assert np.abs(out[0, toks, h] - dense[toks]).max() < 1e-12, f"h{h} prefix row {i} output"
+    assert 0 < kept < w.heads * Vt * Vt, "the threshold must keep some tiles and drop others"
+
+
 def check_tau_fractions():
     """On near-Gaussian pooled logits the kept share of video tiles follows the
     pages' tau -> share table (statistical sanity, loose bound)."""
@@ -712,6 +748,7 @@ ALL_CHECKS = [
     ("topk_ties", check_topk_ties_in_forward),
     ("tau_threshold", check_tau_threshold),
     ("tau_limits", lambda: check_tau_limits(SMALL)),
+    ("tau_dense_rows", check_tau_dense_rows),
     ("tau_fractions", check_tau_fractions),
     ("logmass", check_logmass),
     ("weighted_summaries", check_weighted_summaries),

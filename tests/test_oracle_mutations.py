@@ -15,7 +15,7 @@ from oracle import vsa_oracle as O
 _orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
                                       "logmass_bias", "coarse_branch", "tau_threshold",
                                       "keep_count", "pool_tiles", "fine_row", "weighted_summaries",
-                                      "key_candidates", "extra_tokens_for_row")}
+                                      "key_candidates", "extra_tokens_for_row", "tau_rows")}
 
 
 def _geom_swapped_axes(segments, T, H, W):
@@ -105,6 +105,11 @@ def _weighted_bias_vs_mean(Q, K, V, geom, scale, cand=None):
     return kt, vt, b2, qa
 
 
+def _tau_rows_all_tiles(geom, sink):
+    """The prefix query tiles counted in the tau moments although they run dense."""
+    return list(range(geom.n_tiles))
+
+
 def _fine_k_for_v(Q, K, V, geom, qtile, key_tiles, scale, extra=None):
     return _orig["fine_row"](Q, K, K, geom, qtile, key_tiles, scale, extra)
 
@@ -137,6 +142,7 @@ MUTATIONS = [
     ("bias_no_anchor", "logmass_bias", _bias_no_anchor, "logmass"),
     ("coarse_ignores_bias", "coarse_branch", _coarse_no_bias, "coarse_logmass"),
     ("tau_uses_variance", "tau_threshold", _tau_variance, "tau_threshold"),
+    ("tau_moments_with_dense_rows", "tau_rows", _tau_rows_all_tiles, "tau_dense_rows"),
     ("keep_floor", "keep_count", lambda p, n: max(1, min(n, math.floor(p * n / 100.0))), "keep_counts"),
     ("pool_sum", "pool_tiles", lambda X, tiles: np.stack([X[t].sum(axis=0) for t in tiles]), "pooling"),
     ("fine_k_as_v", "fine_row", _fine_k_for_v, "dense_equivalence"),
