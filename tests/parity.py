@@ -12,12 +12,15 @@ Extra tokens: the same rule on the token scores z of the row's eligible tokens
 (given the row's list): exact where z(E) - z(E+1) > GAP, else a valid top-E
 within GAP, adopted.
 
-Outputs, over every valid element produced:
-|O_gpu - O_ref| <= 2e-2 + 2^-8 |O_ref| and ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2.
-The output is bf16, so rounding it alone moves an element by up to half an ulp,
-at most 2^-8 of its magnitude (up to 0.0156 for |O| in [4, 8)); 2e-2 bounds the
-rest (bf16 inputs, bf16 probabilities in the PV product, fp32 accumulation in
-any order).
+Outputs, over every valid element produced, against the unrounded fp64 oracle:
+|O_gpu - O_ref| <= 2e-2 + h and ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 1e-2, where h
+is exactly half a bf16 ulp at the larger of |O_gpu| and |O_ref| (2^(e-8) for a
+magnitude in [2^e, 2^(e+1))).  The output is bf16, so its own rounding moves an
+element by up to h whatever the arithmetic: h is 0.0156 for |O| in [4, 8) and
+0.031 from 8 on, so a flat 2e-2 on the rounded output cannot hold for large
+outputs even with exact arithmetic.  The 2e-2 therefore bounds the arithmetic
+(bf16 inputs, bf16 probabilities in the PV product, fp32 accumulation in any
+order); ``max_abs`` reports the raw largest error.
 """
 from __future__ import annotations
 
@@ -28,7 +31,12 @@ from oracle import vsa_oracle as O
 GAP = 1e-4
 TOL_ABS = 2e-2
 TOL_REL = 1e-2
-OUT_ROUND = 2.0 ** -8  # bf16 output: half an ulp is at most this fraction of the value
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 ulp at |x| (8 significant bits): 2^(e-8) for |x| in [2^e, 2^(e+1)); 0 at 0."""
+    _, e = np.frexp(np.abs(x))          # |x| = m 2^e with m in [0.5, 1)
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
 
 
 def bits_to_f64(b):
@@ -178,13 +186,14 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
         assert np.all(np.isfinite(og)), f"(b{b},h{h}) non-finite GPU output"
         diff = og - orf
         rep["max_abs"] = max(rep["max_abs"], float(np.abs(diff).max()))
-        rep["max_excess"] = max(rep["max_excess"], float((np.abs(diff) - OUT_ROUND * np.abs(orf)).max()))
+        h_ulp = bf16_half_ulp(np.maximum(np.abs(og), np.abs(orf)))
+        rep["max_excess"] = max(rep["max_excess"], float((np.abs(diff) - h_ulp).max()))
         rep["err2"] += float((diff ** 2).sum())
         rep["ref2"] += float((orf ** 2).sum())
         rep["rows"] += len(list(row_ids))
     rep["rel_l2"] = (rep["err2"] / rep["ref2"]) ** 0.5 if rep["ref2"] > 0 else 0.0
     assert rep["max_excess"] <= tol_abs, \
-        f"error beyond bf16 output rounding {rep['max_excess']:.3g} > {tol_abs} (max abs {rep['max_abs']:.3g})"
+        f"error beyond half a bf16 ulp {rep['max_excess']:.3g} > {tol_abs} (max abs {rep['max_abs']:.3g})"
     assert rep["rel_l2"] <= tol_rel, f"relative L2 error {rep['rel_l2']:.3g} > {tol_rel}"
     if check_intermediates:
         # fp32 dot products of length 128 on pooled values: ~1e-6 relative to the logit size
@@ -193,4 +202,63 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
         assert rep["max_oc_err"] < 1e-4, f"O_coarse differs by {rep['max_oc_err']:.3g}"
         assert rep["max_bias_err"] < 1e-5 * rep["bias_mag"], \
             f"log-mass bias differs by {rep['max_bias_err']:.3g}"
+    return rep
+
+
+def check_lists(w, x, gpu, heads, gap=GAP):
+    """Selections of every sparse row of the given (batch, head) pairs against the
+    oracle (its selection only: no fine branch), with the gap rule above, plus the
+    coarse logits.  Returns a report dict; raises AssertionError on a mismatch."""
+    geom = O.map_geometry(w.segments(), *w.grid)
+    sparse, dense = O.row_classes(geom, w.sink)
+    n_dense = len(dense)
+    P = 0 if w.sink == O.SINK_OFF else geom.n_prefix
+    cand = O.key_candidates(geom, w.sink)
+    c0, nc = cand[0], len(cand)
+    rep = dict(rows=0, exact_rows=0, adopted_rows=0, max_s_err=0.0, s_mag=1.0)
+    for b, h in heads:
+        Q, K, V = (bits_to_f64(x[n][b, :, h]) for n in "qkv")
+        _, it = O.forward_head(Q, K, V, None, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                               rows=sparse, want_intermediates=True, fine=False)
+        S_ref = it["S"]
+        rep["s_mag"] = max(rep["s_mag"], float(np.abs(S_ref).max()))
+        for n_i, i in enumerate(it["sparse_rows"]):
+            s = i - n_dense
+            srow_ref = S_ref[n_i]
+            rep["max_s_err"] = max(rep["max_s_err"],
+                                   float(np.abs(gpu["scores"][b, h, s].astype(np.float64) - srow_ref).max()))
+            cnt = int(gpu["counts"][b, h, s])
+            glist = gpu["lists"][b, h, s, :cnt].astype(np.int64)
+            olist = it["lists"][i]
+            assert list(glist[:P]) == list(range(P)), f"(b{b},h{h},tile {i}) prefix tiles missing"
+            gvid = glist[P:] - c0
+            assert np.all(np.diff(gvid) > 0), f"(b{b},h{h},tile {i}) list not ascending"
+            assert gvid.size == 0 or (gvid.min() >= 0 and gvid.max() < nc)
+            sel = np.zeros(nc, bool)
+            sel[gvid] = True
+            if w.select == O.SELECT_TOPK:
+                k = it["k"]
+                assert cnt == P + k, f"(b{b},h{h},tile {i}) count {cnt} != {P + k}"
+                srt = np.sort(srow_ref)[::-1]
+                sk = srt[k - 1]
+                sk1 = srt[k] if k < len(srt) else -np.inf
+                if sk - sk1 > gap:
+                    assert np.array_equal(glist, olist), \
+                        f"(b{b},h{h},tile {i}) selection differs at gap {sk - sk1:.3g}"
+                    rep["exact_rows"] += 1
+                else:
+                    assert np.all(srow_ref[sel] >= sk - gap), f"(b{b},h{h},tile {i}) weak pick"
+                    assert np.all(srow_ref[~sel] <= sk1 + gap), f"(b{b},h{h},tile {i}) weak drop"
+                    rep["adopted_rows"] += 1
+            else:
+                thr = it["thr"]
+                clear = np.abs(srow_ref - thr) > gap
+                assert np.array_equal(sel[clear], (srow_ref > thr)[clear]), \
+                    f"(b{b},h{h},tile {i}) tau selection differs away from the threshold"
+                if np.array_equal(glist, olist):
+                    rep["exact_rows"] += 1
+                else:
+                    rep["adopted_rows"] += 1
+            rep["rows"] += 1
+    assert rep["max_s_err"] < 1e-5 * rep["s_mag"], f"coarse logits differ by {rep['max_s_err']:.3g}"
     return rep

@@ -132,6 +132,81 @@ def test_parity_small(w):
           flush=True)
 
 
+# Exact ties in the top-k selection: every video key tile a copy of video tile 0 (K only,
+# mean pooling, no bias), so every logit of a row ties exactly, in fp32 on the GPU as in
+# fp64 in the oracle.  The lowest video tile indices must win, compared with no adoption.
+# 32 candidates (one selector slot per lane) and 80 (two slots per lane, dense prefix rows).
+TIE_CASES = [
+    Workload("ties_one_slot", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 40)), (8, 16, 16), 25.0,
+             SINK_EXACT_KV, seed=97, recipe="scaled"),
+    Workload("ties_two_slots", 2, ((SEG_TEXT, 64),), (16, 16, 20), 20.0, SINK_EXACT_KV_AND_ROWS,
+             seed=98, recipe="scaled"),
+]
+
+
+@pytest.mark.parametrize("w", TIE_CASES, ids=[w.name for w in TIE_CASES])
+def test_topk_exact_ties(w):
+    x = make_inputs(w)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    k = x["k"].copy()
+    first = geom.tiles[geom.n_prefix]
+    for toks in geom.tiles[geom.n_prefix + 1:]:
+        k[:, toks] = x["k"][:, first]
+    x = dict(x, k=k)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    d = plan.desc
+    P, kk = d.n_prefix_tiles, d.k
+    assert d.n_candidates == geom.n_video and 0 < kk < geom.n_video
+    sc = gpu["scores"]
+    assert np.array_equal(sc, np.broadcast_to(sc[..., :1], sc.shape)), "GPU logits of a row do not tie"
+    want = np.array(list(range(P)) + [P + j for j in range(kk)])
+    assert np.all(gpu["counts"] == P + kk)
+    assert np.array_equal(gpu["lists"][..., :P + kk], np.broadcast_to(want, gpu["lists"][..., :P + kk].shape)), \
+        "ties must go to the lowest video tile indices"
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, want_intermediates=True, fine=False)
+    for it in inter.values():
+        for i in it["sparse_rows"]:
+            assert np.array_equal(it["lists"][i], want), f"oracle row {i}"
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[ties] {w.name}: k={kk} rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
+
+
+def test_extra_tokens_exact_ties():
+    """One token of every video tile holds the same key, aligned with head 0's mean
+    query so it out-scores every other token: for every sparse row of head 0 its copies
+    outside the listed tiles tie exactly, and the three lowest token indices must win,
+    compared with the oracle's choice with no adoption."""
+    from workloads.synth import f32_to_bf16_bits
+    w = Workload("extra_ties", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 40)), (8, 16, 16), 25.0,
+                 SINK_EXACT_KV, seed=99, recipe="offset", extra=3)
+    x = make_inputs(w)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    mu = PAR.bits_to_f64(x["q"][0, :, 0]).mean(axis=0)
+    key = f32_to_bf16_bits((3.0 * np.sqrt(128.0) * mu / np.linalg.norm(mu)).astype(np.float32))
+    k = x["k"].copy()
+    for t in range(geom.n_prefix, geom.n_tiles):
+        k[0, geom.tiles[t][5], 0] = key
+    x = dict(x, k=k)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, heads=[(0, 0)], want_intermediates=True,
+                         extra_tokens=w.extra)
+    it = inter[(0, 0)]
+    copies = {int(geom.tiles[t][5]) for t in range(geom.n_prefix, geom.n_tiles)}
+    for i in it["sparse_rows"]:
+        s = i   # exact_kv: no dense rows
+        cnt = int(gpu["counts"][0, 0, s])
+        assert np.array_equal(gpu["lists"][0, 0, s, :cnt], it["lists"][i]), f"row {i} list"
+        xc = int(gpu["xcnt"][0, 0, s])
+        gx = gpu["xtok"][0, 0, s, :xc].astype(np.int64)
+        ox = it["extras"][i]
+        assert set(ox.tolist()) <= copies and len(ox) == 3, f"row {i}: oracle extras {ox} are not tied copies"
+        assert np.array_equal(gx, ox), f"row {i}: GPU extras {gx} != oracle {ox} (lowest token ids)"
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[ties] extra tokens: rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
+
+
 def test_parity_no_gate():
     w = scaled_down(WORKLOADS["full"], heads=2, grid=(8, 16, 16), name="nogate")
     x = make_inputs(w)
@@ -245,6 +320,12 @@ def test_parity_full_size_sampled(name):
     rep = PAR.check_parity(w, x, gpu, heads=heads, rows=rows)
     print(f"[parity-full] {name}: rows={rep['rows']} exact={rep['exact_rows']} adopted={rep['adopted_rows']} "
           f"max_abs={rep['max_abs']:.3e} rel_l2={rep['rel_l2']:.3e}", flush=True)
+    # every sparse row's selection and logits on four heads (head 0 and three others)
+    others = rng.choice(np.arange(1, w.heads), size=3, replace=False)
+    lheads = [(0, 0)] + [(0, int(hh)) for hh in sorted(others)]
+    lrep = PAR.check_lists(w, x, gpu, heads=lheads)
+    print(f"[lists-full] {name}: heads={[hh for _, hh in lheads]} rows={lrep['rows']} "
+          f"exact={lrep['exact_rows']} adopted={lrep['adopted_rows']} s_err={lrep['max_s_err']:.2e}", flush=True)
 
 
 # The plan's limits: 16 prefix segments (most of them partial tiles), a sparse row list at
