@@ -144,15 +144,18 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     if (e_ != hipSuccess) return hip_fail(name, e_);           \
   } while (0)
 
-  VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
-  if (G.coarse == VSA_COARSE_MEAN_LOGMASS || G.coarse == VSA_COARSE_WEIGHTED_LOGMASS) {
-    VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
-    VSA_STEP("logmass", vsa_launch_logmass(G, k, v, kbar, vbar, anchor, bias, st));
+  // with no sparse row (the dense mode) nothing is pooled, scored or selected
+  if (G.Qs > 0) {
+    VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
+    if (G.coarse == VSA_COARSE_MEAN_LOGMASS || G.coarse == VSA_COARSE_WEIGHTED_LOGMASS) {
+      VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
+      VSA_STEP("logmass", vsa_launch_logmass(G, k, v, kbar, vbar, anchor, bias, st));
+    }
+    VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, cpart, st));
+    if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
+    VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
+    if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, st));
   }
-  VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, cpart, st));
-  if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
-  VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
-  if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, st));
   VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, kx, vx, xcnt, st));
 #undef VSA_STEP
   return VSA_OK;

@@ -43,7 +43,9 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   if (opts != nullptr) o = *opts;
   if (o.sink != VSA_SINK_OFF && o.sink != VSA_SINK_EXACT_KV && o.sink != VSA_SINK_EXACT_KV_AND_ROWS)
     return VSA_ERR_UNSUPPORTED;
-  if (o.select != VSA_SELECT_TOPK && o.select != VSA_SELECT_TAU) return VSA_ERR_UNSUPPORTED;
+  if (o.select != VSA_SELECT_TOPK && o.select != VSA_SELECT_TAU && o.select != VSA_SELECT_DENSE)
+    return VSA_ERR_UNSUPPORTED;
+  const bool dense_all = o.select == VSA_SELECT_DENSE;
   if (o.coarse != VSA_COARSE_MEAN && o.coarse != VSA_COARSE_MEAN_LOGMASS &&
       o.coarse != VSA_COARSE_WEIGHTED_LOGMASS)
     return VSA_ERR_UNSUPPORTED;
@@ -52,6 +54,7 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   if (o.select == VSA_SELECT_TAU && !std::isfinite(o.tau)) return VSA_ERR_UNSUPPORTED;
   if (o.extra_tokens < 0) return VSA_ERR_INVALID_ARGUMENT;
   if (o.extra_tokens > VSA_MAX_EXTRA) return VSA_ERR_UNSUPPORTED;
+  if (dense_all && o.extra_tokens > 0) return VSA_ERR_UNSUPPORTED;  // no sparse row to take them
 
   // spans: sort by start, must partition [0, N)
   std::vector<Seg> s;
@@ -118,9 +121,9 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   }
   // candidates: the video tiles, or with sink off every tile ("BSAI FastH3 Native VSA
   // (recipe)", "The inputs that matter": off protects no conditioning tile)
-  g.npin = (o.sink == VSA_SINK_OFF) ? 0 : g.P;
+  g.npin = (o.sink == VSA_SINK_OFF || dense_all) ? 0 : g.P;
   g.kc0 = g.npin;
-  g.Kc = g.Tq - g.kc0;
+  g.Kc = dense_all ? 0 : g.Tq - g.kc0;  // the dense mode scores no candidate
   if (g.Kc > VSA_MAX_VIDEO_TILES) {
     delete p;
     return VSA_ERR_UNSUPPORTED;
@@ -128,10 +131,13 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   g.N = (int32_t)N;
   g.heads = heads;
   g.batch = batch;
-  g.n_dense = (o.sink == VSA_SINK_EXACT_KV_AND_ROWS) ? g.P : 0;
+  g.n_dense = dense_all ? g.Tq : (o.sink == VSA_SINK_EXACT_KV_AND_ROWS) ? g.P : 0;
   g.Qs = g.Tq - g.n_dense;
   // k = ceil(keep * Kc / 100), clamped to [1, Kc]
-  if (o.select == VSA_SELECT_TOPK) {
+  if (dense_all) {
+    g.k = 0;
+    g.cap = 0;
+  } else if (o.select == VSA_SELECT_TOPK) {
     int k = (int)std::ceil((double)keep_percent * g.Kc / 100.0 - 1e-9);
     g.k = std::max(1, std::min(g.Kc, k));
     g.cap = g.npin + g.k;
@@ -176,14 +182,15 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     off = align_up(off + std::max<size_t>(bytes, 1), A);
     return at;
   };
-  L.qbar = take(BH * g.Tq * VSA_HEAD_DIM * 4);
+  // the dense mode pools nothing: only its (empty) sparse-row sections remain
+  L.qbar = take(dense_all ? 0 : BH * g.Tq * VSA_HEAD_DIM * 4);
   L.kbar = take(BH * g.Kc * VSA_HEAD_DIM * 4);
   L.vbar = take(BH * g.Kc * VSA_HEAD_DIM * 4);
   L.bias = take(BH * g.Kc * 4);
-  L.anchor = take(BH * VSA_HEAD_DIM * 4);
+  L.anchor = take(dense_all ? 0 : BH * VSA_HEAD_DIM * 4);
   L.scores = take(BH * (size_t)g.Qs * g.Kc * 4);
   L.ocoarse = take(BH * (size_t)g.Qs * VSA_HEAD_DIM * 4);
-  L.thr = take(BH * 4);
+  L.thr = take(dense_all ? 0 : BH * 4);
   L.lists = take(BH * (size_t)g.Qs * g.cap * 4);
   L.counts = take(BH * (size_t)g.Qs * 4);
   L.statp = take(BH * (size_t)g.coarse_blocks * 2 * 8);

@@ -9,9 +9,8 @@ Policy follows the pages; none of it lives in the library, which only runs a for
   paragraph: a 0.2 - 1.0 window keeps the first denoise steps dense; its benchmark
   paragraph keeps the first transformer layer dense at every step.
 - Same page: outside the window or under min_tokens the ordinary dense attention runs.
-  Here that is the same forward on a keep = 100% plan with no gate: every list then
-  holds every tile, so the fine branch is exact dense attention over the valid tokens
-  and no coarse term is added.
+  Here that is the library's dense plan (select mode DENSE): every query tile attends
+  to every key tile exactly, and no pooling, coarse branch or selection runs.
 
 Every forward runs in libvsa.so's kernels; this module only picks the plan and the
 buffers.  A captured graph replays the same kernel launches on fixed buffers.
@@ -68,7 +67,7 @@ class LayerDriver:
                                                 keep_percent, sink=sink, select=select, coarse=coarse, tau=tau,
                                                 extra_tokens=extra_tokens)
         self.dense_plan = _v.vsa_plan_geometry(segments, batch, video_T, video_H, video_W, heads, _v.HEAD_DIM,
-                                               100.0, sink=sink)
+                                               100.0, sink=sink, select=_v.VSA_SELECT_DENSE)
         self.n_tokens = int(self.sparse_plan.desc.n_tokens)
         big = max(self.sparse_plan.workspace_bytes, self.dense_plan.workspace_bytes)
         import torch

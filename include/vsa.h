@@ -109,8 +109,14 @@ typedef enum {
  * largest coarse logits of each sparse query tile (ties to the lowest tile
  * index); TAU keeps every candidate whose logit exceeds mean + tau * std of
  * all the (sparse query tile, candidate) logits of its (batch, head)
- * (Sol-Attn, "un nodo, tres backends"). */
-typedef enum { VSA_SELECT_TOPK = 0, VSA_SELECT_TAU = 1 } vsa_select;
+ * (Sol-Attn, "un nodo, tres backends").
+ * DENSE is the explicit dense call the schedule makes outside its window
+ * ("ComfyUI Agrega Nodo Central de Atencion Dispersa y Compilador Comfy", schedule
+ * paragraph: outside the start/end window the ordinary dense attention runs): every
+ * query tile attends to every key tile exactly, no pooling, coarse branch or
+ * selection runs, g is ignored (no coarse term), and keep_percent, sink, coarse
+ * and tau are ignored; extra_tokens must be 0 (else VSA_ERR_UNSUPPORTED). */
+typedef enum { VSA_SELECT_TOPK = 0, VSA_SELECT_TAU = 1, VSA_SELECT_DENSE = 2 } vsa_select;
 
 /* Coarse logits: MEAN is s * qbar . kbar; MEAN_LOGMASS adds the per candidate
  * tile bias b_j = log(mean_{t in j} exp(s q_a . (k_t - kbar_j))) with q_a the
@@ -220,6 +226,12 @@ int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out);
  * [tau statistics], selection, [extra-token scoring and staging],
  * block-sparse fine attention with the gated
  * combine O = O_fine + G * O_coarse written in packed order.
+ * Defined by "BSAI FastH3 Native VSA (recipe)", "The mechanism, briefly"
+ * (64-token blocks scored, only the top share attended exactly), and by
+ * "Spark-H3: atencion dispersa por bloques acelera MiniMax-H3 en ComfyUI",
+ * "Que cambia Spark-Attn" (an exact branch over the top-ranked key/value
+ * blocks plus a compressed branch over the pooled summaries); the gate is
+ * "Ref2VA VSA : noeud d'attention sparse pour le Ref2VA H3", item 3.
  * q, k, v, o: [batch, N, heads, 128] bf16 device buffers; g: same shape or
  * NULL (no coarse term in O).  o must not overlap q, k, v, g or the
  * workspace.  workspace: >= vsa_plan_workspace_bytes, 256-byte aligned,

@@ -70,7 +70,10 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, sink=0), 0),                                     # sink_conditioning off
     (dict(segs=[(0, 64, 0), (64, 4 * 256 * 256, 4)], T=4, H=256, W=256), 0),          # 4096 video tiles
     (dict(segs=[(0, 64, 0), (64, 4 * 256 * 256, 4)], T=4, H=256, W=256, sink=0), -2),  # 4097 candidates
-    (dict(segs=GOOD, select=2), -2),
+    (dict(segs=GOOD, select=2), 0),                                   # dense mode
+    (dict(segs=GOOD, select=2, keep=0.0, sink=0, coarse=2), 0),       # ... ignores keep, sink, coarse
+    (dict(segs=GOOD, select=2, extra_tokens=4), -2),                  # ... takes no extra tokens
+    (dict(segs=GOOD, select=3), -2),
     (dict(segs=GOOD, coarse=5), -2),
     (dict(segs=GOOD, coarse=2), 0),                                   # weighted summaries
     (dict(segs=GOOD, extra_tokens=64), 0),                            # extra tokens: 0 .. 64
@@ -86,6 +89,18 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
 ])
 def test_plan_validation(case, expect):
     assert plan_status(**case) == expect
+
+
+def test_dense_plan_shape():
+    """The dense mode: every query tile is a dense row; nothing is pooled or selected, so
+    the workspace holds only empty sections."""
+    w = WORKLOADS["full"]
+    p = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, 100.0, sink=w.sink,
+                            select=V.VSA_SELECT_DENSE)
+    d = p.desc
+    assert d.n_dense_rows == d.n_tiles == 564 and d.n_sparse_rows == 0
+    assert d.k == 0 and d.list_capacity == 0 and d.n_candidates == 0
+    assert p.workspace_bytes <= 64 * 256
 
 
 def test_null_options_defaults():

@@ -4,7 +4,8 @@
   its buffers before each replay, with eager forwards and synchronisations in between.
   Every replay must equal the eager forward on the same inputs, bit for bit (the kernels
   are deterministic).
-- The dense fallback (keep 100%, no gate) must match the fp64 oracle's dense attention.
+- The dense fallback (the plan's dense mode) must match the fp64 oracle's dense
+  attention (keep 100%, no gate), and so must a direct dense-mode forward.
 """
 import dataclasses
 
@@ -60,8 +61,45 @@ def test_driver_dense_fallback_matches_oracle():
     o = torch.empty_like(q)
     assert drv.forward(1, 4, 3, q, k, v, g, o) is False
     torch.cuda.synchronize()
-    gpu = PAR.gpu_results_to_numpy(drv.dense_plan, drv.workspace, o)
-    PAR.check_parity(dataclasses.replace(w, keep=100.0), dict(x, g=None), gpu)
+    d = drv.dense_plan.desc
+    assert d.n_dense_rows == d.n_tiles and d.n_sparse_rows == 0
+    _check_dense(w, x, o)
+
+
+def _check_dense(w, x, o):
+    """GPU output against the oracle's keep-100% forward with no gate (dense attention)."""
+    from oracle import vsa_oracle as O
+    ref, _ = O.forward(dict(x, g=None), w.segments(), w.grid, 100.0, w.sink)
+    got = PAR.bits_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    diff = got - ref
+    max_abs = float(np.abs(diff).max())
+    rel = float(np.sqrt((diff ** 2).sum() / (ref ** 2).sum()))
+    print(f"[dense] {w.name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= PAR.TOL_ABS and rel <= PAR.TOL_REL
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_dense_mode_matches_oracle(name):
+    """A dense-mode plan runs every query tile over every key tile with no coarse term,
+    whatever the gate: ragged prefix tiles, two batch items, video span first."""
+    import block_sparse_video_geometry_amd as V
+    from workloads.synth import Workload, SEG_TEXT, SEG_REF_IMAGE, SINK_EXACT_KV_AND_ROWS
+    w = WORKLOADS["tiny"] if name == "tiny" else Workload(
+        "dense_ragged", 3, ((SEG_TEXT, 100), (SEG_REF_IMAGE, 30)), (8, 12, 16), 10.0,
+        SINK_EXACT_KV_AND_ROWS, seed=101, recipe="scaled", batch=2, video_first=True)
+    print(f"[gpu] dense mode on {w.name}", flush=True)
+    x = make_inputs(w)
+    plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128, 100.0,
+                               select=V.VSA_SELECT_DENSE)
+    q, k, v, g = (_dev(x[n]) for n in "qkvg")
+    o = torch.empty_like(q)
+    ws = V.alloc_workspace(plan)
+    V.vsa_forward(plan, q, k, v, g, o, ws)
+    st = V.vsa_read_stats(plan, ws)
+    d = plan.desc
+    assert st["executed_pairs"] == st["dense_pairs"] == w.batch * w.heads * d.n_tiles ** 2
+    assert st["sparse_rows"] == 0
+    _check_dense(w, x, o)
 
 
 def test_driver_sparse_call_matches_forward():
