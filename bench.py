@@ -1,7 +1,7 @@
 """Benchmark of the two-branch video sparse attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload full]
-                    [--no-cpu-baseline] [--cpu-seconds 15]
+                    [--no-cpu-baseline] [--cpu-workers 16] [--cpu-heads H]
 
 One step = one whole vsa_forward (pool, [log-mass], coarse logits + softmax +
 O_coarse, [tau], selection, fine attention + gated combine) on the full clip
@@ -39,10 +39,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="most worker processes of the oracle's CPU baseline (one head per task)")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="time the oracle on this many heads only (default: all, the whole forward)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fine_full_traffic.json"),
                     help="measured HBM bytes per fine launch (from rocprofv3 counters)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the dense call (the dense-mode plan the schedule runs outside its window)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (ms_per_step_graph)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -51,60 +55,62 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, x, target_s):
-    """Time the fp64 oracle on a bounded sample of the same workload: heads in
-    order, each with its pooling, coarse branch and selection and then the fine
-    branch of its query tiles (dense and sparse alternately, in growing
-    batches), until about target_s seconds have passed.  Reported as
-    effective TFLOP/s over the sampled pairs."""
-    from threadpoolctl import threadpool_info
+# inputs of the CPU baseline, read by forked workers (set before the pool starts)
+_CPU_INPUTS = {}
+
+
+def _oracle_head(h):
+    """One (batch 0, head h) of the oracle's whole forward, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+    from oracle import vsa_oracle as O
+    w, x = _CPU_INPUTS["w"], _CPU_INPUTS["x"]
+    geom = O.map_geometry(w.segments(), *w.grid)
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        Qh, Kh, Vh = (O.bf16_bits_to_f64(x[n][0, :, h]) for n in "qkv")
+        Gh = O.bf16_bits_to_f64(x["g"][0, :, h]) if x.get("g") is not None else None
+        O.forward_head(Qh, Kh, Vh, Gh, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
+                       extra_tokens=w.extra)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, x, max_workers, heads=None):
+    """Wall-clock of the fp64 oracle's whole forward on the same inputs (every head,
+    every query tile: pooling, coarse branch, selection, fine branch and combine), one
+    head per task over a pool of forked single-threaded workers on the host cores.
+    Reported as effective TFLOP/s over the executed pairs, like the GPU figure.  Runs
+    before anything touches the GPU, so the workers fork from a process without it."""
+    import multiprocessing as mp
     from oracle import vsa_oracle as O
     geom = O.map_geometry(w.segments(), *w.grid)
     sparse, dense = O.row_classes(geom, w.sink)
-    order = []
-    for i in range(max(len(sparse), len(dense))):
-        if i < len(dense):
-            order.append(dense[i])
-        if i < len(sparse):
-            order.append(sparse[i])
-    dense_set = set(dense)
-    k = O.keep_count(w.keep, geom.n_video)
+    k = O.keep_count(w.keep, len(O.key_candidates(geom, w.sink)))
+    n_heads = w.heads if heads is None else min(heads, w.heads)
+    pairs = n_heads * (len(dense) * geom.n_tiles + len(sparse) * ((0 if w.sink == 0 else geom.n_prefix) + k))
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(max_workers, avail, n_heads))
+    _CPU_INPUTS.update(w=w, x=x)
     t0 = time.perf_counter()
-    rows = 0
-    pairs = 0
-    heads = 0
-    done = False
-    for h in range(w.heads):
-        Qh = O.bf16_bits_to_f64(x["q"][0, :, h])
-        Kh = O.bf16_bits_to_f64(x["k"][0, :, h])
-        Vh = O.bf16_bits_to_f64(x["v"][0, :, h])
-        Gh = O.bf16_bits_to_f64(x["g"][0, :, h])
-        heads += 1
-        pos, n = 0, 1
-        while pos < len(order):
-            batch = order[pos:pos + n]
-            O.forward_head(Qh, Kh, Vh, Gh, geom, w.keep, w.sink, w.select, w.coarse, w.tau, rows=batch)
-            pos += len(batch)
-            rows += len(batch)
-            pairs += sum(geom.n_tiles if r in dense_set else geom.n_prefix + k for r in batch)
-            if time.perf_counter() - t0 >= target_s:
-                done = True
-                break
-            n = min(64, n * 2)
-        if done:
-            break
+    with mp.get_context("fork").Pool(workers) as pool:
+        per_head = pool.map(_oracle_head, range(n_heads), chunksize=1)
     el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    _CPU_INPUTS.clear()
     return {
-        "value": pairs * PAIR_FLOP / el / 1e12,
+        "value": round(pairs * PAIR_FLOP / el / 1e12, 5),
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle on the same inputs, heads taken in order ({heads} started): "
-                   f"pooling + coarse + selection per head and the fine branch of {rows} query-tile rows "
-                   f"({pairs} pairs of {w.heads * (geom.n_video * (geom.n_prefix + k) + geom.n_prefix * geom.n_tiles) if w.sink == 2 else 'n/a'}) "
-                   f"in {el:.1f} s; dense and sparse rows alternate"),
+        "sample": (f"whole forward of the fp64 numpy oracle on the same inputs: {n_heads} of {w.heads} heads, "
+                   f"every query tile ({pairs} executed pairs), one head per task on {workers} forked "
+                   f"workers with single-threaded BLAS; wall-clock {el:.1f} s"),
         "seconds": round(el, 2),
+        "ms_per_layer": round(1e3 * el, 1) if n_heads == w.heads else None,
+        "head_seconds_mean": round(sum(per_head) / len(per_head), 2),
+        "nproc": os.cpu_count(),
+        "affinity_cores": avail,
     }
 
 
@@ -115,13 +121,19 @@ def main():
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
-    import block_sparse_video_geometry_amd as V
     from workloads.synth import WORKLOADS, make_inputs
 
     w = WORKLOADS[a.workload]
     t0 = time.perf_counter()
     x = make_inputs(w)
     gen_s = time.perf_counter() - t0
+    # the CPU baseline first: its workers fork from a process that has not touched the GPU
+    cpu = None
+    if not a.no_cpu_baseline:
+        print(f"[bench] cpu baseline: fp64 oracle, whole forward of {w.name}", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x, a.cpu_workers, a.cpu_heads)
+        print(f"[bench] cpu baseline done in {cpu['seconds']} s", file=sys.stderr, flush=True)
+    import block_sparse_video_geometry_amd as V
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -179,6 +191,29 @@ def main():
             graph.replay()
         graph_ms, _ = timed_steps(graph.replay)
     kt = timer.read()
+    # the dense call on the same inputs: every query tile over every key tile, no coarse branch
+    dense = None
+    if not a.no_dense:
+        dplan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128, 100.0,
+                                    select=V.VSA_SELECT_DENSE)
+        dws = V.alloc_workspace(dplan)
+        od = torch.empty_like(q)
+        for _ in range(2):
+            V.vsa_forward(dplan, q, k, v, None, od, dws)
+        dstats = V.vsa_read_stats(dplan, dws)
+        n_dense_calls = 5
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for _ in range(n_dense_calls):
+            V.vsa_forward(dplan, q, k, v, None, od, dws)
+        evs[1].record(stream)
+        torch.cuda.synchronize()
+        dms = evs[0].elapsed_time(evs[1]) / n_dense_calls
+        dense = {"ms_per_call": round(dms, 3), "calls": n_dense_calls,
+                 "tflops": round(dstats["executed_pairs"] * PAIR_FLOP / (dms * 1e-3) / 1e12, 1),
+                 "executed_pairs": dstats["executed_pairs"]}
+        del od, dws, dplan
     flop = stats["executed_pairs"] * PAIR_FLOP
     tflops = flop / (ms * 1e-3) / 1e12
 
@@ -238,11 +273,13 @@ def main():
             "avg_launch_ms": round(fine_avg_ms, 4),
         },
         "whole_forward_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_call": dense,
+        "sparse_speedup_vs_dense": round(dense["ms_per_call"] / ms, 2) if dense else None,
         "kernels": kernels,
         "input_gen_s": round(gen_s, 1),
     }
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x, a.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
