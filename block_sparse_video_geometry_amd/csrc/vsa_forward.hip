@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -198,6 +199,55 @@ extern "C" int vsa_forward(const vsa_plan* plan, const void* q, const void* k, c
                            const void* g, void* o, void* workspace, size_t workspace_bytes,
                            void* stream) {
   return forward_common(plan, q, k, v, g, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+// ---- the no-allocation forward ---------------------------------------------------
+// The workspace of vsa_forward_noalloc: one static device array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not a device address:
+// the host only ever uses the per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[VSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// Address of the scratch array on the current device, looked up on the first call there
+// (with that device current).  No allocation.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return VSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (ptr == nullptr) return hip_fail("hipGetSymbolAddress(scratch)", hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" int vsa_forward_noalloc(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                                   const void* g, void* o, void* stream) {
+  if (plan == nullptr || q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return VSA_ERR_INVALID_ARGUMENT;
+  if (plan->ws.total > VSA_NOALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "vsa_forward_noalloc: the plan needs %zu workspace bytes; the static scratch holds %zu",
+                  plan->ws.total, (size_t)VSA_NOALLOC_SCRATCH_BYTES);
+    return VSA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != VSA_OK) return rc;
+  return forward_common(plan, q, k, v, g, o, ws, VSA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 extern "C" int vsa_forward_timed(const vsa_plan* plan, const void* q, const void* k, const void* v,

@@ -64,7 +64,10 @@ class vsa_kernel_time(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("launches", C.c_int32), ("total_ms", C.c_double)]
 
 
+VSA_NOALLOC_SCRATCH_BYTES = 160 << 20
+
 EXPORTS = ["vsa_plan_geometry", "vsa_plan_workspace_bytes", "vsa_plan_describe", "vsa_forward",
+           "vsa_forward_noalloc",
            "vsa_read_stats", "vsa_debug_views", "vsa_plan_destroy", "vsa_status_string",
            "vsa_last_error",
            "vsa_timer_create", "vsa_timer_destroy", "vsa_timer_reset", "vsa_forward_timed",
@@ -90,6 +93,7 @@ def _load():
         "vsa_plan_workspace_bytes": (I, [P, C.POINTER(S)]),
         "vsa_plan_describe": (I, [P, C.POINTER(vsa_plan_desc)]),
         "vsa_forward": (I, [P, P, P, P, P, P, P, S, P]),
+        "vsa_forward_noalloc": (I, [P, P, P, P, P, P, P]),
         "vsa_read_stats": (I, [P, P, P, C.POINTER(vsa_stats)]),
         "vsa_debug_views": (I, [P, C.POINTER(vsa_debug)]),
         "vsa_plan_destroy": (I, [P]),
@@ -114,7 +118,7 @@ _lib = _load()
 class VsaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        detail = _lib.vsa_last_error().decode() if status == VSA_ERR_HIP else ""
+        detail = _lib.vsa_last_error().decode() if status in (VSA_ERR_HIP, VSA_ERR_WORKSPACE) else ""
         super().__init__(f"{what}: {vsa_status_string(status)} ({status}) {detail}".rstrip())
 
 
@@ -213,6 +217,17 @@ def vsa_forward(plan: Plan, q, k, v, g, o, workspace, stream=None) -> None:
     """Enqueue the forward on `stream` (default: torch's current stream)."""
     args = _forward_args(plan, q, k, v, g, o, workspace)
     _check(_lib.vsa_forward(*args, _stream_handle(stream)), "vsa_forward")
+
+
+def vsa_forward_noalloc(plan: Plan, q, k, v, g, o, stream=None) -> None:
+    """Enqueue the forward with the library's static device scratch as its workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    d = plan.desc
+    shape = (d.batch, d.n_tokens, d.heads, HEAD_DIM)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)) + ((("g", g),) if g is not None else ()):
+        _check_tensor(name, t, shape)
+    _check(_lib.vsa_forward_noalloc(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o),
+                                    _stream_handle(stream)), "vsa_forward_noalloc")
 
 
 def vsa_read_stats(plan: Plan, workspace, stream=None) -> dict:

@@ -241,6 +241,25 @@ int vsa_plan_describe(const vsa_plan* plan, vsa_plan_desc* out);
 int vsa_forward(const vsa_plan* plan, const void* q, const void* k, const void* v, const void* g,
                 void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): vsa_forward with the
+ * workspace taken from a library-owned device array of VSA_NOALLOC_SCRATCH_BYTES
+ * (160 MiB) on each GPU, instead of a caller buffer.  The array is a static
+ * device variable of the library: each GPU the call runs on holds its own copy
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the first call on a device only looks up the
+ * array's address there.  Plans whose workspace exceeds the array are rejected
+ * with VSA_ERR_WORKSPACE before anything is enqueued (vsa_last_error names both
+ * sizes).  Every call on one GPU shares that GPU's array and leaves the last
+ * call's intermediates in it: calls that overlap on one GPU (other streams, other
+ * threads) race, so order them on one stream.  No kernel needs the array cleared
+ * (every intermediate is written before it is read).  Other arguments, checks and
+ * results as vsa_forward; vsa_read_stats does not apply (it reads a caller
+ * workspace). */
+#define VSA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+int vsa_forward_noalloc(const vsa_plan* plan, const void* q, const void* k, const void* v,
+                        const void* g, void* o, void* stream);
+
 /* Counters of the last forward that used `workspace` (reads the list counts
  * back; synchronises `stream`). */
 int vsa_read_stats(const vsa_plan* plan, const void* workspace, void* stream, vsa_stats* out);
@@ -253,9 +272,10 @@ int vsa_plan_destroy(vsa_plan* plan);
 /* Static string for a status code (never NULL). */
 const char* vsa_status_string(int status);
 
-/* Detail of the last VSA_ERR_HIP returned on the calling thread: the step
- * and the HIP error name and text ("" if none).  Valid until the next call
- * on the same thread. */
+/* Detail of the last VSA_ERR_HIP returned on the calling thread (the step and
+ * the HIP error name and text), or of the last VSA_ERR_WORKSPACE returned by
+ * vsa_forward_noalloc (the sizes); "" if none.  Valid until the next call on the
+ * same thread. */
 const char* vsa_last_error(void);
 
 /* ---- kernel timing for measurement -------------------------------------
