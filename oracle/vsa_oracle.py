@@ -92,7 +92,22 @@ the design notes):
   * weighted summaries (the page does not give the weights): the anchor's own
     attention over the tile, w_t = softmax_t(l_t); ktil_j = sum_t w_t k_t,
     vtil_j = sum_t w_t v_t; the bias keeps the same anchor identity,
-    b_j = log(mean_t exp(l_t)) - s q_a . ktil_j.
+    b_j = log(mean_t exp(l_t)) - s q_a . ktil_j;
+  * Spark-Reblock ([SPK-es] "Que cambia Spark-Attn", Spark-Reblock item, and
+    reblock_layout=q_reuse_k in its "Flujos de trabajo"; the page gives the
+    similarity and the hierarchical splitting down to the block size in
+    O(N log N), not the split rule): per (batch, head) the video tokens are
+    partitioned by a fixed-shape binary tree.  M = mean over the video keys of
+    k k^T (the opposite side's second moment); a query's M-normalised form is
+    psi = q / sqrt(q^T M q), so the M-cosine of two queries is the cosine of
+    their score patterns over the video keys.  A group of m tiles (64 m
+    tokens, m >= 2) is split along its principal axis: the group's centred
+    psi covariance C, REBLOCK_POWER_STEPS power steps z <- C M z from z = 1
+    (z scaled to M-norm 1 at every step), projections p = psi^T M z; tokens
+    sorted by (p, token id), the first 64 floor(m/2) form the left child
+    (tiles [t0, t0 + floor(m/2))), the rest the right.  Leaves are the video
+    tiles in tree order (the tie-break index), tokens ascending inside a
+    leaf; key tiles reuse the query partition; prefix tiles are unchanged.
 """
 from __future__ import annotations
 
@@ -220,6 +235,102 @@ def row_classes(geom: Geometry, sink: int):
     if sink == SINK_EXACT_KV_AND_ROWS:
         return video, prefix
     raise ValueError("unsupported sink mode")
+
+
+# --------------------------------------------------------------------------
+# 1b. Spark-Reblock: an adaptive partition of the video tokens
+# --------------------------------------------------------------------------
+REBLOCK_POWER_STEPS = 3
+
+
+def reblock_metric(Q: np.ndarray, K: np.ndarray, geom: Geometry) -> np.ndarray:
+    """M = (1/Nv) sum over the video keys of k k^T ([SPK-es] Spark-Reblock: the
+    metric is induced by the second moment of the opposite side; for the query
+    partition that is the keys).  Q is not used; it is an argument so that the
+    choice of side is explicit."""
+    vt = np.concatenate(geom.tiles[geom.n_prefix:])
+    Kv = K[vt]
+    return Kv.T @ Kv / len(vt)
+
+
+def reblock_features(qv: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """psi = q / sqrt(q^T M q) per row of qv: the M-cosine of two queries is the
+    M inner product of their psi.  A query with q^T M q = 0 takes psi = 0."""
+    nrm = np.sqrt(np.maximum(np.einsum("id,de,ie->i", qv, M, qv), 0.0))
+    return np.where(nrm[:, None] > 0, qv / np.where(nrm > 0, nrm, 1.0)[:, None], 0.0)
+
+
+def principal_projection(X: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Projections of a group's psi rows X on the group's principal axis in the
+    metric M: REBLOCK_POWER_STEPS power steps z <- C M z from z = 1 with C the
+    centred covariance of X, z scaled to M-norm 1 before each step; then
+    p_i = X_i^T M z / |z|_M (in [-1, 1]).  A zero axis gives p = 0 everywhere."""
+    n = X.shape[0]
+    Xc = X - X.mean(axis=0)
+    z = np.ones(X.shape[1])
+    for _ in range(REBLOCK_POWER_STEPS):
+        a = M @ z
+        za = float(z @ a)
+        a = a / math.sqrt(za) if za > 0 else np.zeros_like(a)
+        z = Xc.T @ (Xc @ a) / n
+    a = M @ z
+    za = float(z @ a)
+    a = a / math.sqrt(za) if za > 0 else np.zeros_like(a)
+    return X @ a
+
+
+def reblock_order(p: np.ndarray, toks: np.ndarray) -> np.ndarray:
+    """Positions of a group's tokens sorted by projection, equal projections by
+    the lower token id."""
+    return np.lexsort((toks, p))
+
+
+def reblock_left_tiles(m: int) -> int:
+    """Tiles of the left (lower-projection) child of a group of m tiles."""
+    return m // 2
+
+
+def reblock_geometry(Q: np.ndarray, K: np.ndarray, geom: Geometry, split_hook=None) -> Geometry:
+    """The fixed-tile geometry with its video tiles replaced by the Spark-Reblock
+    leaves of one (batch, head) ([SPK-es] "Que cambia Spark-Attn", Spark-Reblock item).
+
+    Two queries are similar when their score patterns over the keys are: the
+    cosine of K q and K q' is the M-cosine q^T M q' / (|q|_M |q'|_M) with M the
+    keys' second moment.  A hierarchical splitter halves each group of m tiles
+    along its principal axis in that metric (the lower-projection 64 floor(m/2)
+    tokens form the left child) until every leaf holds one tile of 64 tokens: a
+    fixed tree shape of ceil(log2 Vt) levels, O(N log N) work.  Leaves are
+    numbered left to right; tokens ascending inside a leaf; key tiles reuse the
+    query partition.
+
+    split_hook(t0, m, toks, p, left, right) -> (left, right), if given, may replace
+    the split of a node (tests adopt another valid split where projections nearly
+    tie); toks are the group's tokens ascending, p their projections.
+    """
+    M = reblock_metric(Q, K, geom)
+    vt = np.sort(np.concatenate(geom.tiles[geom.n_prefix:]))
+    psi = reblock_features(Q[vt], M)
+    row_of = {int(t): i for i, t in enumerate(vt)}
+    leaves = [None] * geom.n_video
+
+    def split(toks, t0, m):
+        if m == 1:
+            leaves[t0] = toks
+            return
+        X = psi[[row_of[int(t)] for t in toks]]
+        p = principal_projection(X, M)
+        order = reblock_order(p, toks)
+        ml = reblock_left_tiles(m)
+        kl = TILE_TOKENS * ml
+        left, right = np.sort(toks[order[:kl]]), np.sort(toks[order[kl:]])
+        if split_hook is not None:
+            left, right = split_hook(t0, m, toks, p, left, right)
+        split(left, t0, ml)
+        split(right, t0 + ml, m - ml)
+
+    split(vt, 0, geom.n_video)
+    return Geometry(geom.n_tokens, list(geom.tiles[:geom.n_prefix]) + leaves, list(geom.tile_kind),
+                    geom.n_prefix, geom.n_video, geom.grid, geom.video_start)
 
 
 # --------------------------------------------------------------------------
@@ -484,11 +595,13 @@ def forward_head(Q, K, V, G, geom: Geometry, keep_percent: float, sink: int,
 def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
             select: int = SELECT_TOPK, coarse: int = COARSE_MEAN, tau: float = 0.0,
             heads=None, rows=None, list_override=None, want_intermediates=False,
-            extra_tokens: int = 0, fine: bool = True):
+            extra_tokens: int = 0, fine: bool = True, reblock: bool = False, split_hooks=None):
     """Oracle forward on bf16 bit arrays q, k, v, g ([B, N, H, D] uint16; g
     may be None).  Returns (O float64 [B, N, H, D] (NaN where not produced),
     {(b, h): intermediates}).  heads: iterable of (b, h) to run (None = all).
-    list_override: {(b, h): {query tile: tile ids}}.  fine=False: selection only."""
+    list_override: {(b, h): {query tile: tile ids}}.  fine=False: selection only.
+    reblock: Spark-Reblock video tiles per (b, h) (the intermediates then hold the
+    head's geometry under "geom"); split_hooks: {(b, h): split_hook}."""
     q, k, v, g = inputs["q"], inputs["k"], inputs["v"], inputs.get("g")
     B, N, H, D = q.shape
     T, Hh, W = grid
@@ -507,9 +620,15 @@ def forward(inputs: dict, segments, grid, keep_percent: float, sink: int,
             if not np.all(np.isfinite(arr)):
                 raise ValueError("inputs must be finite")
         lo = None if list_override is None else list_override.get((b, h))
-        O[b, :, h, :], it = forward_head(Qh, Kh, Vh, Gh, geom, keep_percent, sink, select,
+        gh = geom
+        if reblock:
+            hook = None if split_hooks is None else split_hooks.get((b, h))
+            gh = reblock_geometry(Qh, Kh, geom, hook)
+        O[b, :, h, :], it = forward_head(Qh, Kh, Vh, Gh, gh, keep_percent, sink, select,
                                          coarse, tau, rows=rows, list_override=lo,
                                          want_intermediates=want_intermediates,
                                          extra_tokens=extra_tokens, fine=fine)
+        if it is not None and reblock:
+            it["geom"] = gh
         inter[(b, h)] = it
     return O, inter

@@ -733,6 +733,243 @@ def check_extra_zero():
     assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------- Spark-Reblock
+# [SPK-es] "Que cambia Spark-Attn", Spark-Reblock item.  The pins below use float64
+# arrays handed straight to reblock_geometry (no bf16 rounding needed).
+RB_W = Workload("rb", 2, ((SEG_TEXT, 100), (SEG_REF_AUDIO, 30)), (8, 8, 12), 25.0, SINK_EXACT_KV,
+                seed=41, recipe="offset")       # 12 video tiles: groups of 3 occur
+
+
+def _rb_geom(w: Workload):
+    return O.map_geometry(w.segments(), *w.grid)
+
+
+def _video_ids(w: Workload):
+    vstart = [s0 for s0, n, kd in w.segments() if kd == SEG_VIDEO][0]
+    return vstart + np.arange(w.n_video)
+
+
+def _leaf_sets(g):
+    return [frozenset(t.tolist()) for t in g.tiles[g.n_prefix:]]
+
+
+def check_reblock_partition():
+    """The leaves partition the video tokens into tiles of exactly 64, ascending inside a
+    leaf; the prefix tiles are the fixed geometry's (segment-pure); a forward with reblock
+    reports each head's own partition."""
+    w = RB_W
+    x = make_inputs(w)
+    base = _rb_geom(w)
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, reblock=True, want_intermediates=True,
+                         fine=False)
+    vids = _video_ids(w)
+    seen = []
+    for (b, h), it in inter.items():
+        g = it["geom"]
+        assert g.n_video == base.n_video and g.n_prefix == base.n_prefix
+        for i in range(base.n_prefix):
+            assert np.array_equal(g.tiles[i], base.tiles[i]), f"h{h} prefix tile {i} changed"
+        leaves = g.tiles[g.n_prefix:]
+        assert all(len(t) == 64 and np.all(np.diff(t) > 0) for t in leaves)
+        assert np.array_equal(np.sort(np.concatenate(leaves)), vids), f"h{h}: leaves do not partition the video"
+        seen.append(_leaf_sets(g))
+    assert seen[0] != seen[1], "the partition must follow the head's own inputs"
+    assert seen[0] != _leaf_sets(base), "reblock left the fixed cubes in place"
+
+
+def _planted(rng, n_tok, centers, noise):
+    """Queries around planted centres: token i of a random order belongs to cluster i // 64."""
+    perm = rng.permutation(n_tok)
+    q = np.empty((n_tok, D))
+    for c, cen in enumerate(centers):
+        ids = perm[64 * c:64 * (c + 1)]
+        q[ids] = cen[None, :] + noise * rng.standard_normal((64, D))
+    return q, [frozenset(perm[64 * c:64 * (c + 1)].tolist()) for c in range(len(centers))]
+
+
+def _keys_with_moment(rng, n_tok, scales):
+    """Keys whose second moment is exactly diag(scales^2): orthonormal columns, rescaled."""
+    Qm, _ = np.linalg.qr(rng.standard_normal((n_tok, D)))
+    return Qm * math.sqrt(n_tok) * np.asarray(scales)[None, :]
+
+
+def _embed(w: Workload, qv, kv):
+    """Full-length Q, K with the video rows given and random prefix rows."""
+    rng = np.random.default_rng(5)
+    Q = rng.standard_normal((w.n_tokens, D))
+    K = rng.standard_normal((w.n_tokens, D))
+    vids = _video_ids(w)
+    Q[vids], K[vids] = qv, kv
+    return Q, K
+
+
+def check_reblock_planted_tree():
+    """Queries planted on a binary tree of 16 clusters (offsets 27, 9, 3, 1 along four
+    axes, small noise) with an isotropic key moment: the leaves are the 16 clusters."""
+    w = Workload("rb16", 1, ((SEG_TEXT, 64),), (4, 16, 16), 25.0, SINK_EXACT_KV, seed=1)
+    rng = np.random.default_rng(42)
+    cents = []
+    for c in range(16):
+        v = np.zeros(D)
+        v[0] = 100.0
+        for lvl, amp in enumerate((27.0, 9.0, 3.0, 1.0)):
+            v[1 + lvl] = amp * (1 if (c >> (3 - lvl)) & 1 else -1)
+        cents.append(v)
+    qv, groups = _planted(rng, w.n_video, cents, 0.05)
+    kv = _keys_with_moment(rng, w.n_video, np.ones(D))
+    Q, K = _embed(w, qv, kv)
+    g = O.reblock_geometry(Q, K, _rb_geom(w))
+    vids = _video_ids(w)
+    want = {frozenset((vids[list(gr)]).tolist()) for gr in groups}
+    assert set(_leaf_sets(g)) == want, "planted clusters not recovered"
+
+
+def check_reblock_metric():
+    """The metric is the keys' second moment: clusters split by 5 along e1 and by 1 along
+    e2, with key scales 0.1 (e1) and 10 (e2).  In the metric, e2 separates them by 10 and
+    e1 by 0.5, so the root split follows e2; in plain (or query-moment) geometry it would
+    follow e1."""
+    w = Workload("rb4", 1, ((SEG_TEXT, 64),), (4, 4, 16), 25.0, SINK_EXACT_KV, seed=1)
+    rng = np.random.default_rng(43)
+    cents = []
+    for s1 in (-1, 1):
+        for s2 in (-1, 1):
+            v = np.zeros(D)
+            v[0], v[1], v[2] = 10.0, 5.0 * s1, 1.0 * s2
+            cents.append(v)
+    qv, groups = _planted(rng, w.n_video, cents, 0.01)
+    scales = np.ones(D)
+    scales[1], scales[2] = 0.1, 10.0
+    kv = _keys_with_moment(rng, w.n_video, scales)
+    Q, K = _embed(w, qv, kv)
+    g = O.reblock_geometry(Q, K, _rb_geom(w))
+    vids = _video_ids(w)
+    leaves = _leaf_sets(g)
+    root_left = leaves[0] | leaves[1]
+    e2_neg = frozenset(vids[list(groups[0] | groups[2])].tolist())   # centres with s2 = -1
+    e2_pos = frozenset(vids[list(groups[1] | groups[3])].tolist())
+    assert root_left in (e2_neg, e2_pos), "the root split must follow the key metric (e2)"
+    assert set(leaves) == {frozenset(vids[list(gr)].tolist()) for gr in groups}
+
+
+def check_reblock_vs_eigh():
+    """One split with a dominant axis, against an independent formulation: explicit
+    whitening with the Cholesky factor of M, the top eigenvector of the centred
+    covariance (numpy eigh), and a sort by (projection, token)."""
+    w = Workload("rb2", 1, ((SEG_TEXT, 64),), (4, 4, 8), 25.0, SINK_EXACT_KV, seed=1)
+    rng = np.random.default_rng(44)
+    n = w.n_video
+    u = rng.standard_normal(D)
+    u[0] = 0.0
+    u /= np.linalg.norm(u)
+    qv = 10.0 * np.eye(D)[0][None, :] + 3.0 * rng.standard_normal((n, 1)) * u[None, :] \
+        + 0.15 * rng.standard_normal((n, D))
+    kv = _keys_with_moment(rng, n, rng.uniform(0.5, 2.0, size=D))   # anisotropic, well conditioned
+    Q, K = _embed(w, qv, kv)
+    g = O.reblock_geometry(Q, K, _rb_geom(w))
+    vids = _video_ids(w)
+    M = kv.T @ kv / n
+    L = np.linalg.cholesky(M)
+    phi = qv @ L
+    phi /= np.linalg.norm(phi, axis=1, keepdims=True)
+    C = np.cov(phi.T, bias=True)
+    evals, evecs = np.linalg.eigh(C)
+    top = evecs[:, -1]
+    assert evals[-1] > 20 * evals[-2]
+    proj = phi @ top
+    srt = np.sort(proj)
+    assert srt[64] - srt[63] > 1e-6, "pick a seed without a near tie at the median"
+    lower = frozenset(vids[np.argsort(proj)[:64]].tolist())
+    upper = frozenset(vids[np.argsort(proj)[64:]].tolist())
+    leaves = _leaf_sets(g)
+    assert set(leaves) == {lower, upper}, "split differs from the principal axis"
+
+
+def check_reblock_invariance():
+    """Cosine similarity in the key metric: scaling each query by its own positive factor,
+    or all keys by one factor, leaves the leaves unchanged; relabelling the video tokens
+    (Q and K rows permuted together) relabels the leaves and keeps their order."""
+    w = RB_W
+    x = make_inputs(w)
+    Q, K = as_f64(x["q"][0, :, 0]), as_f64(x["k"][0, :, 0])
+    base = _rb_geom(w)
+    ref = _leaf_sets(O.reblock_geometry(Q, K, base))
+    rng = np.random.default_rng(45)
+    Q2 = Q * rng.uniform(0.5, 2.0, size=(Q.shape[0], 1))
+    assert _leaf_sets(O.reblock_geometry(Q2, 3.0 * K, base)) == ref
+    vids = _video_ids(w)
+    perm = rng.permutation(len(vids))
+    Q3, K3 = Q.copy(), K.copy()
+    Q3[vids[perm]], K3[vids[perm]] = Q[vids], K[vids]     # token vids[i] moves to vids[perm[i]]
+    new_of = dict(zip(vids.tolist(), vids[perm].tolist()))
+    got = _leaf_sets(O.reblock_geometry(Q3, K3, base))
+    assert got == [frozenset(new_of[t] for t in leaf) for leaf in ref]
+
+
+def check_reblock_ties():
+    """Every video query equal: every projection ties, so each split keeps the lower token
+    ids on the left and the leaves are the video tokens in ascending runs of 64."""
+    w = RB_W
+    x = make_inputs(w)
+    Q, K = as_f64(x["q"][0, :, 0]), as_f64(x["k"][0, :, 0])
+    vids = _video_ids(w)
+    Q[vids] = Q[vids[0]]
+    g = O.reblock_geometry(Q, K, _rb_geom(w))
+    for j, leaf in enumerate(g.tiles[g.n_prefix:]):
+        assert np.array_equal(leaf, vids[64 * j:64 * (j + 1)]), f"leaf {j}"
+
+
+def check_reblock_split_sizes():
+    """Three planted clusters (three tiles) A = -4 e1, B = e1 + 2 e3, C = 3 e1 - 2 e3 (plus a
+    shared 20 e0): the root axis is mostly e1 with A lowest, so the left child is A alone
+    (floor(3/2) = 1 tile) and the right child {B, C} splits along its own axis, C first;
+    the leaves in tree order are A, C, B.  (A left child of ceil(3/2) tiles would be {A, B},
+    giving A, B, C; the upper half on the left would put C first.)"""
+    w = Workload("rb3", 1, ((SEG_TEXT, 64),), (4, 4, 12), 25.0, SINK_EXACT_KV, seed=1)
+    rng = np.random.default_rng(46)
+    cents = []
+    for c1, c3 in ((-4.0, 0.0), (1.0, 2.0), (3.0, -2.0)):
+        v = np.zeros(D)
+        v[0], v[1], v[3] = 20.0, c1, c3
+        cents.append(v)
+    qv, groups = _planted(rng, w.n_video, cents, 0.01)
+    kv = _keys_with_moment(rng, w.n_video, np.ones(D))
+    Q, K = _embed(w, qv, kv)
+    g = O.reblock_geometry(Q, K, _rb_geom(w))
+    vids = _video_ids(w)
+    want = [frozenset(vids[list(groups[i])].tolist()) for i in (0, 2, 1)]
+    assert _leaf_sets(g) == want, "leaves must be A, C, B"
+
+
+def check_reblock_forward():
+    """A forward on the reblocked tiles, rebuilt from independent pieces: pooled means of
+    each leaf, the coarse branch as torch sdpa on them, brute-force top-k, and every row's
+    output as sdpa over its listed tiles plus the gated coarse term."""
+    w = Workload("rbf", 2, ((SEG_TEXT, 64), (SEG_REF_AUDIO, 40)), (8, 8, 8), 25.0, SINK_EXACT_KV,
+                 seed=47, recipe="smooth")
+    x = make_inputs(w, with_gate=True)
+    out, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, reblock=True, want_intermediates=True)
+    for h in range(w.heads):
+        Q, K, V, G = (as_f64(x[n][0, :, h]) for n in "qkvg")
+        g = inter[(0, h)]["geom"]
+        P, tiles = g.n_prefix, g.tiles
+        pool = lambda X, ts: np.stack([X[t].sum(axis=0) / len(t) for t in ts])
+        qall = pool(Q, tiles)
+        kv, vv = pool(K, tiles[P:]), pool(V, tiles[P:])
+        S = qall @ kv.T / math.sqrt(D)
+        oc = torch_sdpa(qall, kv, vv)
+        k = O.keep_count(w.keep, g.n_video)
+        for i in range(len(tiles)):
+            pick = list(range(P)) + [P + j for j in brute_topk(list(S[i]), k)] if k < 8 else None
+            if pick is None:
+                order = sorted(range(g.n_video), key=lambda j: (-S[i, j], j))[:k]
+                pick = list(range(P)) + sorted(P + j for j in order)
+            assert list(inter[(0, h)]["lists"][i]) == pick, f"h{h} row {i}"
+            keys = np.concatenate([tiles[t] for t in pick])
+            ref = torch_sdpa(Q[tiles[i]], K[keys], V[keys]) + G[tiles[i]] * oc[i][None, :]
+            assert np.abs(out[0, tiles[i], h] - ref).max() < 1e-12, f"h{h} row {i} output"
+
+
 ALL_CHECKS = [
     ("geometry", lambda: (check_geometry(SMALL), check_geometry(SMALL_VIDEO_FIRST),
                           check_geometry(GEOM_3D))),
@@ -764,4 +1001,12 @@ ALL_CHECKS = [
     ("extra_choice", check_extra_choice),
     ("extra_ties", check_extra_ties),
     ("extra_zero", check_extra_zero),
+    ("reblock_partition", check_reblock_partition),
+    ("reblock_planted_tree", check_reblock_planted_tree),
+    ("reblock_metric", check_reblock_metric),
+    ("reblock_vs_eigh", check_reblock_vs_eigh),
+    ("reblock_invariance", check_reblock_invariance),
+    ("reblock_ties", check_reblock_ties),
+    ("reblock_split_sizes", check_reblock_split_sizes),
+    ("reblock_forward", check_reblock_forward),
 ]

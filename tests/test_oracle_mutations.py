@@ -15,7 +15,9 @@ from oracle import vsa_oracle as O
 _orig = {n: getattr(O, n) for n in ("softmax_scale", "map_geometry", "select_topk", "row_list",
                                       "logmass_bias", "coarse_branch", "tau_threshold",
                                       "keep_count", "pool_tiles", "fine_row", "weighted_summaries",
-                                      "key_candidates", "extra_tokens_for_row", "tau_rows")}
+                                      "key_candidates", "extra_tokens_for_row", "tau_rows",
+                                      "reblock_metric", "reblock_features", "principal_projection",
+                                      "reblock_order", "reblock_left_tiles")}
 
 
 def _geom_swapped_axes(segments, T, H, W):
@@ -130,6 +132,36 @@ def _extra_ties_high(qbar_i, K, geom, key_tiles, n_extra, scale):
     return np.sort(toks[order[:n_extra]])
 
 
+def _rb_identity_metric(Q, K, geom):
+    return np.eye(K.shape[1])
+
+
+def _rb_query_metric(Q, K, geom):
+    """The queries' own second moment instead of the keys' (the wrong side)."""
+    vt = np.concatenate(geom.tiles[geom.n_prefix:])
+    return Q[vt].T @ Q[vt] / len(vt)
+
+
+def _rb_inverse_metric(Q, K, geom):
+    return np.linalg.inv(_orig["reblock_metric"](Q, K, geom))
+
+
+def _uncentred_projection(X, M):
+    """Power steps on the group's uncentred second moment instead of its covariance."""
+    n = X.shape[0]
+    z = np.ones(X.shape[1])
+    for _ in range(_orig_steps()):
+        a = M @ z
+        a = a / math.sqrt(float(z @ a))
+        z = X.T @ (X @ a) / n
+    a = M @ z
+    return X @ (a / math.sqrt(float(z @ a)))
+
+
+def _orig_steps():
+    return O.REBLOCK_POWER_STEPS
+
+
 MUTATIONS = [
     ("scale_1_over_d", "softmax_scale", lambda d=128: 1.0 / d, "dense_equivalence"),
     ("tile_axes_swapped", "map_geometry", _geom_swapped_axes, "geometry"),
@@ -157,6 +189,15 @@ MUTATIONS = [
     ("extra_ignores_list_choice", "extra_tokens_for_row", _extra_ignores_list, "extra_choice"),
     ("extra_lowest", "extra_tokens_for_row", _extra_lowest, "extra_choice"),
     ("extra_ties_high", "extra_tokens_for_row", _extra_ties_high, "extra_ties"),
+    ("reblock_no_normalisation", "reblock_features", lambda qv, M: qv.copy(), "reblock_invariance"),
+    ("reblock_identity_metric", "reblock_metric", _rb_identity_metric, "reblock_metric"),
+    ("reblock_query_metric", "reblock_metric", _rb_query_metric, "reblock_metric"),
+    ("reblock_inverse_metric", "reblock_metric", _rb_inverse_metric, "reblock_metric"),
+    ("reblock_uncentred", "principal_projection", _uncentred_projection, "reblock_planted_tree"),
+    ("reblock_upper_half_left", "principal_projection",
+     lambda X, M: -_orig["principal_projection"](X, M), "reblock_split_sizes"),
+    ("reblock_left_ceil", "reblock_left_tiles", lambda m: m - m // 2, "reblock_split_sizes"),
+    ("reblock_ties_high", "reblock_order", lambda p, toks: np.lexsort((-toks, p)), "reblock_ties"),
 ]
 
 
