@@ -33,7 +33,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 SOURCES = ["vsa_plan.cpp", "vsa_forward.hip", "k_pool.hip", "k_coarse.hip", "k_select.hip", "k_extra.hip",
-           "k_fine.hip"]
+           "k_fine.hip", "k_reblock.hip"]
 # Per-file extras.  The fine kernel never sees a NaN (finite inputs; masked logits are -inf),
 # so fmaxf needs no quieting of signalling NaNs.
 EXTRA = {"k_fine.hip": ["-fno-honor-nans"]}

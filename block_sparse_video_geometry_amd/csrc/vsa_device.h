@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "vsa_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

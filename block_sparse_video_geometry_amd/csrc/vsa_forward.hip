@@ -134,6 +134,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   int* xcnt = reinterpret_cast<int*>(ws + L.xcnt);
   void* kx = ws + L.kx;
   void* vx = ws + L.vx;
+  void* o_user = o;
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   int rc = VSA_OK;
@@ -145,6 +146,25 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     if (e_ != hipSuccess) return hip_fail(name, e_);           \
   } while (0)
 
+  // Spark-Reblock: the mapper's leaves become the video tiles of each (b, h) by permuting the
+  // inputs' video rows; the rest of the forward runs on the permuted tensors and the output
+  // rows are scattered back at the end
+  const int* rb_tiles = nullptr;
+  if (G.reblock) {
+    VSA_STEP("reblock", rb_tiles = vsa_launch_reblock(
+                            G, q, k, reinterpret_cast<float*>(ws + L.rb_mpart), reinterpret_cast<float*>(ws + L.rb_m),
+                            reinterpret_cast<unsigned short*>(ws + L.rb_mhl), reinterpret_cast<float*>(ws + L.rb_norms),
+                            reinterpret_cast<int*>(ws + L.rb_list_a), reinterpret_cast<int*>(ws + L.rb_list_b),
+                            reinterpret_cast<float*>(ws + L.rb_pbuf), reinterpret_cast<float*>(ws + L.rb_part),
+                            reinterpret_cast<float*>(ws + L.rb_state), st));
+    void* gp = g != nullptr ? static_cast<void*>(ws + L.rb_g) : nullptr;
+    VSA_STEP("permute", vsa_launch_rb_permute(G, rb_tiles, q, k, v, g, ws + L.rb_q, ws + L.rb_k, ws + L.rb_v, gp, st));
+    q = ws + L.rb_q;
+    k = ws + L.rb_k;
+    v = ws + L.rb_v;
+    g = gp;
+    o = ws + L.rb_o;
+  }
   // with no sparse row (the dense mode) nothing is pooled, scored or selected
   if (G.Qs > 0) {
     VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
@@ -158,6 +178,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, st));
   }
   VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, kx, vx, xcnt, st));
+  if (G.reblock) VSA_STEP("unpermute", vsa_launch_rb_unpermute(G, rb_tiles, o, o_user, st));
 #undef VSA_STEP
   return VSA_OK;
 }

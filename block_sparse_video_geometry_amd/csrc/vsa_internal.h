@@ -41,12 +41,19 @@ struct VsaGeom {
                                            // row blocks x csplit
   int32_t csplit;                          // candidate-tile slices per row block (1: no merge)
   int32_t cchunks;                         // 64-tile chunks per slice
+  int32_t reblock;                         // 1: Spark-Reblock video tiles per (batch, head)
+  int32_t rb_nsplit;                       // tile ranges per (batch, head) of the key-moment sums
 };
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
   size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
   size_t cpart;               // coarse partials per (row, slice): max, sum, 2 pad, O[128]
+  // Spark-Reblock: key-moment partials and M (fp32, bf16 hi/lo), video-token norms, token
+  // lists (ping-pong; `tiles` is the final one), projections, pass partials, node states,
+  // and the permuted Q, K, V, G and the permuted output
+  size_t rb_mpart, rb_m, rb_mhl, rb_norms, rb_list_a, rb_list_b, rb_tiles, rb_pbuf, rb_part, rb_state;
+  size_t rb_q, rb_k, rb_v, rb_g, rb_o;
   size_t total;
 };
 
@@ -57,6 +64,12 @@ struct vsa_plan {
   float keep;
   int64_t n_tokens;
 };
+
+// Spark-Reblock tree shape (defined in k_reblock.hip): levels = ceil(log2 Vt); pass
+// workgroups per node at a level.
+int vsa_reblock_levels(int Vt);
+int vsa_reblock_chunks(int Vt, int level);
+constexpr int VSA_RB_STATE = 260;  // floats of a node state: mu[128], a[128], mu.a, pad
 
 // kernel launch sequence (defined in vsa_forward.hip)
 struct vsa_timer;

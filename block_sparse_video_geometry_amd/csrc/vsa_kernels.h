@@ -37,6 +37,16 @@ void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, 
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
                       const int* counts, int* xtok, int* xcnt, void* kx, void* vx, hipStream_t st);
 
+// Spark-Reblock mapper: M, norms and the tree levels; returns the final token list
+// ([batch, heads, Vt, 64] packed token ids, leaf j = video tile j).
+const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, float* mpart, float* M,
+                              unsigned short* mhl, float* norms, int* list_a, int* list_b, float* pbuf,
+                              float* part, float* state, hipStream_t st);
+// Q, K, V, G with each head's video rows permuted onto the reblocked tiles, and back for O.
+void vsa_launch_rb_permute(const VsaGeom& g, const int* tiles, const void* q, const void* k, const void* v,
+                           const void* gate, void* q2, void* k2, void* v2, void* g2, hipStream_t st);
+void vsa_launch_rb_unpermute(const VsaGeom& g, const int* tiles, const void* o2, void* o, hipStream_t st);
+
 // Block-sparse fine attention + gated combine, output in packed order; a sparse row's
 // staged extra tokens (kx, vx, xcnt; unused when the option is off) run as its first tile.
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,

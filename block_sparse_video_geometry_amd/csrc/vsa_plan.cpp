@@ -55,6 +55,8 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   if (o.extra_tokens < 0) return VSA_ERR_INVALID_ARGUMENT;
   if (o.extra_tokens > VSA_MAX_EXTRA) return VSA_ERR_UNSUPPORTED;
   if (dense_all && o.extra_tokens > 0) return VSA_ERR_UNSUPPORTED;  // no sparse row to take them
+  if (o.reblock != 0 && o.reblock != 1) return VSA_ERR_UNSUPPORTED;
+  if (o.reblock && (dense_all || o.extra_tokens > 0)) return VSA_ERR_UNSUPPORTED;
 
   // spans: sort by start, must partition [0, N)
   std::vector<Seg> s;
@@ -159,6 +161,8 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   g.select = o.select;
   g.coarse = o.coarse;
   g.tau = o.tau;
+  g.reblock = o.reblock;
+  g.rb_nsplit = o.reblock ? std::min(8, g.Vt) : 0;
   g.scale = (float)(1.0 / std::sqrt((double)VSA_HEAD_DIM));
   // The coarse kernel runs 64 rows per workgroup; with few row blocks per head the
   // candidate tiles are cut into slices of whole 64-tile chunks (each slice a workgroup,
@@ -200,6 +204,32 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   L.kx = take(xrows * heads * VSA_HEAD_DIM * 2);
   L.vx = take(xrows * heads * VSA_HEAD_DIM * 2);
   L.cpart = take(g.csplit > 1 ? BH * (size_t)g.Qs * g.csplit * (VSA_HEAD_DIM + 4) * 4 : 0);
+  {
+    const bool rb = g.reblock != 0;
+    const size_t Nv = (size_t)VSA_TILE_TOKENS * g.Vt;
+    const size_t DD = (size_t)VSA_HEAD_DIM * VSA_HEAD_DIM;
+    const int levels = rb ? vsa_reblock_levels(g.Vt) : 0;
+    size_t maxparts = 1;
+    for (int lv = 0; lv < levels; ++lv)
+      maxparts = std::max(maxparts, ((size_t)1 << lv) * (size_t)vsa_reblock_chunks(g.Vt, lv));
+    const size_t maxnodes = levels > 0 ? ((size_t)1 << (levels - 1)) : 1;
+    const size_t tb = (size_t)batch * N * heads * VSA_HEAD_DIM * 2;
+    L.rb_mpart = take(rb ? BH * g.rb_nsplit * DD * 4 : 0);
+    L.rb_m = take(rb ? BH * DD * 4 : 0);
+    L.rb_mhl = take(rb ? BH * 2 * DD * 2 : 0);
+    L.rb_norms = take(rb ? BH * Nv * 4 : 0);
+    L.rb_list_a = take(rb ? BH * Nv * 4 : 0);
+    L.rb_list_b = take(rb ? BH * Nv * 4 : 0);
+    L.rb_tiles = (levels % 2 == 0) ? L.rb_list_a : L.rb_list_b;
+    L.rb_pbuf = take(rb ? BH * Nv * 4 : 0);
+    L.rb_part = take(rb ? BH * maxparts * VSA_HEAD_DIM * 4 : 0);
+    L.rb_state = take(rb ? BH * maxnodes * VSA_RB_STATE * 4 : 0);
+    L.rb_q = take(rb ? tb : 0);
+    L.rb_k = take(rb ? tb : 0);
+    L.rb_v = take(rb ? tb : 0);
+    L.rb_g = take(rb ? tb : 0);
+    L.rb_o = take(rb ? tb : 0);
+  }
   L.total = off;
 
   p->opts = o;
@@ -251,6 +281,7 @@ extern "C" int vsa_debug_views(const vsa_plan* plan, vsa_debug* out) {
   out->counts = L.counts;
   out->xtok = L.xtok;
   out->xcnt = L.xcnt;
+  out->tiles = L.rb_tiles;
   out->total_bytes = L.total;
   return VSA_OK;
 }

@@ -34,7 +34,7 @@ class vsa_segment(C.Structure):
 
 class vsa_options(C.Structure):
     _fields_ = [("sink", C.c_int32), ("select", C.c_int32), ("coarse", C.c_int32),
-                ("tau", C.c_float), ("extra_tokens", C.c_int32)]
+                ("tau", C.c_float), ("extra_tokens", C.c_int32), ("reblock", C.c_int32)]
 
 
 class vsa_plan_desc(C.Structure):
@@ -57,7 +57,7 @@ class vsa_stats(C.Structure):
 class vsa_debug(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("qbar", "kbar", "vbar", "bias", "anchor", "scores",
                                            "ocoarse", "thr", "lists", "counts", "xtok", "xcnt",
-                                           "total_bytes")]
+                                           "tiles", "total_bytes")]
 
 
 class vsa_kernel_time(C.Structure):
@@ -151,13 +151,13 @@ def vsa_plan_geometry(segments, batch: int, video_T: int, video_H: int, video_W:
                       heads: int, head_dim: int = HEAD_DIM, keep_percent: float = 10.0,
                       sink: int = VSA_SINK_EXACT_KV, select: int = VSA_SELECT_TOPK,
                       coarse: int = VSA_COARSE_MEAN, tau: float = 0.0, use_options: bool = True,
-                      extra_tokens: int = 0) -> Plan:
+                      extra_tokens: int = 0, reblock: int = 0) -> Plan:
     """segments: iterable of (start, length, kind).  Raises VsaError on a bad layout."""
     segs = list(segments)
     arr = (vsa_segment * max(1, len(segs)))()
     for i, (s, n, kd) in enumerate(segs):
         arr[i] = vsa_segment(int(s), int(n), int(kd), 0)
-    opts = vsa_options(int(sink), int(select), int(coarse), float(tau), int(extra_tokens))
+    opts = vsa_options(int(sink), int(select), int(coarse), float(tau), int(extra_tokens), int(reblock))
     out = C.c_void_p()
     rc = _lib.vsa_plan_geometry(arr, len(segs), int(batch), int(video_T), int(video_H), int(video_W),
                                 int(heads), int(head_dim), float(keep_percent),
@@ -294,9 +294,12 @@ def debug_tensor(plan: Plan, workspace, field: str):
         "counts": (torch.int32, (B, H, Qs)),
         "xtok": (torch.int32, (B, H, Qs, 64)),
         "xcnt": (torch.int32, (B, H, Qs)),
+        "tiles": (torch.int32, (B, H, d.n_video_tiles, 64)),
     }[field]
     if field in ("xtok", "xcnt") and d.options.extra_tokens == 0:
         raise ValueError(f"{field}: the plan has no extra tokens (extra_tokens = 0)")
+    if field == "tiles" and d.options.reblock == 0:
+        raise ValueError("tiles: the plan has the fixed video tiles (reblock = 0)")
     dtype, shape = spec
     off = getattr(plan.debug, field)
     n = 1

@@ -145,6 +145,19 @@ typedef struct {
    * remain).  Dense rows take none.  > 64 is VSA_ERR_UNSUPPORTED, < 0
    * VSA_ERR_INVALID_ARGUMENT. */
   int32_t extra_tokens;
+  /* reblock ("Spark-H3: atencion dispersa por bloques acelera MiniMax-H3 en ComfyUI",
+   * "Que cambia Spark-Attn", Spark-Reblock item; reblock_layout=q_reuse_k in its
+   * "Flujos de trabajo"): 0 = the fixed 4x4x4 video tiles; 1 = an adaptive
+   * partition of each (batch, head)'s video tokens into 64-token tiles, computed
+   * on the GPU every forward.  M = mean over the video keys of k k^T; queries are
+   * compared by the cosine in the metric M (the cosine of their score patterns over
+   * the keys).  A group of m tiles splits along its principal axis (three power
+   * steps on the centred covariance of q / sqrt(q^T M q), from z = 1): the
+   * 64 floor(m/2) tokens lowest by (projection, token id) form its first floor(m/2)
+   * tiles.  Video tile j is then the tree's j-th leaf, tokens ascending; key tiles
+   * reuse the query partition; prefix tiles are unchanged.  Not with extra_tokens
+   * or the DENSE mode (VSA_ERR_UNSUPPORTED). */
+  int32_t reblock;
 } vsa_options;
 
 typedef struct vsa_plan vsa_plan; /* opaque, host-only, immutable after creation */
@@ -196,10 +209,11 @@ typedef struct {
  *   counts[batch, heads, Qs]        int32 valid entries of each list
  *   xtok  [batch, heads, Qs, 64]    int32 extra token ids, ascending (extra_tokens > 0)
  *   xcnt  [batch, heads, Qs]        int32 extra tokens of each sparse row
+ *   tiles [batch, heads, Vt, 64]    int32 packed token ids of each video tile (reblock = 1)
  * Sparse row s of a (batch, head) is query tile s + n_dense_rows. */
 typedef struct {
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts;
-  size_t xtok, xcnt;
+  size_t xtok, xcnt, tiles;
   size_t total_bytes;
 } vsa_debug;
 
@@ -209,7 +223,7 @@ typedef struct {
  * start inside), exactly one of kind VSA_SEG_VIDEO with length
  * video_T * video_H * video_W, each dim a multiple of 4, at most 16 prefix
  * spans.  keep_percent in (0, 100] is used in TOPK mode.  opts may be NULL
- * ({EXACT_KV, TOPK, MEAN, tau 0, extra_tokens 0}).  On success *out owns a new plan (free with
+ * ({EXACT_KV, TOPK, MEAN, tau 0, extra_tokens 0, reblock 0}).  On success *out owns a new plan (free with
  * vsa_plan_destroy); on error *out is NULL.  Host only, no device work. */
 int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch, int video_T, int video_H,
                       int video_W, int heads, int head_dim, float keep_percent,

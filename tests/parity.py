@@ -57,12 +57,14 @@ def gpu_results_to_numpy(plan, ws, o, fields=("scores", "lists", "counts", "qbar
 
 
 def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol_rel=TOL_REL,
-                 check_intermediates=True):
+                 check_intermediates=True, geoms=None):
     """Raise AssertionError on a mismatch; return a report dict.
 
     w: workload, x: input bit arrays, gpu: dict from gpu_results_to_numpy.
-    heads: (b, h) pairs to check (None = all); rows: query tile ids (None = all)."""
+    heads: (b, h) pairs to check (None = all); rows: query tile ids (None = all).
+    geoms: {(b, h): Geometry} per-head tiles (adaptive partitions), else the fixed tiles."""
     geom = O.map_geometry(w.segments(), *w.grid)
+    fixed_geom = geom
     sparse, dense = O.row_classes(geom, w.sink)
     n_dense = len(dense)
     P = 0 if w.sink == O.SINK_OFF else geom.n_prefix   # protected (always listed) tiles
@@ -78,6 +80,7 @@ def check_parity(w, x, gpu, heads=None, rows=None, gap=GAP, tol_abs=TOL_ABS, tol
                bias_mag=1.0)
     g_all = x.get("g")
     for b, h in heads:
+        geom = geoms[(b, h)] if geoms is not None else fixed_geom
         Q, K, V = (bits_to_f64(x[n][b, :, h]) for n in "qkv")
         G = bits_to_f64(g_all[b, :, h]) if g_all is not None else None
         _, it = O.forward_head(Q, K, V, G, geom, w.keep, w.sink, w.select, w.coarse, w.tau,
@@ -262,3 +265,50 @@ def check_lists(w, x, gpu, heads, gap=GAP):
             rep["rows"] += 1
     assert rep["max_s_err"] < 1e-5 * rep["s_mag"], f"coarse logits differ by {rep['max_s_err']:.3g}"
     return rep
+
+
+def check_reblock_tiles(w, x, gpu_tiles, heads, gap=GAP):
+    """The GPU's adaptive tiles against the oracle's tree, node by node from the root.
+
+    At a node the oracle sorts its tokens by projection; with p(k), p(k+1) the k-th and
+    (k+1)-th smallest (k = 64 floor(m/2)), where p(k+1) - p(k) > gap the GPU's left child
+    (the union of its leaves in the left tile range) must equal the oracle's exactly.
+    Elsewhere the GPU's split must be valid within gap (left projections <= p(k+1) + gap,
+    right ones >= p(k) - gap) and the oracle adopts it.  Returns ({(b, h): the oracle's
+    geometry with the adoptions}, report)."""
+    base = O.map_geometry(w.segments(), *w.grid)
+    rep = dict(nodes=0, exact_nodes=0, adopted_nodes=0, min_gap=np.inf)
+    geoms = {}
+    for b, h in heads:
+        Q, K = bits_to_f64(x["q"][b, :, h]), bits_to_f64(x["k"][b, :, h])
+        tiles = np.asarray(gpu_tiles[b, h], dtype=np.int64)
+
+        def hook(t0, m, toks, p, left, right, tiles=tiles, b=b, h=h):
+            ml = m // 2
+            gl = np.sort(tiles[t0:t0 + ml].ravel())
+            gr = np.sort(tiles[t0 + ml:t0 + m].ravel())
+            assert np.array_equal(np.sort(np.concatenate([gl, gr])), toks), \
+                f"(b{b},h{h}) node tiles [{t0},{t0 + m}): GPU tokens differ from the node's"
+            srt = np.sort(p)
+            kl = 64 * ml
+            pk, pk1 = srt[kl - 1], srt[kl]
+            rep["nodes"] += 1
+            rep["min_gap"] = min(rep["min_gap"], float(pk1 - pk))
+            if pk1 - pk > gap:
+                assert np.array_equal(gl, left), \
+                    f"(b{b},h{h}) node [{t0},{t0 + m}) split differs at gap {pk1 - pk:.3g}"
+                rep["exact_nodes"] += 1
+                return left, right
+            pos = {int(t): i for i, t in enumerate(toks)}
+            pl = p[[pos[int(t)] for t in gl]]
+            pr = p[[pos[int(t)] for t in gr]]
+            assert np.all(pl <= pk1 + gap) and np.all(pr >= pk - gap), \
+                f"(b{b},h{h}) node [{t0},{t0 + m}) GPU split invalid within {gap}"
+            rep["adopted_nodes"] += 1
+            return gl, gr
+
+        gh = O.reblock_geometry(Q, K, base, hook)
+        for j in range(base.n_video):
+            assert np.array_equal(gh.tiles[base.n_prefix + j], tiles[j]), f"(b{b},h{h}) leaf {j}"
+        geoms[(b, h)] = gh
+    return geoms, rep

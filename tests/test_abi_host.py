@@ -74,6 +74,11 @@ def plan_status(segs, batch=1, T=4, H=16, W=16, heads=2, hd=128, keep=25.0, **kw
     (dict(segs=GOOD, select=2, keep=0.0, sink=0, coarse=2), 0),       # ... ignores keep, sink, coarse
     (dict(segs=GOOD, select=2, extra_tokens=4), -2),                  # ... takes no extra tokens
     (dict(segs=GOOD, select=3), -2),
+    (dict(segs=GOOD, reblock=1), 0),                                  # adaptive video tiles
+    (dict(segs=GOOD, reblock=1, sink=0, select=1, tau=1.0, coarse=2), 0),
+    (dict(segs=GOOD, reblock=2), -2),
+    (dict(segs=GOOD, reblock=1, extra_tokens=8), -2),                 # not with extra tokens
+    (dict(segs=GOOD, reblock=1, select=2), -2),                       # nor the dense mode
     (dict(segs=GOOD, coarse=5), -2),
     (dict(segs=GOOD, coarse=2), 0),                                   # weighted summaries
     (dict(segs=GOOD, extra_tokens=64), 0),                            # extra tokens: 0 .. 64
@@ -228,6 +233,24 @@ def test_plan_agrees_with_oracle_geometry_on_random_layouts():
         assert d.k == k and d.list_capacity == pinned + k
         assert d.n_dense_rows == len(O.row_classes(geom, sink)[1])
     assert accepted > 100 and rejected > 50
+
+
+def test_reblock_workspace_and_tiles_view():
+    """With reblock the workspace also holds the mapper's buffers and the permuted
+    inputs and output (five tensors); the tiles view is [B, H, Vt, 64] and needs the option."""
+    torch = pytest.importorskip("torch")
+    w = WORKLOADS["full_reblock"]
+    p0 = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, w.keep, sink=w.sink)
+    p1 = V.vsa_plan_geometry(w.segments(), 1, *w.grid, w.heads, 128, w.keep, sink=w.sink, reblock=1)
+    tb = w.n_tokens * w.heads * 128 * 2
+    assert p1.workspace_bytes >= p0.workspace_bytes + 5 * tb
+    assert p1.desc.options.reblock == 1 and p0.desc.options.reblock == 0
+    small = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0, reblock=1)
+    ws = torch.empty(small.workspace_bytes, dtype=torch.uint8)
+    assert tuple(V.debug_tensor(small, ws, "tiles").shape) == (1, 2, 16, 64)
+    plain = V.vsa_plan_geometry(GOOD, 1, 4, 16, 16, 2, 128, 25.0)
+    with pytest.raises(ValueError):
+        V.debug_tensor(plain, torch.empty(plain.workspace_bytes, dtype=torch.uint8), "tiles")
 
 
 def test_extra_token_views_need_the_option():

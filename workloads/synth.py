@@ -55,6 +55,7 @@ class Workload:
     batch: int = 1
     video_first: bool = False   # put the video span before the prefix (edge case)
     extra: int = 0              # extra_tokens per sparse query tile (0: off)
+    reblock: int = 0            # 1: adaptive (Spark-Reblock) video tiles per (batch, head)
 
     @property
     def n_video(self) -> int:
@@ -116,6 +117,12 @@ WORKLOADS = {
     # the full workload's inputs plus 64 extra tokens per sparse query tile
     "full_extra64": Workload("full_extra64", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
                              SINK_EXACT_KV_AND_ROWS, seed=1003, recipe="scaled", extra=64),
+    # adaptive video tiles: on the full workload's inputs, and on the smooth inputs (whose
+    # queries cluster by 4x4x4 cube) at 20% keep
+    "full_reblock": Workload("full_reblock", 32, _FULL_PREFIX, _FULL_GRID, 10.0,
+                             SINK_EXACT_KV_AND_ROWS, seed=1003, recipe="scaled", reblock=1),
+    "full_smooth_reblock_20": Workload("full_smooth_reblock_20", 32, _FULL_PREFIX, _FULL_GRID, 20.0,
+                                       SINK_EXACT_KV_AND_ROWS, seed=1004, recipe="smooth", reblock=1),
 }
 
 
