@@ -145,7 +145,7 @@ def main():
     o = torch.empty_like(q)
     plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128,
                                w.keep if w.keep > 0 else 100.0, sink=w.sink, select=w.select,
-                               coarse=w.coarse, tau=w.tau, extra_tokens=w.extra)
+                               coarse=w.coarse, tau=w.tau, extra_tokens=w.extra, reblock=w.reblock)
     ws = V.alloc_workspace(plan)
     timer = V.Timer()
     stream = torch.cuda.current_stream()
@@ -257,7 +257,8 @@ def main():
         "config": {
             "workload": f"{w.name}: {H} heads x 128, prefix 512 text + 1536 ref-image + 256 ref-audio, "
                         f"video {w.grid[0]}x{w.grid[1]}x{w.grid[2]}, keep {w.keep:g}%, "
-                        f"{'exact_kv_and_rows' if w.sink == 2 else 'exact_kv'}",
+                        f"{'exact_kv_and_rows' if w.sink == 2 else 'exact_kv'}"
+                        f"{', adaptive (reblocked) video tiles' if w.reblock else ''}",
             "batch": w.batch, "n_tokens": N, "video_tokens": w.n_video, "heads": H, "head_dim": 128,
             "executed_pairs": stats["executed_pairs"], "dense_pairs": stats["dense_pairs"],
             "k": stats["k"],

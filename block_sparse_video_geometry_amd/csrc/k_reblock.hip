@@ -20,13 +20,16 @@
 //
 // Kernels (all per (batch, head), launched by vsa_launch_reblock):
 //   moment      k k^T over ranges of video tiles with bf16 MFMAs (products exact, fp32 sums)
-//   reduce      the ranges summed in a fixed order; M and its bf16 hi/lo split
-//   norm        |q|_M per video token with bf16 MFMAs against the hi/lo split of M; the
-//               level-0 token list (the video tokens ascending)
-//   per level:  pass(mean) finish  3 x [pass(power) finish]  pass(projection)  split
-//     pass      chunks of up to 2048 tokens of one node: sums of psi, or of
-//               (psi.a - mu.a)(psi - mu), or the projections psi.a
-//     finish    per node: the chunk sums added in a fixed order; mu, then a = M z / |z|_M
+//   reduce      the ranges summed in a fixed order; M, its bf16 hi/lo split, and the first
+//               direction a0 = M 1 / |1|_M (the same for every node: z starts at 1)
+//   norm        |q|_M per video token with bf16 MFMAs against the hi/lo split of M (staged
+//               in LDS, 512 tokens per workgroup); the level-0 token list (tokens ascending)
+//   per level:  pass(first) finish  2 x [pass(power) finish]  pass(projection)  split
+//     pass      chunks of up to 2048 tokens of one node.  first: the sums of psi and of
+//               (psi.a0) psi (then C a0 = those / n - mu (mu.a0), since the centred psi sum
+//               to zero); power: the sums of (psi.a - mu.a)(psi - mu); projection: psi.a
+//     finish    per node: the chunk sums added in chunk order, then z, a = M z / |z|_M
+//               and mu.a
 //     split     per node: the k-th smallest projection by an MSB radix search over
 //               order-preserving keys, then a stable partition (ties to the lower token)
 //   permute     Q, K, V, G with each head's video rows reordered so that fixed tile j of
@@ -102,10 +105,19 @@ __global__ __launch_bounds__(256) void vsa_rb_moment_kernel(VsaGeom g, const uns
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int tk = tid >> 3, d0 = 16 * (tid & 7);
+  u32x4 n0 = u32x4{0u, 0u, 0u, 0u}, n1 = n0;
+  if (j1 > j0) {
+    const unsigned short* row = kb + (size_t)(g.vstart + 64 * j0 + tk) * ts + d0;
+    n0 = *reinterpret_cast<const u32x4*>(row);
+    n1 = *reinterpret_cast<const u32x4*>(row + 8);
+  }
   for (int t = 64 * j0; t < 64 * j1; t += 32) {
-    const unsigned short* row = kb + (size_t)(g.vstart + t + tk) * ts + d0;
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(row);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(row + 8);
+    const u32x4 w0 = n0, w1 = n1;
+    if (t + 32 < 64 * j1) {  // the next chunk's rows, in flight during this chunk's MFMAs
+      const unsigned short* row = kb + (size_t)(g.vstart + t + 32 + tk) * ts + d0;
+      n0 = *reinterpret_cast<const u32x4*>(row);
+      n1 = *reinterpret_cast<const u32x4*>(row + 8);
+    }
     __syncthreads();  // the previous chunk's operand reads are done
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -137,14 +149,16 @@ __global__ __launch_bounds__(256) void vsa_rb_moment_kernel(VsaGeom g, const uns
 }
 
 // M = (sum of the ranges, in range order) / Nv, and its split M = hi + lo into two bf16
-// matrices (hi = M rounded to bf16, lo = the remainder rounded).
+// matrices (hi = M rounded to bf16, lo = the remainder rounded).  Workgroup (x, bh): rows
+// 8 x .. 8 x + 7 of M; the workgroup of row block 0 also leaves nothing else to do.
 __global__ __launch_bounds__(256) void vsa_rb_moment_reduce_kernel(VsaGeom g, const float* __restrict__ mpart,
                                                                    int nsplit, float* __restrict__ M,
                                                                    unsigned short* __restrict__ mhl) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   constexpr int DD = VSA_HEAD_DIM * VSA_HEAD_DIM;
   const float inv = 1.0f / (float)(VSA_TILE_TOKENS * g.Vt);
-  for (int e = threadIdx.x; e < DD; e += 256) {
+  for (int r = 0; r < 4; ++r) {
+    const int e = blockIdx.x * 1024 + r * 256 + threadIdx.x;
     float s = 0.f;
     for (int i = 0; i < nsplit; ++i) s += mpart[((size_t)bh * nsplit + i) * DD + e];
     s *= inv;
@@ -155,74 +169,121 @@ __global__ __launch_bounds__(256) void vsa_rb_moment_reduce_kernel(VsaGeom g, co
   }
 }
 
+// a0 = M 1 / sqrt(1^T M 1) per (b, h) (0 if that is 0): the first power step's direction.
+__global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_a0_kernel(const float* __restrict__ M, float* __restrict__ a0) {
+  __shared__ float red[2];
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
+  float av = 0.f;
+  for (int e = 0; e < VSA_HEAD_DIM; ++e) av += Mr[e];
+  const float za = wave_sum(av);
+  if ((d & 63) == 0) red[d >> 6] = za;
+  __syncthreads();
+  const float zat = red[0] + red[1];
+  a0[(size_t)bh * VSA_HEAD_DIM + d] = zat > 0.f ? av / sqrtf(zat) : 0.f;
+}
+
 // |q|_M = sqrt(q^T M q) of each video token, and the level-0 token list (video tokens
-// ascending).  Workgroup (x, bh): video offsets 64 x .. 64 x + 63, 16 per wave.
-// U = Q M with MFMA 16x16x32 (A = the wave's 16 tokens x 32 dims, contiguous; B = M rows by
-// symmetry, hi and lo parts), then q . u per token from the Q rows kept in LDS.
+// ascending).  Workgroup (x, bh): video offsets 512 x .. 512 x + 511, 16 per wave step.
+// M's hi and lo parts are staged in LDS once per workgroup.  U = Q M with MFMA 16x16x32
+// (A = 16 tokens x 32 dims, contiguous in global memory; B = rows of M by symmetry), then
+// q . u per token from the Q rows kept in LDS.
+constexpr int RB_NORM_TOKENS = 512;
+
 __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsigned short* __restrict__ q,
                                                           const unsigned short* __restrict__ mhl,
                                                           float* __restrict__ norms, int* __restrict__ list0) {
+  __shared__ __attribute__((aligned(16))) unsigned short ms[2][VSA_HEAD_DIM][VSA_HEAD_DIM + 8];
   __shared__ __attribute__((aligned(16))) unsigned short qs[4][16][VSA_HEAD_DIM + 8];
   const int bh = blockIdx.y;
   const int b = bh / g.heads, h = bh - b * g.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
   const int Nv = VSA_TILE_TOKENS * g.Vt;
-  const int off0 = 64 * blockIdx.x + 16 * wave;
-  const size_t ts = (size_t)g.heads * VSA_HEAD_DIM;
-  const unsigned short* qrow = q + ((size_t)b * g.N * g.heads + h) * VSA_HEAD_DIM + (size_t)(g.vstart + off0 + ql) * ts;
-  bf16x8 A[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * grp);
-    A[ks] = __builtin_bit_cast(bf16x8, w);
-    *reinterpret_cast<u32x4*>(&qs[wave][ql][32 * ks + 8 * grp]) = w;
-  }
   const unsigned short* Mh = mhl + (size_t)bh * 2 * VSA_HEAD_DIM * VSA_HEAD_DIM;
-  f32x4 acc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(
-            Mh + (size_t)part * VSA_HEAD_DIM * VSA_HEAD_DIM + (16 * nb + ql) * VSA_HEAD_DIM + 32 * ks + 8 * grp);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8, w), acc[nb], 0, 0, 0);
-      }
+  for (int i = tid; i < 2 * VSA_HEAD_DIM * 16; i += 256) {  // 16-byte pieces of M hi, lo
+    const int part = i >> 11, row = (i >> 4) & 127, c = i & 15;
+    *reinterpret_cast<u32x4*>(&ms[part][row][8 * c]) =
+        *reinterpret_cast<const u32x4*>(Mh + (size_t)part * VSA_HEAD_DIM * VSA_HEAD_DIM + row * VSA_HEAD_DIM + 8 * c);
   }
+  const int base = RB_NORM_TOKENS * blockIdx.x;
+  for (int i = tid; i < RB_NORM_TOKENS; i += 256)
+    if (base + i < Nv) list0[(size_t)bh * Nv + base + i] = g.vstart + base + i;
   __syncthreads();
-  // lane (grp, ql) holds U[token 4 grp + i][dim 16 nb + ql]
-  float part[4];
+  const size_t ts = (size_t)g.heads * VSA_HEAD_DIM;
+  const unsigned short* qh = q + ((size_t)b * g.N * g.heads + h) * VSA_HEAD_DIM;
+  u32x4 nq[4];
+  {
+    const int off0 = base + 16 * wave;
+    if (off0 < Nv) {
+      const unsigned short* qrow = qh + (size_t)(g.vstart + off0 + ql) * ts;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    part[i] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      part[i] += __uint_as_float((unsigned)qs[wave][4 * grp + i][16 * nb + ql] << 16) * acc[nb][i];
-    part[i] = row16_sum(part[i]);
+      for (int ks = 0; ks < 4; ++ks) nq[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * grp);
+    }
   }
-  if (ql == 0) {
+  for (int step = 0; step < RB_NORM_TOKENS / 64; ++step) {
+    const int off0 = base + 64 * step + 16 * wave;  // the wave's 16 tokens (wave-uniform)
+    if (off0 >= Nv) break;
+    bf16x8 A[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) norms[(size_t)bh * Nv + off0 + 4 * grp + i] = sqrtf(fmaxf(part[i], 0.f));
+    for (int ks = 0; ks < 4; ++ks) {
+      A[ks] = __builtin_bit_cast(bf16x8, nq[ks]);
+      *reinterpret_cast<u32x4*>(&qs[wave][ql][32 * ks + 8 * grp]) = nq[ks];
+    }
+    if (step + 1 < RB_NORM_TOKENS / 64 && off0 + 64 < Nv) {  // the next step's rows, in flight
+      const unsigned short* qrow = qh + (size_t)(g.vstart + off0 + 64 + ql) * ts;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) nq[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * grp);
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&ms[part][16 * nb + ql][32 * ks + 8 * grp]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], __builtin_bit_cast(bf16x8, w), acc[nb], 0, 0, 0);
+        }
+    }
+    // the wave's own Q rows in qs: written above and read below by this wave (LDS keeps a
+    // wave's accesses in order; the barrier keeps the compiler from moving them)
+    __builtin_amdgcn_wave_barrier();
+    // lane (grp, ql) holds U[token 4 grp + i][dim 16 nb + ql]
+    float part[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      part[i] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        part[i] += __uint_as_float((unsigned)qs[wave][4 * grp + i][16 * nb + ql] << 16) * acc[nb][i];
+      part[i] = row16_sum(part[i]);
+    }
+    if (ql == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) norms[(size_t)bh * Nv + off0 + 4 * grp + i] = sqrtf(fmaxf(part[i], 0.f));
+    }
+    __builtin_amdgcn_wave_barrier();  // qs is rewritten by the next step
   }
-  if (tid < 64) list0[(size_t)bh * Nv + 64 * blockIdx.x + tid] = g.vstart + 64 * blockIdx.x + tid;
 }
 
 // ---------------------------------------------------------------- per-level passes
-// MODE 0: sums of psi; 1: sums of (psi.a - mu.a)(psi - mu); 2: projections psi.a to pbuf.
-// Workgroup (x, bh): node x / cpn, positions [2048 c, 2048 c + 2048) of it (c = x % cpn).
-// 16 lanes per token (8 dims each), 16 tokens per step.
+// MODE 0 (first power step): sums of psi and of (psi.a0) psi; 1 (later power steps): sums of
+// (psi.a - mu.a)(psi - mu); 2: projections psi.a to pbuf.  Workgroup (x, bh): node x / cpn,
+// positions [2048 c, 2048 c + 2048) of it (c = x % cpn).  16 lanes per token (8 dims each),
+// 16 tokens per step, eight steps' loads in flight.
 constexpr int RB_CH = 2048;
+constexpr int RB_PART = 2 * VSA_HEAD_DIM;  // floats per chunk partial
 
 template <int MODE>
 __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsigned short* __restrict__ q,
                                                           const float* __restrict__ norms,
                                                           const int* __restrict__ list,
                                                           const float* __restrict__ state,
+                                                          const float* __restrict__ a0,
                                                           float* __restrict__ part, float* __restrict__ pbuf,
                                                           int level, int cpn) {
-  __shared__ float red[16][VSA_HEAD_DIM];
+  __shared__ float red[16][RB_PART];
   const int bh = blockIdx.y;
   const int b = bh / g.heads, h = bh - b * g.heads;
   const int node = blockIdx.x / cpn, c = blockIdx.x - node * cpn;
@@ -232,77 +293,80 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
   const int n = VSA_TILE_TOKENS * m;
   const int lo = c * RB_CH, hi = min(n, lo + RB_CH);
   const int tid = threadIdx.x, l16 = tid & 15, slot = tid >> 4;
-  float* pp = part + ((size_t)bh * gridDim.x + blockIdx.x) * VSA_HEAD_DIM;
+  float* pp = part + ((size_t)bh * gridDim.x + blockIdx.x) * RB_PART;
   if (m < 2 || lo >= hi) {
-    if (MODE != 2 && tid < VSA_HEAD_DIM) pp[tid] = 0.f;
+    if (MODE != 2)
+      for (int i = tid; i < RB_PART; i += 256) pp[i] = 0.f;
     return;
   }
   const float* st = state + ((size_t)bh * (1 << level) + node) * RB_STATE;
   float a[8], mu[8], mua = 0.f;
-  if (MODE != 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      a[e] = st[VSA_HEAD_DIM + 8 * l16 + e];
-      mu[e] = st[8 * l16 + e];
-    }
-    mua = st[2 * VSA_HEAD_DIM];
+  for (int e = 0; e < 8; ++e) {
+    a[e] = MODE == 0 ? a0[(size_t)bh * VSA_HEAD_DIM + 8 * l16 + e] : st[VSA_HEAD_DIM + 8 * l16 + e];
+    mu[e] = MODE == 1 ? st[8 * l16 + e] : 0.f;
   }
+  if (MODE == 1) mua = st[2 * VSA_HEAD_DIM];
   const size_t ts = (size_t)g.heads * VSA_HEAD_DIM;
   const unsigned short* qb = q + ((size_t)b * g.N * g.heads + h) * VSA_HEAD_DIM + 8 * l16;
   const int* lst = list + (size_t)bh * Nv + VSA_TILE_TOKENS * t0;
   const float* nrm = norms + (size_t)bh * Nv - g.vstart;
-  float acc[8];
+  float acc[8], acc2[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int i0 = lo + slot; i0 < hi; i0 += 64) {
-    // four tokens in flight per lane
-    int tok[4];
-    u32x4 w[4];
-    float nv[4];
+  for (int e = 0; e < 8; ++e) acc[e] = acc2[e] = 0.f;
+  constexpr int U = 8;
+  for (int i0 = lo + slot; i0 < hi; i0 += 16 * U) {
+    int tok[U];
+    u32x4 w[U];
+    float nv[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + 16 * u;
       // list entries are video tokens; the clamp only keeps every address inside the tensors
       tok[u] = i < hi ? min(max(lst[i], g.vstart), g.vstart + Nv - 1) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (tok[u] >= 0) {
         w[u] = *reinterpret_cast<const u32x4*>(qb + (size_t)tok[u] * ts);
         nv[u] = nrm[tok[u]];
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (tok[u] < 0) continue;
       float x[8];
       unpack8(w[u], x);
       const float inv = nv[u] > 0.f ? 1.0f / nv[u] : 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= inv;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(x[e], a[e], d);
+      d = row16_sum(d);
       if (MODE == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[e];
-      } else {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(x[e], a[e], d);
-        d = row16_sum(d);
-        if (MODE == 1) {
-          const float cc = d - mua;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fmaf(cc, x[e] - mu[e], acc[e]);
-        } else if (l16 == 0) {
-          pbuf[(size_t)bh * Nv + VSA_TILE_TOKENS * t0 + i0 + 16 * u] = d;
+        for (int e = 0; e < 8; ++e) {
+          acc[e] += x[e];
+          acc2[e] = fmaf(d, x[e], acc2[e]);
         }
+      } else if (MODE == 1) {
+        const float cc = d - mua;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(cc, x[e] - mu[e], acc[e]);
+      } else if (l16 == 0) {
+        pbuf[(size_t)bh * Nv + VSA_TILE_TOKENS * t0 + i0 + 16 * u] = d;
       }
     }
   }
   if (MODE == 2) return;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[slot][8 * l16 + e] = acc[e];
+  for (int e = 0; e < 8; ++e) {
+    red[slot][8 * l16 + e] = acc[e];
+    red[slot][VSA_HEAD_DIM + 8 * l16 + e] = acc2[e];
+  }
   __syncthreads();
-  if (tid < VSA_HEAD_DIM) {
+  {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += red[i][tid];
@@ -310,34 +374,44 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
   }
 }
 
-// Per node: the chunk sums added in chunk order, divided by n: mu (after the mean pass, with
-// z = 1) or z (after a power pass); then a = M z / |z|_M (0 if |z|_M = 0) and mu . a.
+// One node per workgroup (128 threads, one per dim).  The chunk sums added in chunk order and
+// divided by n; after the first pass mu = sum psi / n and z = C a0 = sum (psi.a0) psi / n -
+// mu (mu.a0); after a later pass z = sum / n.  Then a = M z / |z|_M (0 if |z|_M = 0; M rows
+// read from L2) and mu . a go to the node state.
 __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, const float* __restrict__ M,
+                                                                     const float* __restrict__ a0,
                                                                      const float* __restrict__ part,
                                                                      float* __restrict__ state, int level,
-                                                                     int cpn, int after_mean) {
+                                                                     int cpn, int first) {
   __shared__ float zs[VSA_HEAD_DIM];
-  __shared__ float red[2][2];
+  __shared__ float red[3][2];
   const int bh = blockIdx.y, node = blockIdx.x;
   int t0, m;
   node_range(g.Vt, level, node, t0, m);
   if (m < 2) return;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, wave = d >> 6;
+  const int nodes = 1 << level;
   const float inv_n = 1.0f / (float)(VSA_TILE_TOKENS * m);
-  const float* pp = part + ((size_t)bh * (1 << level) * cpn + (size_t)node * cpn) * VSA_HEAD_DIM;
-  float v = 0.f;
-  for (int c = 0; c < cpn; ++c) v += pp[(size_t)c * VSA_HEAD_DIM + d];
-  v *= inv_n;
-  float* st = state + ((size_t)bh * (1 << level) + node) * RB_STATE;
-  float mu;
-  if (after_mean) {
-    mu = v;
+  const float* pp = part + ((size_t)bh * nodes * cpn + (size_t)node * cpn) * RB_PART;
+  float* st = state + ((size_t)bh * nodes + node) * RB_STATE;
+  float v = 0.f, v2 = 0.f;
+  for (int c = 0; c < cpn; ++c) {
+    v += pp[(size_t)c * RB_PART + d];
+    if (first) v2 += pp[(size_t)c * RB_PART + VSA_HEAD_DIM + d];
+  }
+  float mu, z;
+  if (first) {
+    mu = v * inv_n;
+    const float ma0 = wave_sum(mu * a0[(size_t)bh * VSA_HEAD_DIM + d]);
+    if ((d & 63) == 0) red[0][wave] = ma0;
+    __syncthreads();
+    z = v2 * inv_n - mu * (red[0][0] + red[0][1]);
     st[d] = mu;
-    zs[d] = 1.0f;
   } else {
     mu = st[d];
-    zs[d] = v;
+    z = v * inv_n;
   }
+  zs[d] = z;
   __syncthreads();
   const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
   float av = 0.f;
@@ -349,17 +423,17 @@ __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, 
     av = fmaf(mr[2], zs[e + 2], av);
     av = fmaf(mr[3], zs[e + 3], av);
   }
-  const float za = wave_sum(zs[d] * av);
-  if ((d & 63) == 0) red[0][d >> 6] = za;
+  const float za = wave_sum(z * av);
+  if ((d & 63) == 0) red[1][wave] = za;
   __syncthreads();
-  const float zat = red[0][0] + red[0][1];
+  const float zat = red[1][0] + red[1][1];
   const float sc = zat > 0.f ? 1.0f / sqrtf(zat) : 0.f;
   av *= sc;
   const float ma = wave_sum(mu * av);
-  if ((d & 63) == 0) red[1][d >> 6] = ma;
+  if ((d & 63) == 0) red[2][wave] = ma;
   __syncthreads();
   st[VSA_HEAD_DIM + d] = av;
-  if (d == 0) st[2 * VSA_HEAD_DIM] = red[1][0] + red[1][1];
+  if (d == 0) st[2 * VSA_HEAD_DIM] = red[2][0] + red[2][1];
 }
 
 // Per node: the split.  k = 64 floor(m/2); the k-th smallest key T by a four-round 8-bit MSB
@@ -544,31 +618,36 @@ int vsa_reblock_chunks(int Vt, int level) {
 }
 
 const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, float* mpart, float* M,
-                              unsigned short* mhl, float* norms, int* list_a, int* list_b, float* pbuf,
+                              unsigned short* mhl, float* a0, float* norms, int* list_a, int* list_b, float* pbuf,
                               float* part, float* state, hipStream_t st) {
   const int BH = g.batch * g.heads;
   const int nsplit = g.rb_nsplit;
+  const int Nv = VSA_TILE_TOKENS * g.Vt;
+  const unsigned short* qs = (const unsigned short*)q;
   hipLaunchKernelGGL(vsa_rb_moment_kernel, dim3(nsplit, BH), dim3(256), 0, st, g, (const unsigned short*)k, mpart,
                      nsplit);
-  hipLaunchKernelGGL(vsa_rb_moment_reduce_kernel, dim3(BH), dim3(256), 0, st, g, mpart, nsplit, M, mhl);
-  hipLaunchKernelGGL(vsa_rb_norm_kernel, dim3(g.Vt, BH), dim3(256), 0, st, g, (const unsigned short*)q, mhl, norms,
-                     list_a);
+  hipLaunchKernelGGL(vsa_rb_moment_reduce_kernel, dim3(VSA_HEAD_DIM * VSA_HEAD_DIM / 1024, BH), dim3(256), 0, st, g,
+                     mpart, nsplit, M, mhl);
+  hipLaunchKernelGGL(vsa_rb_a0_kernel, dim3(BH), dim3(VSA_HEAD_DIM), 0, st, (const float*)M, a0);
+  hipLaunchKernelGGL(vsa_rb_norm_kernel, dim3((Nv + RB_NORM_TOKENS - 1) / RB_NORM_TOKENS, BH), dim3(256), 0, st, g,
+                     qs, mhl, norms, list_a);
   int* src = list_a;
   int* dst = list_b;
   const int levels = vsa_reblock_levels(g.Vt);
   for (int L = 0; L < levels; ++L) {
     const int cpn = vsa_reblock_chunks(g.Vt, L);
     const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH);
-    hipLaunchKernelGGL(vsa_rb_pass_kernel<0>, pgrid, dim3(256), 0, st, g, (const unsigned short*)q, norms, src, state,
-                       part, pbuf, L, cpn);
-    hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, part, state, L, cpn, 1);
-    for (int s = 0; s < RB_STEPS; ++s) {
-      hipLaunchKernelGGL(vsa_rb_pass_kernel<1>, pgrid, dim3(256), 0, st, g, (const unsigned short*)q, norms, src,
-                         state, part, pbuf, L, cpn);
-      hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, part, state, L, cpn, 0);
+    // power step 1 (z from 1: the direction a0 is the head's), steps 2 .. RB_STEPS
+    hipLaunchKernelGGL(vsa_rb_pass_kernel<0>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
+                       cpn);
+    hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 1);
+    for (int s = 1; s < RB_STEPS; ++s) {
+      hipLaunchKernelGGL(vsa_rb_pass_kernel<1>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
+                         cpn);
+      hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 0);
     }
-    hipLaunchKernelGGL(vsa_rb_pass_kernel<2>, pgrid, dim3(256), 0, st, g, (const unsigned short*)q, norms, src, state,
-                       part, pbuf, L, cpn);
+    hipLaunchKernelGGL(vsa_rb_pass_kernel<2>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
+                       cpn);
     hipLaunchKernelGGL(vsa_rb_split_kernel, ngrid, dim3(1024), 0, st, g, pbuf, src, dst, L);
     int* t = src;
     src = dst;

@@ -153,7 +153,8 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   if (G.reblock) {
     VSA_STEP("reblock", rb_tiles = vsa_launch_reblock(
                             G, q, k, reinterpret_cast<float*>(ws + L.rb_mpart), reinterpret_cast<float*>(ws + L.rb_m),
-                            reinterpret_cast<unsigned short*>(ws + L.rb_mhl), reinterpret_cast<float*>(ws + L.rb_norms),
+                            reinterpret_cast<unsigned short*>(ws + L.rb_mhl), reinterpret_cast<float*>(ws + L.rb_a0),
+                            reinterpret_cast<float*>(ws + L.rb_norms),
                             reinterpret_cast<int*>(ws + L.rb_list_a), reinterpret_cast<int*>(ws + L.rb_list_b),
                             reinterpret_cast<float*>(ws + L.rb_pbuf), reinterpret_cast<float*>(ws + L.rb_part),
                             reinterpret_cast<float*>(ws + L.rb_state), st));

@@ -52,7 +52,7 @@ struct VsaLayout {        // byte offsets into the workspace
   // Spark-Reblock: key-moment partials and M (fp32, bf16 hi/lo), video-token norms, token
   // lists (ping-pong; `tiles` is the final one), projections, pass partials, node states,
   // and the permuted Q, K, V, G and the permuted output
-  size_t rb_mpart, rb_m, rb_mhl, rb_norms, rb_list_a, rb_list_b, rb_tiles, rb_pbuf, rb_part, rb_state;
+  size_t rb_mpart, rb_m, rb_mhl, rb_a0, rb_norms, rb_list_a, rb_list_b, rb_tiles, rb_pbuf, rb_part, rb_state;
   size_t rb_q, rb_k, rb_v, rb_g, rb_o;
   size_t total;
 };

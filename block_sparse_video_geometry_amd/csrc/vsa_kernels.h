@@ -40,7 +40,7 @@ void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const floa
 // Spark-Reblock mapper: M, norms and the tree levels; returns the final token list
 // ([batch, heads, Vt, 64] packed token ids, leaf j = video tile j).
 const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, float* mpart, float* M,
-                              unsigned short* mhl, float* norms, int* list_a, int* list_b, float* pbuf,
+                              unsigned short* mhl, float* a0, float* norms, int* list_a, int* list_b, float* pbuf,
                               float* part, float* state, hipStream_t st);
 // Q, K, V, G with each head's video rows permuted onto the reblocked tiles, and back for O.
 void vsa_launch_rb_permute(const VsaGeom& g, const int* tiles, const void* q, const void* k, const void* v,

@@ -162,7 +162,7 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   g.coarse = o.coarse;
   g.tau = o.tau;
   g.reblock = o.reblock;
-  g.rb_nsplit = o.reblock ? std::min(8, g.Vt) : 0;
+  g.rb_nsplit = o.reblock ? std::min(32, g.Vt) : 0;
   g.scale = (float)(1.0 / std::sqrt((double)VSA_HEAD_DIM));
   // The coarse kernel runs 64 rows per workgroup; with few row blocks per head the
   // candidate tiles are cut into slices of whole 64-tile chunks (each slice a workgroup,
@@ -217,12 +217,13 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     L.rb_mpart = take(rb ? BH * g.rb_nsplit * DD * 4 : 0);
     L.rb_m = take(rb ? BH * DD * 4 : 0);
     L.rb_mhl = take(rb ? BH * 2 * DD * 2 : 0);
+    L.rb_a0 = take(rb ? BH * VSA_HEAD_DIM * 4 : 0);
     L.rb_norms = take(rb ? BH * Nv * 4 : 0);
     L.rb_list_a = take(rb ? BH * Nv * 4 : 0);
     L.rb_list_b = take(rb ? BH * Nv * 4 : 0);
     L.rb_tiles = (levels % 2 == 0) ? L.rb_list_a : L.rb_list_b;
     L.rb_pbuf = take(rb ? BH * Nv * 4 : 0);
-    L.rb_part = take(rb ? BH * maxparts * VSA_HEAD_DIM * 4 : 0);
+    L.rb_part = take(rb ? BH * maxparts * 2 * VSA_HEAD_DIM * 4 : 0);
     L.rb_state = take(rb ? BH * maxnodes * VSA_RB_STATE * 4 : 0);
     L.rb_q = take(rb ? tb : 0);
     L.rb_k = take(rb ? tb : 0);
