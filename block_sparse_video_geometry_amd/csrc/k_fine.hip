@@ -70,19 +70,29 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
 // Direct buffer -> LDS copy of 16 bytes per lane: lane i of the wave writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16) with the 16 bytes at buffer offset soff + voff (zero when
-// out of the resource's range).  Issued from asm so the compiler neither inserts its own
-// (whole-queue) waits for the LDS write nor moves LDS reads across it; completion is
-// tracked with vmcnt by the waits below.  No register results, so nothing is left pending
-// in a VGPR.  M0 is used by nothing else in this kernel, so it is set here and not restored.
+// [M0 + IMM + 16 i, +16) with the 16 bytes at buffer offset soff + voff + IMM (zero when out
+// of the resource's range): the immediate offset moves both addresses.  Four consecutive
+// copies into consecutive 1 KB rows of a buffer therefore share one M0 value (the first of
+// the four sets it, SET_M0) and differ by IMM = 0, 1024, 2048, 3072, the caller taking IMM
+// off soff.  Issued from asm so the compiler neither inserts its own (whole-queue) waits
+// for the LDS write nor moves LDS reads across it; completion is tracked with vmcnt by the
+// waits below.  No register results, so nothing is left pending in a VGPR.  M0 is used by
+// nothing else in this kernel, so it is set here and not restored.
+template <int IMM, bool SET_M0>
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, unsigned lds) {
-  asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
-      : "memory");
+  if (SET_M0)
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
+        :
+        : "v"(voff), "s"(rs), "s"(soff), "s"(lds), "n"(IMM)
+        : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(soff), "n"(IMM)
+                 : "memory");
 }
 // Wait until at most N vector-memory operations of this wave are outstanding; also a
 // compiler memory barrier, so LDS reads stay after it.
@@ -282,11 +292,27 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     stp = (flags & 1) ? plane : 16 * rowbytes;
     stl = (flags & 1) ? line : 4 * rowbytes;
   };
+  // Copy n writes LDS rows 4n .. 4n + 3 (1 KB at buffer + 1024 n): M0 = buffer + 4096 (n >> 2)
+  // is set by copy 4 (n >> 2) and the immediate 1024 (n & 3) reaches the row, so soff takes
+  // that immediate off again.  (stl >= 4 row bytes >= 1 KB, so soff stays non-negative, and
+  // an out-of-range tile offset stays out of range.)
+  // (n is a constant once the loops around the calls are unrolled, so the switch folds away.)
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, unsigned vo, int n, unsigned off, unsigned stp, unsigned stl,
+                 unsigned buf) {
+    const unsigned so = off + (unsigned)(n >> 2) * stp + (unsigned)(n & 3) * (stl - 1024u);
+    const unsigned lds = buf + 4096u * (unsigned)(n >> 2);
+    switch (n & 3) {
+      case 0: bdma16<0, true>(rs, vo, so, lds); break;
+      case 1: bdma16<1024, false>(rs, vo, so, lds); break;
+      case 2: bdma16<2048, false>(rs, vo, so, lds); break;
+      default: bdma16<3072, false>(rs, vo, so, lds); break;
+    }
+  };
   auto kdma_r = [&](__amdgpu_buffer_rsrc_t rs, int n, unsigned off, unsigned stp, unsigned stl) {
-    bdma16(rs, koff[(n >> 1) & 3], off + (n >> 2) * stp + (n & 3) * stl, kbuf_u + 1024 * n);
+    dma(rs, koff[(n >> 1) & 3], n, off, stp, stl, kbuf_u);
   };
   auto vdma_r = [&](__amdgpu_buffer_rsrc_t rs, int n, unsigned off, unsigned stp, unsigned stl) {
-    bdma16(rs, voff[(n >> 1) & 1], off + (n >> 2) * stp + (n & 3) * stl, vbuf_u + 1024 * n);
+    dma(rs, voff[(n >> 1) & 1], n, off, stp, stl, vbuf_u);
   };
   auto kdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { kdma_r(krs, n, off, stp, stl); };
   auto vdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { vdma_r(vrs, n, off, stp, stl); };
@@ -525,23 +551,42 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) asel[qb][i] = ql == 4 * grp + i ? alpha[qb] : 0.f;
-      // The B operands are read out of the accumulator file by explicit moves inside this
-      // branch (the compiler would otherwise copy all 128 accumulators on every iteration);
-      // the NOPs cover the MFMA-result-to-VALU-read latency for those moves.
+      // Per (db, qb) block one asm sequence: O's four accumulator values are moved to four
+      // distinct VGPRs, then the four MFMAs, with explicit waits (the compiler sees none of
+      // these instructions): after the moves before the MFMAs read them, between the
+      // dependent MFMAs, and at the end so that no later write reaches a register an MFMA
+      // may still be reading.  The whole rescale is rare, so the waits cost nothing.
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
-          float ob[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ob[i] = acc_read(oacc[db][qb][i]);
-          f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][0], ob[0], zero4, 0, 0, 0);
-#pragma unroll
-          for (int i = 1; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(asel[qb][i], ob[i], acc, 0, 0, 0);
+          f32x4 acc;
+          float t0, t1, t2, t3;
+          asm volatile(
+              "v_accvgpr_read_b32 %[t0], %[o0]\n\t"
+              "v_accvgpr_read_b32 %[t1], %[o1]\n\t"
+              "v_accvgpr_read_b32 %[t2], %[o2]\n\t"
+              "v_accvgpr_read_b32 %[t3], %[o3]\n\t"
+              "s_nop 4\n\t"
+              "v_mfma_f32_16x16x4_f32 %[d], %[a0], %[t0], 0\n\t"
+              "s_nop 3\n\t"
+              "v_mfma_f32_16x16x4_f32 %[d], %[a1], %[t1], %[d]\n\t"
+              "s_nop 3\n\t"
+              "v_mfma_f32_16x16x4_f32 %[d], %[a2], %[t2], %[d]\n\t"
+              "s_nop 3\n\t"
+              "v_mfma_f32_16x16x4_f32 %[d], %[a3], %[t3], %[d]\n\t"
+              "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+              : [d] "=&a"(acc), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+              : [o0] "a"(oacc[db][qb][0]), [o1] "a"(oacc[db][qb][1]), [o2] "a"(oacc[db][qb][2]),
+                [o3] "a"(oacc[db][qb][3]), [a0] "v"(asel[qb][0]), [a1] "v"(asel[qb][1]),
+                [a2] "v"(asel[qb][2]), [a3] "v"(asel[qb][3]));
           oacc[db][qb] = acc;
         }
+      // the last MFMA results are complete before anything reads them
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       // P(j) again, against the moved max
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) lt[qb] = 0.f;
