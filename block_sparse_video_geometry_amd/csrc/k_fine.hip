@@ -124,6 +124,8 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(((unsigned long long)hi << 32) | lo);
 }
 
+constexpr bf16x2 ONES_BF16X2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -463,19 +465,21 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     unsigned pe[4][2];  // bf16 pairs of the even key block, until its odd partner is done
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) lt[qb] = 0.f;
+    // The row sums add the bf16-rounded probabilities, two per dot2 against (1, 1): the
+    // normaliser is then the sum of exactly the weights the PV product applies.
     auto soft = [&](int s) {
       const int kb = s >> 2, qb = s & 3;
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(scur[kb][qb][i], sl2, -mrun[qb]));
-        lt[qb] += p[i];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(scur[kb][qb][i], sl2, -mrun[qb]));
+      const unsigned w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
+      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ONES_BF16X2, lt[qb], false);
+      lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ONES_BF16X2, lt[qb], false);
       if (kb & 1) {
-        pb[qb][kb >> 1] = as_bf16x8(u32x4{pe[qb][0], pe[qb][1], pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+        pb[qb][kb >> 1] = as_bf16x8(u32x4{pe[qb][0], pe[qb][1], w0, w1});
       } else {
-        pe[qb][0] = pack_bf16x2(p[0], p[1]);
-        pe[qb][1] = pack_bf16x2(p[2], p[3]);
+        pe[qb][0] = w0;
+        pe[qb][1] = w1;
       }
     };
 
