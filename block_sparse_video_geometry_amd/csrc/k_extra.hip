@@ -9,27 +9,35 @@
 // i's list the E largest are kept, equal scores to the lower packed token index.
 //
 // vsa_extra_select_kernel: one workgroup per (64 sparse rows, head, batch), wave
-// w owns rows 16 w .. 16 w + 15.  Every key tile of the head streams through LDS
-// in tile-id order (the next two tiles' loads in flight in registers meanwhile):
+// w owns rows 16 w .. 16 w + 15; the workgroups are renumbered so that the row blocks
+// of one (batch, head) share an XCD and its L2.  Every key tile of the head streams
+// through LDS in tile-id order (the next two tiles' loads in flight in registers):
 //   Z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split exactly
 //     into three bf16 terms hi + mid + lo, so the products are exact and only the
 //     fp32 accumulation rounds: the ranking then holds the fp32 order (a plain
-//     bf16 qbar would move logits by ~2^-9 of their size).
+//     bf16 qbar would move logits by ~2^-9 of their size).  Keys are ranked by these
+//     raw dot products; the positive scale s does not change the order.
 //   A tile in the row's list is skipped with a per-row cursor into the (ascending)
 //     list; padding rows of a partial prefix tile are skipped by their index.
-//   Streaming top-E: a key enters the row's LDS candidate buffer only if it beats
-//     the row's threshold, the E-th best (score, token) seen so far.  When a tile's
-//     entrants would overflow a buffer the wave first cuts it back to its E best
-//     with a bitwise ballot search over the 64-bit keys (score order, then ~token),
-//     which also raises the threshold, and tests the tile's keys again.  The keys
-//     are unique, so every cut keeps exactly E.  With E = 64 a row is cut about
-//     (64 + 64 ln(tiles / 2)) / 64 times.
-//   Scoring: a key passes if its float score is >= the threshold's; only a score equal
-//     to it needs the full (score, token) key, and keys are built only for the few
-//     that enter.
-// At the end each row is cut to at most E, ranked by token and written ascending.
-// The kernel issues ~0.4k VALU instructions per tile per wave against 48 MFMAs, at
-// about one wave per SIMD, so it is bound by issue and latency rather than by the MFMAs.
+//   Streaming top-E: a key enters the row's LDS candidate buffer if its score is at
+//     least the row's threshold, a lower bound of the E-th best score seen so far
+//     (equal scores enter too: only the cuts order ties, by token).  When a tile's
+//     entrants would overflow a buffer the wave first cuts it back with a bitwise
+//     ballot search over the 64-bit keys (score order, then ~token) that stops as
+//     soon as a candidate keeps between E and E + 16 entries (exactly E if it has
+//     to go down to the token word), raising the threshold, and tests the tile's
+//     keys again.  Rows are cut about ten times each at E = 64 (the buffer holds
+//     128 entries per row).
+//   Writes: a lane that takes several keys of a tile (early in the stream) writes
+//     them in one step per key index; otherwise one pass per key of the busiest lane,
+//     the score picked by a select tree on the key index.
+// At the end each row is cut to exactly min(E, entries), ranked by token and written
+// ascending.  Measured on the 36,096-token, 32-head workload at E = 64: the stream of
+// one workgroup costs ~290 VALU and ~130 SALU instructions per tile per wave (48 of
+// them MFMAs) at one wave per SIMD, and waves wait for memory or at the barriers for
+// 46% of their cycles; about 620 keys enter each row over the stream (an exact
+// running threshold would still admit E (1 + ln(keys / E)) ~ 470).  The candidate
+// bookkeeping, not the MFMAs or the key traffic, sets the time.
 //
 // vsa_extra_gather_kernel: copies each row's extra K and V rows into staging
 // buffers laid out [batch, Qs, 64, heads, 128] (padding rows zero), i.e. with
@@ -42,6 +50,7 @@ namespace {
 
 constexpr int XROWS = 64;   // sparse rows per workgroup, 16 per wave
 constexpr int XCAP = 128;   // candidate buffer entries per row (a tile adds at most 64)
+constexpr int XSLACK = 16;  // a cut inside the stream may keep up to E + XSLACK entries
 
 __device__ __forceinline__ unsigned order_key(float f) {
   if (f == 0.0f) f = 0.0f;
@@ -111,6 +120,11 @@ __device__ __forceinline__ void walk_init(const VsaGeom& g, TileWalk& w) {
   walk_set(g, w);
 }
 __device__ __forceinline__ void walk_next(const VsaGeom& g, TileWalk& w) {
+  // every field is wave-uniform: said so, the segment tables are read with scalar loads
+  // rather than vector loads (whose waits would also wait for the tile loads)
+  w.t = __builtin_amdgcn_readfirstlane(w.t);
+  w.seg = __builtin_amdgcn_readfirstlane(w.seg);
+  w.tin = __builtin_amdgcn_readfirstlane(w.tin);
   if (w.t < g.P) {  // leaving a prefix tile
     if (w.t + 1 < g.pre_tile0[w.seg + 1]) {
       ++w.tin;
@@ -148,11 +162,20 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   __shared__ __attribute__((aligned(16))) char ktile[64 * 256];
   __shared__ unsigned long long cbuf[XROWS][XCAP];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
-  const int b = blockIdx.z, h = blockIdx.y;
+  // Workgroup order: the hardware deals consecutive workgroup ids to the eight XCDs in turn,
+  // so id L runs on XCD L % 8.  Renumbering so that XCD x takes a run of consecutive logical
+  // ids puts the row blocks of one (batch, head), which stream the same keys, on one XCD and
+  // its L2 at about the same time.
+  const int nrb = (g.Qs + XROWS - 1) / XROWS;
+  const int nb = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int lg = xcd * (nb >> 3) + min(xcd, nb & 7) + (L >> 3);
+  const int rb = lg % nrb, bhl = lg / nrb;
+  const int h = bhl % g.heads, b = bhl / g.heads;
   const size_t bh = (size_t)b * g.heads + h;
   const int rl = 16 * wave + ql;           // this lane's row in the workgroup
-  const int r = blockIdx.x * XROWS + rl;   // its sparse row
+  const int r = rb * XROWS + rl;           // its sparse row
   const bool live = r < g.Qs;
+  const bool wlive = rb * XROWS + 16 * wave < g.Qs;  // the wave has a live row (wave-uniform)
   const int E = g.extra;
 
   // B operands: qbar of row r, dims 32 ks + 8 grp .. +7, as hi / mid / lo bf16 terms
@@ -182,36 +205,52 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   int cur = 0;
   int nl = lst[0];
 
-  int nrow = 0;                  // entries in this row's buffer (same in its four lanes)
-  unsigned long long th = 0ull;  // a key must beat this to enter (0: nothing seen yet)
-  float thz = -INFINITY;         // the score of th: a key scoring below it cannot enter
+  int nrow = 0;            // entries in this row's buffer (same in its four lanes)
+  float thz = -INFINITY;   // the row's threshold: the E-th best raw score at its last cut
 
   // Cut row rc (workgroup row) from n entries to its best `keep`; returns the keep-th key.
-  auto cut = [&](int rc, int n, int keep) -> unsigned long long {
+  // Cuts workgroup row rc (n > E entries) to its entries at or above the threshold key
+  // `pre` returned, keeping `kept` of them, E <= kept <= lim: the score word is found by a
+  // bitwise ballot search from the top, which stops at the first candidate that keeps
+  // between E and lim entries.  Run to its end the search gives the E-th best score word;
+  // if ties at that score still keep more than lim, the token word is searched as well and
+  // exactly E are kept.  n and lim are wave-uniform; every valid key is above 0.
+  struct Cut {
+    unsigned long long pre;
+    int kept;
+  };
+  auto cut = [&](int rc, int n, int lim) -> Cut {
+    n = __builtin_amdgcn_readfirstlane(n);
+    lim = __builtin_amdgcn_readfirstlane(lim);
     const bool v0 = lane < n, v1 = lane + 64 < n;
     const unsigned long long r0 = v0 ? cbuf[rc][lane] : 0ull;
     const unsigned long long r1 = v1 ? cbuf[rc][lane + 64] : 0ull;
     const unsigned long long k0 = v0 ? entry_key(r0) : 0ull;
     const unsigned long long k1 = v1 ? entry_key(r1) : 0ull;
-    // the keep-th largest score word (an empty slot's 0 is below every real one) ...
     const unsigned h0 = (unsigned)(k0 >> 32), h1 = (unsigned)(k1 >> 32);
     unsigned ph = 0u;
+    int kept = n;
     for (int bit = 31; bit >= 0; --bit) {
       const unsigned cand = ph | (1u << bit);
       const int c = __popcll(__ballot(h0 >= cand)) + __popcll(__ballot(h1 >= cand));
-      if (c >= keep) ph = cand;
+      if (c >= E) {
+        ph = cand;
+        kept = c;
+        if (c <= lim) break;
+      }
     }
-    // ... then, only if several entries share it at the boundary, the token word
-    const int need = keep - (__popcll(__ballot(h0 > ph)) + __popcll(__ballot(h1 > ph)));
-    const bool e0 = v0 && h0 == ph, e1 = v1 && h1 == ph;
     unsigned pl = 0u;
-    if (__popcll(__ballot(e0)) + __popcll(__ballot(e1)) > need) {
+    if (kept > lim) {
+      // ties at the E-th best score word: the token word decides, and exactly E stay
+      const int need = E - (__popcll(__ballot(h0 > ph)) + __popcll(__ballot(h1 > ph)));
+      const bool e0 = v0 && h0 == ph, e1 = v1 && h1 == ph;
       const unsigned l0 = (unsigned)k0, l1 = (unsigned)k1;
       for (int bit = 31; bit >= 0; --bit) {
         const unsigned cand = pl | (1u << bit);
         const int c = __popcll(__ballot(e0 && l0 >= cand)) + __popcll(__ballot(e1 && l1 >= cand));
         if (c >= need) pl = cand;
       }
+      kept = E;
     }
     const unsigned long long pre = ((unsigned long long)ph << 32) | pl;
     const bool s0 = v0 && k0 >= pre, s1 = v1 && k1 >= pre;
@@ -220,7 +259,7 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     if (s0) cbuf[rc][lanes_below(b0)] = r0;
     if (s1) cbuf[rc][__popcll(b0) + lanes_below(b1)] = r1;
-    return pre;
+    return Cut{pre, kept};
   };
 
   // staging of a key tile: thread tid moves rows r = (tid >> 4) + 16 m, chunk tid & 15;
@@ -273,17 +312,23 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     __syncthreads();  // every wave is done with the previous tile
     stash(slot, vmask);
     __syncthreads();
+    // The list entry loaded last step, then the next one.  Loads complete in issue order
+    // as far as the waits can tell, so each list load is issued before the step's tile
+    // refill: waiting for it next step then leaves that refill in flight.
+    const bool excl = cur < cnt_l && nl == t;
+    cur += excl ? 1 : 0;
+    nl = lst[min(cur, g.cap - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     // refill two tiles ahead (past the end the last tile again: every step issues the
     // same loads, so the wait before a stash leaves the other slot's loads in flight)
     if (t + 2 < g.Tq) walk_next(g, wf);
     fetch(wf, slot, vmask);
-    __builtin_amdgcn_sched_barrier(0);  // the refill is issued before the wait for nl below
-    // the list entry loaded last step, then the next one (used next step, after that
-    // step's refill has been issued)
-    const bool excl = cur < cnt_l && nl == t;
-    cur += excl ? 1 : 0;
-    nl = lst[min(cur, g.cap - 1)];
+    __builtin_amdgcn_sched_barrier(0);
 
+    if (!wlive) {  // a wave past the last sparse row only helps stage the tiles
+      walk_next(g, wc);
+      return;
+    }
     // all 16 A operands first, then the 48 MFMAs with the four key blocks' accumulator
     // chains interleaved, so no MFMA waits on the one just before it
     bf16x8 a[4][4];
@@ -305,18 +350,19 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
         __builtin_amdgcn_sched_barrier(0);  // keep the four chains interleaved
       }
 
-    // lane holds keys 16 kb + 4 grp + i of the tile for its row
+    // lane holds the raw dot products of keys 16 kb + 4 grp + i of the tile for its row
+    // (e = 4 kb + i).  Ranking by them ranks by the scaled score, the scale being positive.
     const bool video = wc.video;
     const int tok0 = wc.tok0;
     const int nv = wc.nv;
-    // admission on the float score: a key beats th iff z > thz, or z == thz and its
-    // (score, token) order key is above th (thz is th's score; -inf before the first cut).
-    // z >= thz is tested first; only a score equal to thz (rare) needs the exact key.
+    // A key enters if its score is >= the row's threshold score thz (-inf before the first
+    // cut).  A key that only ties the threshold's score enters too: the cuts order equal
+    // scores by token, so such an entrant costs buffer room, never the result.
     float z[16];
     unsigned ge = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      z[e] = acc[e >> 2][e & 3] * g.scale;
+      z[e] = acc[e >> 2][e & 3];
       ge |= (unsigned)(z[e] >= thz) << e;
     }
     if (!video) {  // a prefix tile may end early: key 16 kb + 4 grp + i is valid iff below nv
@@ -335,24 +381,8 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     }
     const int tokl = tok0 + (video ? grp * g.W : 4 * grp);  // key e: tokl + (video ? kb hw + i : 16 kb + i)
     auto tok_of = [&](int e) { return tokl + (e >> 2) * (video ? hw : 16) + (e & 3); };
-    auto admit = [&]() {
-      unsigned f = 0u;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool beat = z[e] > thz || (z[e] == thz && entry_key(entry(z[e], tok_of(e))) > th);
-        f |= (unsigned)(((ge >> e) & 1u) && beat) << e;
-      }
-      return f;
-    };
-    // a score equal to the row's threshold score anywhere in the lane (a superset of the
-    // candidate ties; admit() applies ge)
-    bool tie = false;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) tie |= z[e] == thz;
     // counts over the four lanes of the row (lanes ql + 16 grp)
-    unsigned flag = ge;
-    if (__ballot(tie) != 0ull) flag = admit();  // a score tie with the threshold (rare)
-    int c = __popc(flag);
+    int c = __popc(ge);
     int cr[4];
     row_values4(c, cr);
     int c0 = cr[0], c1 = cr[1], c2 = cr[2], c3 = cr[3];
@@ -364,27 +394,21 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
         const int rc = __builtin_ctzll(full);
         full &= full - 1;
         const int n = __shfl(nrow, rc);
-        const unsigned long long T = cut(16 * wave + rc, n, E);
+        // room for this tile's entrants of the row after the cut
+        const int lim = min(E + XSLACK, XCAP - __shfl(c0 + c1 + c2 + c3, rc));
+        const Cut T = cut(16 * wave + rc, n, lim);
         if (ql == rc) {
-          nrow = E;
-          th = T;
-          const unsigned sk = (unsigned)(T >> 32);  // back from the order key to the float
+          nrow = T.kept;
+          const unsigned sk = (unsigned)(T.pre >> 32);  // back from the order key to the float
           thz = __uint_as_float((sk & 0x80000000u) ? (sk & 0x7fffffffu) : ~sk);
         }
       }
-      // the keys again against the raised thresholds: the same float test, the exact key
-      // only on a tie
+      // the keys again against the raised thresholds
       unsigned ge2 = 0u;
-      bool tie2 = false;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        ge2 |= (unsigned)(z[e] >= thz) << e;
-        tie2 |= z[e] == thz;
-      }
+      for (int e = 0; e < 16; ++e) ge2 |= (unsigned)(z[e] >= thz) << e;
       ge &= ge2;
-      flag = ge;
-      if (__ballot(tie2) != 0ull) flag = admit();
-      c = __popc(flag);
+      c = __popc(ge);
       row_values4(c, cr);
       c0 = cr[0];
       c1 = cr[1];
@@ -392,9 +416,23 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
       c3 = cr[3];
     }
     int at = nrow + (grp > 0 ? c0 : 0) + (grp > 1 ? c1 : 0) + (grp > 2 ? c2 : 0);
-    // the admitted keys, lowest e first: one pass per key of the lane that admits the most
-    // (few once the buffer is warm); key e's score picked by a select tree on e's bits
-    for (unsigned f = flag; __ballot(f != 0u) != 0ull;) {
+    // the admitted keys, lowest e first.  Where a lane takes several (early in the stream)
+    // one step per key index e, skipping the e no lane takes ...
+    if (__ballot(c > 3) != 0ull) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool in = (ge >> e) & 1u;
+        if (__ballot(in) != 0ull) {
+          if (in) cbuf[rl][at++] = entry(z[e], tok_of(e));
+        }
+      }
+      nrow += c0 + c1 + c2 + c3;
+      walk_next(g, wc);
+      return;
+    }
+    // ... else one pass per key of the lane that takes the most, key e's score picked by a
+    // select tree on e's bits
+    for (unsigned f = ge; __ballot(f != 0u) != 0ull;) {
       if (f != 0u) {
         const int e = __builtin_ctz(f);
         f &= f - 1u;
@@ -413,19 +451,22 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     nrow += c0 + c1 + c2 + c3;
     walk_next(g, wc);
   };
-  for (int t = 0; t < g.Tq; t += 2) {
+  // both steps of the loop body unconditional: a conditional second step would make the
+  // wait before the first stash drain the other slot's loads as well
+  for (int t = 0; t + 1 < g.Tq; t += 2) {
     step(t, kr[0], kv[0]);
-    if (t + 1 < g.Tq) step(t + 1, kr[1], kv[1]);
+    step(t + 1, kr[1], kv[1]);
   }
+  if (g.Tq & 1) step(g.Tq - 1, kr[0], kv[0]);
 
   // final cut to at most E, then rank by token and write ascending
   __builtin_amdgcn_s_waitcnt(0xc07f);
   for (int rc = 0; rc < 16; ++rc) {
-    const int row = blockIdx.x * XROWS + 16 * wave + rc;
+    const int row = rb * XROWS + 16 * wave + rc;
     if (row >= g.Qs) break;
     int n = __shfl(nrow, rc);
     if (n > E) {
-      cut(16 * wave + rc, n, E);
+      cut(16 * wave + rc, n, E);  // lim = E: exactly the E best
       n = E;
       __builtin_amdgcn_s_waitcnt(0xc07f);
     }
@@ -479,8 +520,8 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
                       const int* counts, int* xtok, int* xcnt, void* kx, void* vx, hipStream_t st) {
   if (g.Qs == 0 || g.extra == 0) return;
-  dim3 grid((g.Qs + XROWS - 1) / XROWS, g.heads, g.batch);
-  hipLaunchKernelGGL(vsa_extra_select_kernel, grid, dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
+  const int blocks = (g.Qs + XROWS - 1) / XROWS * g.heads * g.batch;
+  hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(blocks), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
                      xtok, xcnt);
   hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(256), 0, st, g,
                      (const u32x4*)k, (const u32x4*)v, xtok, xcnt, (u32x4*)kx, (u32x4*)vx);
