@@ -143,6 +143,27 @@ __device__ __forceinline__ void walk_next(const VsaGeom& g, TileWalk& w) {
   walk_set(g, w);
 }
 
+// Positions a walk at tile t (prefix: its segment and index in it; video: its coordinates).
+__device__ __forceinline__ void walk_seek(const VsaGeom& g, TileWalk& w, int t) {
+  w.t = t;
+  w.seg = w.tin = w.tw = w.th = w.tt = 0;
+  if (t < g.P) {
+    while (t >= g.pre_tile0[w.seg + 1]) ++w.seg;
+    w.tin = t - g.pre_tile0[w.seg];
+  } else {
+    const int v = t - g.P;
+    w.tw = v % g.tw_n;
+    w.th = (v / g.tw_n) % g.th_n;
+    w.tt = v / g.tw_n / g.th_n;
+  }
+  walk_set(g, w);
+}
+
+// The workgroup whose step range holds step x: the largest w with floor(w TS / G) <= x.
+__device__ __forceinline__ int xwg_of(long long x, long long TS, int G) {
+  return (int)(((x + 1) * G + TS - 1) / TS) - 1;
+}
+
 // A buffer entry holds the float score's bits over ~token.  Its 64-bit order key is larger
 // for the better candidate (score order, then the lower token); an empty slot's key is 0.
 __device__ __forceinline__ unsigned long long entry(float z, int tok) {
@@ -156,59 +177,43 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
                                                                const float* __restrict__ qbar,
                                                                const int* __restrict__ lists,
                                                                const int* __restrict__ counts,
-                                                               int* __restrict__ xtok,
-                                                               int* __restrict__ xcnt) {
+                                                               unsigned long long* __restrict__ xpart,
+                                                               int* __restrict__ xpcnt) {
   // K tile: key row r at 256 r, 16-byte chunk c at position c ^ (r & 15)
   __shared__ __attribute__((aligned(16))) char ktile[64 * 256];
   __shared__ unsigned long long cbuf[XROWS][XCAP];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
-  // Workgroup order: the hardware deals consecutive workgroup ids to the eight XCDs in turn,
-  // so id L runs on XCD L % 8.  Renumbering so that XCD x takes a run of consecutive logical
-  // ids puts the row blocks of one (batch, head), which stream the same keys, on one XCD and
-  // its L2 at about the same time.
+  // The work is the sequence of (row block, tile) steps, row blocks in (batch, head, block)
+  // order and tiles in id order; workgroup w takes steps [w TS / G, (w + 1) TS / G), so every
+  // workgroup has the same share and G = 2 per CU run at once.  Its range falls into
+  // segments, one per row block it touches; a segment streams its tiles like a whole row
+  // block would and leaves each row's best E of them in the partial lists, which the gather
+  // kernel merges.  Logical ids are dealt so that XCD x (ids L = x mod 8) takes a run of
+  // consecutive ranges: the row blocks of one (batch, head), which stream the same keys,
+  // share an XCD and its L2.
   const int nrb = (g.Qs + XROWS - 1) / XROWS;
-  const int nb = gridDim.x, L = blockIdx.x, xcd = L & 7;
-  const int lg = xcd * (nb >> 3) + min(xcd, nb & 7) + (L >> 3);
-  const int rb = lg % nrb, bhl = lg / nrb;
-  const int h = bhl % g.heads, b = bhl / g.heads;
-  const size_t bh = (size_t)b * g.heads + h;
-  const int rl = 16 * wave + ql;           // this lane's row in the workgroup
-  const int r = rb * XROWS + rl;           // its sparse row
-  const bool live = r < g.Qs;
-  const bool wlive = rb * XROWS + 16 * wave < g.Qs;  // the wave has a live row (wave-uniform)
+  const long long TS = (long long)nrb * g.heads * g.batch * g.Tq;
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
+  const long long lo = (long long)w * TS / G, hi = (long long)(w + 1) * TS / G;
+  const int rl = 16 * wave + ql;  // this lane's row in the workgroup
   const int E = g.extra;
 
+  // the segment's row block and this lane's row (set per segment)
+  int rb = 0, h = 0, b = 0;
+  size_t bh = 0;
+  int r = 0;
+  bool live = false, wlive = false;
+  int t1 = 0;  // the segment's tiles end here
   // B operands: qbar of row r, dims 32 ks + 8 grp .. +7, as hi / mid / lo bf16 terms
   bf16x8 qs[3][4];
-  {
-    const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? r : 0)) * VSA_HEAD_DIM);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f32x4 a = live ? qp[8 * ks + 2 * grp] : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 c = live ? qp[8 * ks + 2 * grp + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-      const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hi, mid, lo;
-        split3(x[e], hi, mid, lo);
-        qs[0][ks][e] = hi;
-        qs[1][ks][e] = mid;
-        qs[2][ks][e] = lo;
-      }
-    }
-  }
-
   // list cursor: entry cur of this row's (ascending) list is the next listed tile; it is
   // loaded every tile, one tile ahead of its use, so every step issues the same loads
-  const int* lst = lists + (bh * g.Qs + (live ? r : 0)) * g.cap;
-  const int cnt_l = live ? counts[bh * g.Qs + r] : 0;
-  int cur = 0;
-  int nl = lst[0];
-
+  const int* lst = lists;
+  int cnt_l = 0, cur = 0, nl = 0;
   int nrow = 0;            // entries in this row's buffer (same in its four lanes)
-  float thz = -INFINITY;   // the row's threshold: the E-th best raw score at its last cut
+  float thz = -INFINITY;   // the row's threshold: a lower bound of its E-th best raw score
 
-  // Cut row rc (workgroup row) from n entries to its best `keep`; returns the keep-th key.
   // Cuts workgroup row rc (n > E entries) to its entries at or above the threshold key
   // `pre` returned, keeping `kept` of them, E <= kept <= lim: the score word is found by a
   // bitwise ballot search from the top, which stops at the first candidate that keeps
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   // in a video tile row r is (dt, dh, dw) = (m, (tid >> 6) & 3, (tid >> 4) & 3)
   const int hw = g.H * g.W;
   const int fdhw = ((tid >> 6) & 3) * g.W + ((tid >> 4) & 3);
-  const u32x4* kbh = k + (((size_t)b * g.N) * g.heads + h) * (VSA_HEAD_DIM / 8) + (tid & 15);
+  const u32x4* kbh = k;  // this thread's 16-byte chunk of token 0 of the segment's (b, h)
   const int tokstride = g.heads * (VSA_HEAD_DIM / 8);  // u32x4 per token
   // two tiles in flight: slot t & 1 holds tile t, loaded two steps back.  A padding row
   // loads row 0 (always valid) and is zeroed when stashed (bit m of the slot's mask), so
@@ -302,11 +307,6 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   };
 
   TileWalk wc, wf;  // the tile being scored and the last one fetched
-  walk_init(g, wc);
-  wf = wc;
-  fetch(wf, kr[0], kv[0]);
-  if (g.Tq > 1) walk_next(g, wf);
-  fetch(wf, kr[1], kv[1]);
   // one tile: stage it, refill its slot two tiles ahead, score it, admit its keys
   auto step = [&](int t, u32x4 (&slot)[4], unsigned& vmask) {
     __syncthreads();  // every wave is done with the previous tile
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     __builtin_amdgcn_sched_barrier(0);
     // refill two tiles ahead (past the end the last tile again: every step issues the
     // same loads, so the wait before a stash leaves the other slot's loads in flight)
-    if (t + 2 < g.Tq) walk_next(g, wf);
+    if (t + 2 < t1) walk_next(g, wf);
     fetch(wf, slot, vmask);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -451,53 +451,165 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     nrow += c0 + c1 + c2 + c3;
     walk_next(g, wc);
   };
-  // both steps of the loop body unconditional: a conditional second step would make the
-  // wait before the first stash drain the other slot's loads as well
-  for (int t = 0; t + 1 < g.Tq; t += 2) {
-    step(t, kr[0], kv[0]);
-    step(t + 1, kr[1], kv[1]);
-  }
-  if (g.Tq & 1) step(g.Tq - 1, kr[0], kv[0]);
-
-  // final cut to at most E, then rank by token and write ascending
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  for (int rc = 0; rc < 16; ++rc) {
-    const int row = rb * XROWS + 16 * wave + rc;
-    if (row >= g.Qs) break;
-    int n = __shfl(nrow, rc);
-    if (n > E) {
-      cut(16 * wave + rc, n, E);  // lim = E: exactly the E best
-      n = E;
-      __builtin_amdgcn_s_waitcnt(0xc07f);
+  for (long long pos = lo; pos < hi;) {
+    // the segment: tiles [t0, t1) of row block rbg
+    const int rbg = (int)(pos / g.Tq);
+    const int t0 = (int)(pos - (long long)rbg * g.Tq);
+    t1 = (int)min((long long)g.Tq, t0 + (hi - pos));
+    const int seg = w - xwg_of((long long)rbg * g.Tq, TS, G);  // its index among the row block's
+    pos += t1 - t0;
+    rb = rbg % nrb;
+    h = (rbg / nrb) % g.heads;
+    b = rbg / nrb / g.heads;
+    bh = (size_t)b * g.heads + h;
+    r = rb * XROWS + rl;
+    live = r < g.Qs;
+    wlive = rb * XROWS + 16 * wave < g.Qs;
+    {
+      const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? r : 0)) * VSA_HEAD_DIM);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x4 a = live ? qp[8 * ks + 2 * grp] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 c = live ? qp[8 * ks + 2 * grp + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 hi3, mid3, lo3;
+          split3(x[e], hi3, mid3, lo3);
+          qs[0][ks][e] = hi3;
+          qs[1][ks][e] = mid3;
+          qs[2][ks][e] = lo3;
+        }
+      }
     }
-    const int mytok = lane < n ? ~(int)(unsigned)cbuf[16 * wave + rc][lane] : 0;
-    int rank = 0;
-    for (int e = 0; e < n; ++e) rank += (~(int)(unsigned)cbuf[16 * wave + rc][e] < mytok) ? 1 : 0;
-    const size_t ro = bh * g.Qs + row;
-    if (lane < n) xtok[ro * VSA_MAX_EXTRA + rank] = mytok;
-    if (lane == 0) xcnt[ro] = n;
+    // the list cursor at the first listed tile >= t0 (binary search of the ascending list)
+    lst = lists + (bh * g.Qs + (live ? r : 0)) * g.cap;
+    cnt_l = live ? counts[bh * g.Qs + r] : 0;
+    {
+      int a = 0, c = cnt_l;
+      while (a < c) {
+        const int m = (a + c) >> 1;
+        if (lst[m] < t0) a = m + 1;
+        else c = m;
+      }
+      cur = a;
+    }
+    nl = lst[min(cur, g.cap - 1)];
+    nrow = 0;
+    thz = -INFINITY;
+    kbh = k + (((size_t)b * g.N) * g.heads + h) * (VSA_HEAD_DIM / 8) + (tid & 15);
+    walk_seek(g, wc, t0);
+    wf = wc;
+    fetch(wf, kr[0], kv[0]);
+    if (t0 + 1 < t1) walk_next(g, wf);
+    fetch(wf, kr[1], kv[1]);
+    // both steps of the loop body unconditional: a conditional second step would make the
+    // wait before the first stash drain the other slot's loads as well
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
+      step(t, kr[0], kv[0]);
+      step(t + 1, kr[1], kv[1]);
+    }
+    if (t < t1) step(t, kr[0], kv[0]);
+
+    // each row's best E of the segment (exactly), into the partial lists
+    if (wlive) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      for (int rc = 0; rc < 16; ++rc) {
+        const int row = rb * XROWS + 16 * wave + rc;
+        if (row >= g.Qs) break;
+        int n = __shfl(nrow, rc);
+        if (n > E) {
+          cut(16 * wave + rc, n, E);  // lim = E: exactly the E best
+          n = E;
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+        const size_t pr = ((size_t)rbg * g.xms + seg) * XROWS + 16 * wave + rc;
+        if (lane < n) xpart[pr * VSA_MAX_EXTRA + lane] = cbuf[16 * wave + rc][lane];
+        if (lane == 0) xpcnt[pr] = n;
+      }
+    }
   }
 }
 
-// One workgroup per (sparse row, head, batch): thread tid copies 64 bytes of extra row
-// tid >> 2 (zeros past the row's count) of K and of V.
+// One workgroup per (sparse row, head, batch).  Wave 0 merges the row's segment lists: the
+// best E of their union by the 64-bit order key (keys are unique: the tokens differ), then
+// ranks them by token and writes the row's extra tokens and count.  Then thread tid copies
+// 64 bytes of extra row tid >> 2 (zeros past the count) of K and of V.
 __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const u32x4* __restrict__ k,
                                                                const u32x4* __restrict__ v,
-                                                               const int* __restrict__ xtok,
-                                                               const int* __restrict__ xcnt,
+                                                               const unsigned long long* __restrict__ xpart,
+                                                               const int* __restrict__ xpcnt,
+                                                               int* __restrict__ xtok,
+                                                               int* __restrict__ xcnt,
                                                                u32x4* __restrict__ kx,
                                                                u32x4* __restrict__ vx) {
+  __shared__ unsigned long long mbuf[VSA_MAX_EXTRA];
+  __shared__ int mtok[VSA_MAX_EXTRA];
+  __shared__ int stok[VSA_MAX_EXTRA];
+  __shared__ int mcnt;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t ro = ((size_t)b * g.heads + h) * g.Qs + s;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int E = g.extra;
+    const int nrb = (g.Qs + XROWS - 1) / XROWS;
+    const long long TS = (long long)nrb * g.heads * g.batch * g.Tq;
+    const int G = g.xg;
+    const int rbg = (b * g.heads + h) * nrb + s / XROWS, rw = s % XROWS;
+    const int w0 = xwg_of((long long)rbg * g.Tq, TS, G);
+    const int w1 = xwg_of((long long)(rbg + 1) * g.Tq - 1, TS, G);
+    size_t pr = (size_t)rbg * g.xms * XROWS + rw;
+    int n = xpcnt[pr];
+    unsigned long long e0 = lane < n ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
+    for (int sg = 1; sg <= w1 - w0; ++sg) {
+      pr = ((size_t)rbg * g.xms + sg) * XROWS + rw;
+      const int n1 = xpcnt[pr];
+      const unsigned long long e1 = lane < n1 ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
+      const bool v0 = lane < n, v1 = lane < n1;
+      const unsigned long long k0 = v0 ? entry_key(e0) : 0ull, k1 = v1 ? entry_key(e1) : 0ull;
+      const int keep = min(E, n + n1);
+      // the keep-th largest key, bit by bit from the top (an empty slot's 0 is below all)
+      unsigned long long pre = 0ull;
+      for (int bit = 63; bit >= 0; --bit) {
+        const unsigned long long cand = pre | (1ull << bit);
+        const int c = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+        if (c >= keep) pre = cand;
+      }
+      const bool s0 = v0 && k0 >= pre, s1 = v1 && k1 >= pre;
+      const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
+      if (s0) mbuf[lanes_below(b0)] = e0;
+      if (s1) mbuf[__popcll(b0) + lanes_below(b1)] = e1;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes are in LDS
+      n = keep;
+      e0 = lane < n ? mbuf[lane] : 0ull;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read before the next writes
+    }
+    // rank by token and write ascending
+    const int mytok = lane < n ? ~(int)(unsigned)e0 : 0;
+    mtok[lane] = mytok;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    int rank = 0;
+    for (int e = 0; e < n; ++e) rank += mtok[e] < mytok ? 1 : 0;
+    if (lane < n) {
+      xtok[ro * VSA_MAX_EXTRA + rank] = mytok;
+      stok[rank] = mytok;
+    }
+    if (lane == 0) {
+      xcnt[ro] = n;
+      mcnt = n;
+    }
+  }
+  __syncthreads();
   const int e = threadIdx.x >> 2, part = threadIdx.x & 3;
-  const int n = xcnt[ro];
+  const int n = mcnt;
   // destination row (b, s, e) of the [batch, Qs, 64, heads, 128] staging, head h
   const size_t dst = ((((size_t)b * g.Qs + s) * VSA_MAX_EXTRA + e) * g.heads + h) * 16 + 4 * part;
   u32x4 ka[4], va[4];
   if (e < n) {
     // (a token id outside the sequence cannot come from the select kernel; clamped all the
     // same, so that a read never leaves the (b, h) plane)
-    const int tok = min(max(xtok[ro * VSA_MAX_EXTRA + e], 0), g.N - 1);
+    const int tok = min(max(stok[e], 0), g.N - 1);
     const long long src = row_offset(g, b, tok, h) / 8 + 4 * part;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -518,11 +630,12 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
 }  // namespace
 
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
-                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, hipStream_t st) {
+                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, void* xpart, int* xpcnt,
+                      hipStream_t st) {
   if (g.Qs == 0 || g.extra == 0) return;
-  const int blocks = (g.Qs + XROWS - 1) / XROWS * g.heads * g.batch;
-  hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(blocks), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
-                     xtok, xcnt);
+  hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(g.xg), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
+                     (unsigned long long*)xpart, xpcnt);
   hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(256), 0, st, g,
-                     (const u32x4*)k, (const u32x4*)v, xtok, xcnt, (u32x4*)kx, (u32x4*)vx);
+                     (const u32x4*)k, (const u32x4*)v, (const unsigned long long*)xpart, xpcnt, xtok, xcnt,
+                     (u32x4*)kx, (u32x4*)vx);
 }

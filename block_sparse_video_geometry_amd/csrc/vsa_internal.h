@@ -43,11 +43,18 @@ struct VsaGeom {
   int32_t cchunks;                         // 64-tile chunks per slice
   int32_t reblock;                         // 1: Spark-Reblock video tiles per (batch, head)
   int32_t rb_nsplit;                       // tile ranges per (batch, head) of the key-moment sums
+  int32_t xg;                              // extra-token select workgroups (equal step ranges)
+  int32_t xms;                             // most segments (workgroups) a 64-row block spans
 };
+
+// The extra-token select runs this many workgroups at most: two per CU of the 256-CU part,
+// each holding 80 KB of LDS.
+constexpr int VSA_EXTRA_WGS = 512;
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
   size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
+  size_t xpart, xpcnt;        // extra tokens: per-segment best E of each row, and counts
   size_t cpart;               // coarse partials per (row, slice): max, sum, 2 pad, O[128]
   // Spark-Reblock: key-moment partials and M (fp32, bf16 hi/lo), video-token norms, token
   // lists (ping-pong; `tiles` is the final one), projections, pass partials, node states,

@@ -35,7 +35,8 @@ void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, 
 // Extra tokens per sparse row (best pooled-query scores outside the listed tiles): ids
 // ascending and counts, and their K / V rows staged [batch, Qs, 64, heads, 128].
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
-                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, hipStream_t st);
+                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, void* xpart, int* xpcnt,
+                      hipStream_t st);
 
 // Spark-Reblock mapper: M, norms and the tree levels; returns the final token list
 // ([batch, heads, Vt, 64] packed token ids, leaf j = video tile j).

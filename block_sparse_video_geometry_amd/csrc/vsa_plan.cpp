@@ -157,6 +157,21 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     delete p;
     return VSA_ERR_UNSUPPORTED;
   }
+  // Extra-token select: the (64-row block, tile) steps split evenly over xg workgroups (at
+  // least 64 steps each); xms is the most workgroups whose ranges meet one row block.
+  g.xg = 0;
+  g.xms = 0;
+  if (g.extra > 0 && g.Qs > 0) {
+    const int64_t nrb = (g.Qs + 63) / 64;
+    const int64_t NRB = nrb * heads * batch;
+    const int64_t TS = NRB * g.Tq;
+    const int64_t G = std::max<int64_t>(1, std::min<int64_t>(VSA_EXTRA_WGS, TS / 64));
+    auto wg_of = [&](int64_t x) { return ((x + 1) * G + TS - 1) / TS - 1; };
+    int64_t ms = 1;
+    for (int64_t r = 0; r < NRB; ++r) ms = std::max(ms, wg_of((r + 1) * g.Tq - 1) - wg_of(r * g.Tq) + 1);
+    g.xg = (int32_t)G;
+    g.xms = (int32_t)ms;
+  }
   g.sink = o.sink;
   g.select = o.select;
   g.coarse = o.coarse;
@@ -203,6 +218,11 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   L.xcnt = take(g.extra > 0 ? BH * (size_t)g.Qs * 4 : 0);
   L.kx = take(xrows * heads * VSA_HEAD_DIM * 2);
   L.vx = take(xrows * heads * VSA_HEAD_DIM * 2);
+  {
+    const size_t xrb = g.extra > 0 ? BH * (size_t)((g.Qs + 63) / 64) * g.xms * 64 : 0;  // segment rows
+    L.xpart = take(xrb * VSA_MAX_EXTRA * 8);
+    L.xpcnt = take(xrb * 4);
+  }
   L.cpart = take(g.csplit > 1 ? BH * (size_t)g.Qs * g.csplit * (VSA_HEAD_DIM + 4) * 4 : 0);
   {
     const bool rb = g.reblock != 0;
