@@ -8,41 +8,42 @@
 // z = s qbar_i . k_t (no tile bias); over the valid tokens of the tiles not in
 // i's list the E largest are kept, equal scores to the lower packed token index.
 //
-// vsa_extra_select_kernel: one workgroup per (64 sparse rows, head, batch), wave
-// w owns rows 16 w .. 16 w + 15; the workgroups are renumbered so that the row blocks
-// of one (batch, head) share an XCD and its L2.  Every key tile of the head streams
-// through LDS in tile-id order (the next two tiles' loads in flight in registers):
-//   Z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split exactly
-//     into three bf16 terms hi + mid + lo, so the products are exact and only the
-//     fp32 accumulation rounds: the ranking then holds the fp32 order (a plain
-//     bf16 qbar would move logits by ~2^-9 of their size).  Keys are ranked by these
-//     raw dot products; the positive scale s does not change the order.
-//   A tile in the row's list is skipped with a per-row cursor into the (ascending)
-//     list; padding rows of a partial prefix tile are skipped by their index.
-//   Streaming top-E: a key enters the row's LDS candidate buffer if its score is at
-//     least the row's threshold, a lower bound of the E-th best score seen so far
-//     (equal scores enter too: only the cuts order ties, by token).  When a tile's
-//     entrants would overflow a buffer the wave first cuts it back with a bitwise
-//     ballot search over the 64-bit keys (score order, then ~token) that stops as
-//     soon as a candidate keeps between E and E + 16 entries (exactly E if it has
-//     to go down to the token word), raising the threshold, and tests the tile's
-//     keys again.  Rows are cut about ten times each at E = 64 (the buffer holds
-//     128 entries per row).
-//   Writes: a lane that takes several keys of a tile (early in the stream) writes
-//     them in one step per key index; otherwise one pass per key of the busiest lane,
-//     the score picked by a select tree on the key index.
-// At the end each row is cut to exactly min(E, entries), ranked by token and written
-// ascending.  Measured on the 36,096-token, 32-head workload at E = 64: the stream of
-// one workgroup costs ~290 VALU and ~130 SALU instructions per tile per wave (48 of
-// them MFMAs) at one wave per SIMD, and waves wait for memory or at the barriers for
-// 46% of their cycles; about 620 keys enter each row over the stream (an exact
-// running threshold would still admit E (1 + ln(keys / E)) ~ 470).  The candidate
-// bookkeeping, not the MFMAs or the key traffic, sets the time.
+// The select runs in two passes over the keys, scored the same way in both:
+//   z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split exactly into
+//   three bf16 terms hi + mid + lo, so the products are exact and only the fp32
+//   accumulation rounds (a plain bf16 qbar would move logits by ~2^-9 of their size).
+//   Keys are ranked by these raw dot products; the positive scale s does not change the
+//   order.  A tile in the row's list, and the padding rows of a partial prefix tile, take
+//   no part.
+// vsa_extra_tmax_kernel (pass 1): every (sparse row, tile) pair once, keeping only M1, the
+//   row's best score in the tile, and M4, the least of the four lane maxima (four keys of the
+//   tile score at least that).  One workgroup per (head, tile chunk, 64-row block), key tiles
+//   staged by buffer-to-LDS loads two tiles ahead.
+// vsa_extra_thr_kernel: per row T = max(E-th largest M1, ceil(E/4)-th largest M4), read from
+//   the top 16 bits of the order keys: a lower bound of the row's E-th best score (E tiles
+//   hold a key >= the one, ceil(E/4) tiles four keys >= the other).  The row's E best keys
+//   then all lie in its candidate tiles, those with M1 >= T, which are recorded as bits.
+// vsa_extra_score_kernel (pass 2): per (tile, head), the rows with the tile among their
+//   candidates, 16 to an MFMA group; every key scoring >= its row's T is appended to the row's
+//   candidate list (an atomic count gives the slot).  About E + a few keys per row on the
+//   pages' workloads; the list keeps VSA_EXTRA_CAND.
+// vsa_extra_select_kernel (fallback): a row whose list overflowed (heavy exact ties, say) is
+//   selected by streaming every key tile with a running threshold (described at the kernel);
+//   segments with no such row are skipped, so the kernel costs ~8 us when none overflowed.
+// vsa_extra_gather_kernel: the exact best E of the row's candidates (or of the fallback's
+//   partial lists) by (score, then lower token), ranked by token.
+// Measured on the 36,096-token, 32-head workload at E = 64: pass 1 0.49 ms, threshold 0.05,
+// pass 2 0.27, fallback 0.01 (1.69 ms before as one streaming pass).  Pass 1 runs its MFMAs
+// about half the time: every wave reads the whole 16 KB key tile from LDS for its 16 rows, so
+// the LDS reads come close to the MFMA time; pass 2 re-reads a row's split qbar for each of
+// its ~64 candidate tiles.
 //
 // vsa_extra_gather_kernel: copies each row's extra K and V rows into staging
 // buffers laid out [batch, Qs, 64, heads, 128] (padding rows zero), i.e. with
 // the token stride of K and V themselves, so the fine kernel reads a row's
 // extra tokens as one more 64-row tile of consecutive rows.
+#include <type_traits>
+
 #include "vsa_device.h"
 #include "vsa_kernels.h"
 
@@ -173,10 +174,21 @@ __device__ __forceinline__ unsigned long long entry_key(unsigned long long e) {
   return ((unsigned long long)order_key(__uint_as_float((unsigned)(e >> 32))) << 32) | (unsigned)e;
 }
 
+// Streaming selection (the fallback for rows whose candidate list overflowed).  One
+// workgroup per range of (64-row block, tile) steps, wave w owning rows 16 w .. 16 w + 15;
+// every key tile of the segment streams through LDS (two tiles in flight in registers).
+// A key enters the row's LDS candidate buffer if its score is at least the row's
+// threshold, a lower bound of the E-th best score seen so far (equal scores enter too: only
+// the cuts order ties, by token).  When a tile's entrants would overflow a buffer the wave
+// first cuts it back with a bitwise ballot search over the 64-bit keys (score order, then
+// ~token) that stops as soon as a candidate keeps between E and E + 16 entries (exactly E if
+// it has to go down to the token word), raising the threshold, and tests the tile's keys
+// again.  Each segment leaves every row's best E in the partial lists.
 __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const u32x4* __restrict__ k,
                                                                const float* __restrict__ qbar,
                                                                const int* __restrict__ lists,
                                                                const int* __restrict__ counts,
+                                                               const int* __restrict__ ccnt,
                                                                unsigned long long* __restrict__ xpart,
                                                                int* __restrict__ xpcnt) {
   // K tile: key row r at 256 r, 16-byte chunk c at position c ^ (r & 15)
@@ -463,8 +475,10 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
     b = rbg / nrb / g.heads;
     bh = (size_t)b * g.heads + h;
     r = rb * XROWS + rl;
-    live = r < g.Qs;
-    wlive = rb * XROWS + 16 * wave < g.Qs;
+    // only the rows whose candidate list overflowed; a segment without one is skipped
+    live = r < g.Qs && ccnt[bh * g.Qs + r] > VSA_EXTRA_CAND;
+    if (!__syncthreads_or(live)) continue;
+    wlive = __ballot(live) != 0ull;
     {
       const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? r : 0)) * VSA_HEAD_DIM);
 #pragma unroll
@@ -532,18 +546,432 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   }
 }
 
-// One workgroup per (sparse row, head, batch).  Wave 0 merges the row's segment lists: the
-// best E of their union by the 64-bit order key (keys are unique: the tokens differ), then
-// ranks them by token and writes the row's extra tokens and count.  Then thread tid copies
-// 64 bytes of extra row tid >> 2 (zeros past the count) of K and of V.
+// Pass 1 of the two-pass select.  Per (sparse row, tile): M1, the row's best score among
+// the tile's eligible keys, and M4, the least of the four lanes' best (each lane holds 16 of
+// the 64 keys, so at least four keys score >= M4); both -inf for a tile in the row's list.
+// One workgroup per (batch x head, tile chunk, 64-row block): the tiles are cut into xs1
+// chunks, and the row blocks of one chunk get consecutive logical ids, dealt to one XCD so
+// that they stream the same key tiles through its L2 together.  Key tiles come into a ring of three
+// LDS buffers by buffer-to-LDS loads issued two tiles ahead (each wave four 1 KB loads per
+// tile, padding rows of a partial prefix tile read out of range and so as zeros), with one
+// barrier per tile; 48 KB of LDS and no staging registers, so three workgroups fit a CU.
+constexpr int XNB = 3;
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 lane (M0 holds the LDS base).
+// Written as asm so that the compiler neither waits for it before unrelated LDS reads nor
+// counts it: the kernel waits for these loads itself.  Nothing else in the kernel uses M0.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+template <int N>
+using IC = std::integral_constant<int, N>;
+__global__ __launch_bounds__(256) void vsa_extra_tmax_kernel(VsaGeom g, const char* __restrict__ kp,
+                                                             const float* __restrict__ qbar,
+                                                             const int* __restrict__ lists,
+                                                             const int* __restrict__ counts,
+                                                             float* __restrict__ tm1, float* __restrict__ tm4,
+                                                             int* __restrict__ ccnt, u32x4* __restrict__ qsplit) {
+  __shared__ __attribute__((aligned(16))) char kring[XNB][64 * 256];
+  __shared__ unsigned xbits[XROWS][8];  // listed tiles of each row among the current 256
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
+  const int nrb = (g.Qs + XROWS - 1) / XROWS;
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
+  const int rl = 16 * wave + ql;
+  const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
+  const unsigned nrec = (unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2;
+  // this lane's share of a tile's loads: wave w moves rows 4 w + 16 m + (lane >> 4), m = 0..3,
+  // i.e. (dt, dh, dw) = (m, w, lane >> 4) of a video tile; its 16 bytes land at position
+  // lane & 15 of the row, which holds chunk (lane & 15) ^ (row & 15)
+  const unsigned chunk = (unsigned)((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 16u;
+  const unsigned vrow = (unsigned)(wave * g.W + (lane >> 4));  // (dh, dw) offset in tokens
+  const unsigned plane = (unsigned)(g.H * g.W);
+
+  {
+    const int rb = w % nrb;
+    const int tch = (w / nrb) % g.xs1;  // the tile chunk
+    const int bhl = w / nrb / g.xs1;
+    const int h = bhl % g.heads, b = bhl / g.heads;
+    const size_t bh = (size_t)b * g.heads + h;
+    const int t0 = (int)((long long)tch * g.Tq / g.xs1);
+    const int t1 = (int)((long long)(tch + 1) * g.Tq / g.xs1);
+    const int r = rb * XROWS + rl;
+    const bool live = r < g.Qs;
+    const bool wlive = rb * XROWS + 16 * wave < g.Qs;
+    bf16x8 qs[3][4];
+    {
+      const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? r : 0)) * VSA_HEAD_DIM);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x4 a = live ? qp[8 * ks + 2 * grp] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 c = live ? qp[8 * ks + 2 * grp + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 hi3, mid3, lo3;
+          split3(x[e], hi3, mid3, lo3);
+          qs[0][ks][e] = hi3;
+          qs[1][ks][e] = mid3;
+          qs[2][ks][e] = lo3;
+        }
+      }
+    }
+    // the row's three bf16 terms of qbar, in the lane order of the MFMA operands, for pass 2
+    if (tch == 0 && live) {
+      // layout per row: (term, ks, grp) at 16 term + 4 ks + grp, 16 bytes each
+      u32x4* qo = qsplit + (bh * g.Qs + r) * 48 + grp;
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qo[16 * pp + 4 * ks] = __builtin_bit_cast(u32x4, qs[pp][ks]);
+    }
+    const int* lst = lists + (bh * g.Qs + (live ? r : 0)) * g.cap;
+    const int cnt_l = live ? counts[bh * g.Qs + r] : 0;
+    int cur;
+    {
+      int a = 0, c = cnt_l;
+      while (a < c) {
+        const int m = (a + c) >> 1;
+        if (lst[m] < t0) a = m + 1;
+        else c = m;
+      }
+      cur = a;
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kp + ((size_t)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2)), 0, (int)nrec, 0x00020000);
+    // the loads of tile `tw` into ring buffer bi (four 1 KB loads of this wave)
+    auto issue = [&](const TileWalk& tw, auto bic) {
+      constexpr int BI = decltype(bic)::value;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 4 * wave + 16 * m + (lane >> 4);
+        unsigned off;
+        if (tw.video) off = (unsigned)(tw.tok0 + m * (int)plane + (int)vrow) * rowbytes + chunk;
+        else off = row < tw.nv ? (unsigned)(tw.tok0 + row) * rowbytes + chunk : nrec;
+        lds_dma16(rs, off, (unsigned)(size_t)(kring[BI] + 1024 * (wave + 4 * m)));
+      }
+    };
+    TileWalk wc, wf;
+    walk_seek(g, wc, t0);
+    wf = wc;
+    issue(wf, IC<0>{});
+    if (t0 + 1 < t1) walk_next(g, wf);
+    issue(wf, IC<1>{});
+    // one tile from ring buffer BI (a constant, so that the compiler can tell the buffer
+    // read from the one being loaded and adds no wait for the loads in flight)
+    auto step = [&](int t, auto bic) {
+      constexpr int BI = decltype(bic)::value;
+      const int i = t - t0;
+      if ((i & 255) == 0) {
+        // the row's listed tiles among the next 256, as bits (by the row's grp-0 lane; the
+        // wave's other lanes read them after this wave's LDS writes)
+        unsigned* xm = xbits[rl];
+        if (grp == 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xm[j] = 0u;
+          while (cur < cnt_l) {
+            const int x = lst[cur];
+            if (x >= t + 256) break;
+            atomicOr(&xm[(x - t) >> 5], 1u << ((x - t) & 31));
+            ++cur;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      }
+      // Wait for this wave's loads of tile t: the loads issued after them are the next
+      // tile's four and, in a wave with live rows, the two stores of each tile since.  A
+      // plain barrier would make the compiler wait for every load in flight first; the bare
+      // barrier between two compiler fences does not.
+      if (i == 0 || !wlive) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if (i == 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // tile t is in LDS; every wave is done with tile t - 1
+      asm volatile("" ::: "memory");
+      const bool excl = (xbits[rl][(i & 255) >> 5] >> (i & 31)) & 1u;
+      if (t + 2 < t1) walk_next(g, wf);
+      issue(wf, IC<(BI + 2) % XNB>{});  // into the buffer tile t - 1 held
+      if (wlive) {
+        const char* kt = kring[BI];
+        f32x4 acc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 a[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
+#pragma unroll
+          for (int pp = 2; pp >= 0; --pp)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kb], qs[pp][ks], acc[kb], 0, 0, 0);
+        }
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = acc[e >> 2][e & 3];
+        if (!wc.video) {  // padding keys of a partial prefix tile take no part
+          const int nv = wc.nv;
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (16 * (e >> 2) + 4 * grp + (e & 3) >= nv) z[e] = -INFINITY;
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
+        if (!live || excl) mx = -INFINITY;
+        int rv[4];
+        row_values4(__float_as_int(mx), rv);
+        const float a0 = __int_as_float(rv[0]), a1 = __int_as_float(rv[1]);
+        const float a2 = __int_as_float(rv[2]), a3 = __int_as_float(rv[3]);
+        if (grp == 0 && live) {
+          const size_t o = (bh * g.Qs + r) * (size_t)g.Tq + t;
+          tm1[o] = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+          tm4[o] = fminf(fminf(a0, a1), fminf(a2, a3));
+          if (t == 0) ccnt[bh * g.Qs + r] = 0;  // the row's candidate count, for pass 2
+        }
+      }
+      walk_next(g, wc);
+    };
+    int t = t0;
+    for (; t + 2 < t1; t += 3) {
+      step(t, IC<0>{});
+      step(t + 1, IC<1>{});
+      step(t + 2, IC<2>{});
+    }
+    if (t < t1) step(t, IC<0>{});
+    if (t + 1 < t1) step(t + 1, IC<1>{});
+  }
+}
+
+template <int NC>
+__global__ __launch_bounds__(64) void vsa_extra_thr_kernel(VsaGeom g, const float* __restrict__ tm1,
+                                                           const float* __restrict__ tm4,
+                                                           float* __restrict__ xthr,
+                                                           unsigned* __restrict__ xmask) {
+  const int s = blockIdx.x, lane = threadIdx.x;
+  const size_t bh = blockIdx.y;
+  const int Tq = g.Tq, E = g.extra, E4 = (g.extra + 3) / 4;
+  const int nc = (Tq + 63) / 64;
+  const float* m1 = tm1 + (bh * g.Qs + s) * (size_t)Tq;
+  const float* m4 = tm4 + (bh * g.Qs + s) * (size_t)Tq;
+  unsigned k1[NC], k4[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int t = 64 * j + lane;
+    const float a = j < nc && t < Tq ? m1[t] : -INFINITY;
+    const float c = j < nc && t < Tq ? m4[t] : -INFINITY;
+    k1[j] = a == -INFINITY ? 0u : order_key(a);  // 0: absent (every present key is above 0)
+    k4[j] = c == -INFINITY ? 0u : order_key(c);
+  }
+  auto counts = [&](unsigned c1, unsigned c4, int& n1, int& n4) {
+    n1 = 0;
+    n4 = 0;
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      if (j < nc) {
+        n1 += __popcll(__ballot(k1[j] >= c1));
+        n4 += __popcll(__ballot(k4[j] >= c4));
+      }
+  };
+  int h1, h4;
+  counts(1u, 1u, h1, h4);
+  // The top 16 bits of the keys only: the threshold then sits at most one step of the 16-bit
+  // prefix (2^-7 of its value) below the exact order statistic, still a lower bound.
+  unsigned p1 = 0u, p4 = 0u;
+  for (int bit = 31; bit >= 16; --bit) {
+    int n1, n4;
+    counts(p1 | (1u << bit), p4 | (1u << bit), n1, n4);
+    if (n1 >= E) p1 |= 1u << bit;
+    if (n4 >= E4) p4 |= 1u << bit;
+  }
+  const unsigned kt = max(h1 >= E ? p1 : 0u, h4 >= E4 ? p4 : 0u);
+  float T = -INFINITY;
+  if (kt != 0u) T = __uint_as_float((kt & 0x80000000u) ? (kt & 0x7fffffffu) : ~kt);
+  if (lane == 0) xthr[bh * g.Qs + s] = T;
+  const int nw = (Tq + 31) / 32;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+    if (j < nc) {
+      const unsigned long long m = __ballot(k1[j] != 0u && k1[j] >= kt);
+      if (lane == 0) {
+        xmask[(bh * nw + 2 * j) * g.Qs + s] = (unsigned)m;
+        if (2 * j + 1 < nw) xmask[(bh * nw + 2 * j + 1) * g.Qs + s] = (unsigned)(m >> 32);
+      }
+    }
+}
+
+// Pass 2: one workgroup per (tile, batch x head).  The rows that have the tile among their
+// candidates are gathered (in row order) from the masks; each wave scores groups of 16 of
+// them against the tile's keys on the MFMAs (the same three-term products as pass 1), and a
+// key scoring >= its row's T is appended to the row's candidate list (its slot from an atomic
+// count; past VSA_EXTRA_CAND the count keeps growing but nothing is written).
+__global__ __launch_bounds__(256, 3) void vsa_extra_score_kernel(VsaGeom g, const u32x4* __restrict__ k,
+                                                              const float* __restrict__ xthr,
+                                                              const unsigned* __restrict__ xmask,
+                                                              int* __restrict__ ccnt,
+                                                              unsigned long long* __restrict__ xcand,
+                                                              const u32x4* __restrict__ qsplit) {
+  __shared__ __attribute__((aligned(16))) char ktile[64 * 256];
+  __shared__ int nrows_s;
+  extern __shared__ int rowlist[];  // Qs entries
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
+  const int t = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int b = (int)(bh / g.heads), h = (int)(bh % g.heads);
+  const int nw = (g.Tq + 31) / 32;
+  // the tile's keys: loads first, so that they are in flight during the row scan
+  TileWalk tw;
+  walk_seek(g, tw, t);
+  u32x4 kreg[4];
+  unsigned kvalid = 0u;
+  {
+    const int hw = g.H * g.W;
+    const int fdhw = ((tid >> 6) & 3) * g.W + ((tid >> 4) & 3);
+    const u32x4* kbh = k + (((size_t)b * g.N) * g.heads + h) * (VSA_HEAD_DIM / 8) + (tid & 15);
+    const int tokstride = g.heads * (VSA_HEAD_DIM / 8);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int rr = (tid >> 4) + 16 * m;
+      const bool valid = tw.video || rr < tw.nv;
+      const int tok = tw.tok0 + (tw.video ? m * hw + fdhw : (valid ? rr : 0));
+      kreg[m] = kbh[(size_t)tok * tokstride];
+      kvalid |= (unsigned)valid << m;
+    }
+  }
+  // the rows that have this tile among their candidates (any order: every wave appends its
+  // 64-row chunks through an LDS count)
+  if (tid == 0) nrows_s = 0;
+  __syncthreads();
+  {
+    const unsigned* mk = xmask + (bh * nw + (t >> 5)) * g.Qs;
+    for (int base = 64 * wave; base < g.Qs; base += 256) {
+      const int s = base + lane;
+      const bool in = s < g.Qs && ((mk[s] >> (t & 31)) & 1u);
+      const unsigned long long m = __ballot(in);
+      int at = 0;
+      if (m != 0ull && lane == 0) at = atomicAdd(&nrows_s, __popcll(m));
+      at = __shfl(at, 0);
+      if (in) rowlist[at + lanes_below(m)] = s;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int rr = (tid >> 4) + 16 * m;
+    *reinterpret_cast<u32x4*>(ktile + 256 * rr + 16 * ((tid & 15) ^ (rr & 15))) =
+        ((kvalid >> m) & 1u) ? kreg[m] : u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  const int n = nrows_s;
+  if (n == 0) return;
+  const int tokl = tw.tok0 + (tw.video ? grp * g.W : 4 * grp);  // key e: tokl + (video ? kb hw + i : 16 kb + i)
+  const int kstep = tw.video ? g.H * g.W : 16;
+  const int ngroups = (n + 15) / 16;
+  for (int gi = wave; gi < ngroups; gi += 4) {
+    const int idx = 16 * gi + ql;
+    const bool live = idx < n;
+    const int s = rowlist[live ? idx : 0];
+    bf16x8 qs[3][4];
+    {
+      const u32x4* qi = qsplit + (bh * g.Qs + s) * 48 + grp;
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qs[pp][ks] = as_bf16x8(qi[16 * pp + 4 * ks]);
+    }
+    const float T = live ? xthr[bh * g.Qs + s] : INFINITY;
+    f32x4 acc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(ktile + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
+#pragma unroll
+      for (int p = 2; p >= 0; --p)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kb], qs[p][ks], acc[kb], 0, 0, 0);
+    }
+    float z[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] = acc[e >> 2][e & 3];
+    if (!tw.video) {  // padding keys get a NaN, which never passes
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (16 * (e >> 2) + 4 * grp + (e & 3) >= tw.nv) z[e] = __builtin_nanf("");
+    }
+    unsigned ge = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ge |= (unsigned)(z[e] >= T) << e;
+    const int c = __popc(ge);
+    int slot = 0;
+    if (c > 0) slot = atomicAdd(&ccnt[bh * g.Qs + s], c);
+    unsigned long long* dst = xcand + (bh * g.Qs + s) * (size_t)VSA_EXTRA_CAND;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool in = (ge >> e) & 1u;
+      if (__ballot(in) != 0ull) {
+        if (in) {
+          if (slot < VSA_EXTRA_CAND) dst[slot] = entry(z[e], tokl + (e >> 2) * kstep + (e & 3));
+          ++slot;
+        }
+      }
+    }
+  }
+}
+
+// The keep-th largest of n unique 64-bit order keys in LDS (keep <= n): the high words by a
+// bitwise ballot search, then, only where several keys share the boundary's high word, the
+// low words among those.  One wave.
+__device__ unsigned long long kth_key(const unsigned long long* keys, int n, int keep, int lane) {
+  auto count = [&](unsigned ph, unsigned pl, int mode) {  // 0: hi >= ph; 1: hi > ph; 2: hi == ph (and lo >= pl)
+    int c = 0;
+    for (int j = 0; j < n; j += 64) {
+      const unsigned long long x = j + lane < n ? keys[j + lane] : 0ull;
+      const unsigned xh = (unsigned)(x >> 32), xl = (unsigned)x;
+      const bool in = j + lane < n &&
+                      (mode == 0 ? xh >= ph : mode == 1 ? xh > ph : (xh == ph && xl >= pl));
+      c += __popcll(__ballot(in));
+    }
+    return c;
+  };
+  unsigned ph = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned cand = ph | (1u << bit);
+    if (count(cand, 0u, 0) >= keep) ph = cand;
+  }
+  const int need = keep - count(ph, 0u, 1);
+  unsigned pl = 0u;
+  if (count(ph, 0u, 2) > need) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned cand = pl | (1u << bit);
+      if (count(ph, cand, 2) >= need) pl = cand;
+    }
+  }
+  return ((unsigned long long)ph << 32) | pl;
+}
+
+// One workgroup per (sparse row, head, batch).  Wave 0 picks the row's extra tokens: the best
+// E of its candidate list by the 64-bit order key (keys are unique: the tokens differ), or,
+// for a row whose list overflowed, of the union of the fallback's segment lists.  It ranks them
+// by token and writes the row's extra tokens and count.  Then thread tid copies 64 bytes of
+// extra row tid >> 2 (zeros past the count) of K and of V.
 __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const u32x4* __restrict__ k,
                                                                const u32x4* __restrict__ v,
+                                                               const int* __restrict__ ccnt,
+                                                               const unsigned long long* __restrict__ xcand,
                                                                const unsigned long long* __restrict__ xpart,
                                                                const int* __restrict__ xpcnt,
                                                                int* __restrict__ xtok,
                                                                int* __restrict__ xcnt,
                                                                u32x4* __restrict__ kx,
                                                                u32x4* __restrict__ vx) {
+  __shared__ unsigned long long ckey[VSA_EXTRA_CAND];
   __shared__ unsigned long long mbuf[VSA_MAX_EXTRA];
   __shared__ int mtok[VSA_MAX_EXTRA];
   __shared__ int stok[VSA_MAX_EXTRA];
@@ -553,39 +981,58 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int E = g.extra;
-    const int nrb = (g.Qs + XROWS - 1) / XROWS;
-    const long long TS = (long long)nrb * g.heads * g.batch * g.Tq;
-    const int G = g.xg;
-    const int rbg = (b * g.heads + h) * nrb + s / XROWS, rw = s % XROWS;
-    const int w0 = xwg_of((long long)rbg * g.Tq, TS, G);
-    const int w1 = xwg_of((long long)(rbg + 1) * g.Tq - 1, TS, G);
-    size_t pr = (size_t)rbg * g.xms * XROWS + rw;
-    int n = xpcnt[pr];
-    unsigned long long e0 = lane < n ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
-    for (int sg = 1; sg <= w1 - w0; ++sg) {
-      pr = ((size_t)rbg * g.xms + sg) * XROWS + rw;
-      const int n1 = xpcnt[pr];
-      const unsigned long long e1 = lane < n1 ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
-      const bool v0 = lane < n, v1 = lane < n1;
-      const unsigned long long k0 = v0 ? entry_key(e0) : 0ull, k1 = v1 ? entry_key(e1) : 0ull;
-      const int keep = min(E, n + n1);
-      // the keep-th largest key, bit by bit from the top (an empty slot's 0 is below all)
-      unsigned long long pre = 0ull;
-      for (int bit = 63; bit >= 0; --bit) {
-        const unsigned long long cand = pre | (1ull << bit);
-        const int c = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
-        if (c >= keep) pre = cand;
+    const int cc = ccnt[ro];
+    int n;
+    unsigned long long e0;  // the lane's kept entry (its low word is ~token)
+    if (cc <= VSA_EXTRA_CAND) {
+      const unsigned long long* cand = xcand + ro * VSA_EXTRA_CAND;
+      for (int j = lane; j < cc; j += 64) ckey[j] = entry_key(cand[j]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): one wave, its writes are in LDS
+      n = min(E, cc);
+      const unsigned long long pre = n > 0 ? kth_key(ckey, cc, n, lane) : ~0ull;
+      int at = 0;
+      for (int j = 0; j < cc; j += 64) {
+        const unsigned long long x = j + lane < cc ? ckey[j + lane] : 0ull;
+        const bool sel = j + lane < cc && x >= pre;
+        const unsigned long long m = __ballot(sel);
+        if (sel) mbuf[at + lanes_below(m)] = x;
+        at += __popcll(m);
       }
-      const bool s0 = v0 && k0 >= pre, s1 = v1 && k1 >= pre;
-      const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
-      if (s0) mbuf[lanes_below(b0)] = e0;
-      if (s1) mbuf[__popcll(b0) + lanes_below(b1)] = e1;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's writes are in LDS
-      n = keep;
+      __builtin_amdgcn_s_waitcnt(0xc07f);
       e0 = lane < n ? mbuf[lane] : 0ull;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read before the next writes
+    } else {
+      // the fallback's segment lists: the top E of their union, pairwise
+      const int nrb = (g.Qs + XROWS - 1) / XROWS;
+      const long long TS = (long long)nrb * g.heads * g.batch * g.Tq;
+      const int G = g.xg;
+      const int rbg = (b * g.heads + h) * nrb + s / XROWS, rw = s % XROWS;
+      const int w0 = xwg_of((long long)rbg * g.Tq, TS, G);
+      const int w1 = xwg_of((long long)(rbg + 1) * g.Tq - 1, TS, G);
+      size_t pr = (size_t)rbg * g.xms * XROWS + rw;
+      n = xpcnt[pr];
+      e0 = lane < n ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
+      for (int sg = 1; sg <= w1 - w0; ++sg) {
+        pr = ((size_t)rbg * g.xms + sg) * XROWS + rw;
+        const int n1 = xpcnt[pr];
+        const unsigned long long e1 = lane < n1 ? xpart[pr * VSA_MAX_EXTRA + lane] : 0ull;
+        ckey[lane] = lane < n ? entry_key(e0) : 0ull;
+        ckey[64 + lane] = lane < n1 ? entry_key(e1) : 0ull;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        // both lists padded to 64 with empty keys (0, below every real key)
+        const int keep = min(E, n + n1);
+        const unsigned long long pre = keep > 0 ? kth_key(ckey, 128, keep, lane) : ~0ull;
+        const unsigned long long k0 = ckey[lane], k1 = ckey[64 + lane];
+        const bool s0 = lane < n && k0 >= pre, s1 = lane < n1 && k1 >= pre;
+        const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
+        if (s0) mbuf[lanes_below(b0)] = e0;
+        if (s1) mbuf[__popcll(b0) + lanes_below(b1)] = e1;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        n = keep;
+        e0 = lane < n ? mbuf[lane] : 0ull;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // every lane has read before the next writes
+      }
     }
-    // rank by token and write ascending
+  // rank by token and write ascending
     const int mytok = lane < n ? ~(int)(unsigned)e0 : 0;
     mtok[lane] = mytok;
     __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -630,12 +1077,24 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
 }  // namespace
 
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
-                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, void* xpart, int* xpcnt,
-                      hipStream_t st) {
+                      const int* counts, const VsaExtraBuffers& x, hipStream_t st) {
   if (g.Qs == 0 || g.extra == 0) return;
+  const int BH = g.heads * g.batch;
+  hipLaunchKernelGGL(vsa_extra_tmax_kernel, dim3((g.Qs + XROWS - 1) / XROWS * BH * g.xs1), dim3(256), 0, st, g,
+                     (const char*)k, qbar, lists, counts, x.tm1, x.tm4, x.ccnt, (u32x4*)x.qsplit);
+  {
+    const int nc = (g.Tq + 63) / 64;
+    auto thr = nc <= 16 ? vsa_extra_thr_kernel<16> : nc <= 32 ? vsa_extra_thr_kernel<32>
+             : nc <= 64 ? vsa_extra_thr_kernel<64> : vsa_extra_thr_kernel<128>;
+    hipLaunchKernelGGL(thr, dim3(g.Qs, BH), dim3(64), 0, st, g, (const float*)x.tm1, (const float*)x.tm4, x.thr,
+                       x.mask);
+  }
+  hipLaunchKernelGGL(vsa_extra_score_kernel, dim3(g.Tq, BH), dim3(256), 4 * g.Qs, st, g, (const u32x4*)k,
+                     (const float*)x.thr, (const unsigned*)x.mask, x.ccnt, x.cand, (const u32x4*)x.qsplit);
   hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(g.xg), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
-                     (unsigned long long*)xpart, xpcnt);
+                     (const int*)x.ccnt, x.part, x.pcnt);
   hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(256), 0, st, g,
-                     (const u32x4*)k, (const u32x4*)v, (const unsigned long long*)xpart, xpcnt, xtok, xcnt,
-                     (u32x4*)kx, (u32x4*)vx);
+                     (const u32x4*)k, (const u32x4*)v, (const int*)x.ccnt, (const unsigned long long*)x.cand,
+                     (const unsigned long long*)x.part, (const int*)x.pcnt, x.xtok, x.xcnt, (u32x4*)x.kx,
+                     (u32x4*)x.vx);
 }

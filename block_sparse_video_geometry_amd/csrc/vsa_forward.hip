@@ -134,8 +134,20 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   int* xcnt = reinterpret_cast<int*>(ws + L.xcnt);
   void* kx = ws + L.kx;
   void* vx = ws + L.vx;
-  void* xpart = ws + L.xpart;
-  int* xpcnt = reinterpret_cast<int*>(ws + L.xpcnt);
+  VsaExtraBuffers xb;
+  xb.tm1 = reinterpret_cast<float*>(ws + L.xtm1);
+  xb.tm4 = reinterpret_cast<float*>(ws + L.xtm4);
+  xb.thr = reinterpret_cast<float*>(ws + L.xthr);
+  xb.mask = reinterpret_cast<unsigned*>(ws + L.xmask);
+  xb.ccnt = reinterpret_cast<int*>(ws + L.xccnt);
+  xb.cand = reinterpret_cast<unsigned long long*>(ws + L.xcand);
+  xb.qsplit = ws + L.xqsplit;
+  xb.part = reinterpret_cast<unsigned long long*>(ws + L.xpart);
+  xb.pcnt = reinterpret_cast<int*>(ws + L.xpcnt);
+  xb.xtok = xtok;
+  xb.xcnt = xcnt;
+  xb.kx = kx;
+  xb.vx = vx;
   void* o_user = o;
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
@@ -178,7 +190,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     VSA_STEP("coarse", vsa_launch_coarse(G, qbar, kbar, vbar, bias, scores, ocoarse, statp, cpart, st));
     if (G.select == VSA_SELECT_TAU) VSA_STEP("tau", vsa_launch_tau(G, statp, thr, st));
     VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
-    if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xtok, xcnt, kx, vx, xpart, xpcnt, st));
+    if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xb, st));
   }
   VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, kx, vx, xcnt, st));
   if (G.reblock) VSA_STEP("unpermute", vsa_launch_rb_unpermute(G, rb_tiles, o, o_user, st));

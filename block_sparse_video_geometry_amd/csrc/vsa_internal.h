@@ -45,16 +45,22 @@ struct VsaGeom {
   int32_t rb_nsplit;                       // tile ranges per (batch, head) of the key-moment sums
   int32_t xg;                              // extra-token select workgroups (equal step ranges)
   int32_t xms;                             // most segments (workgroups) a 64-row block spans
+  int32_t xs1;                             // extra-token pass 1: tile chunks per row block
 };
 
 // The extra-token select runs this many workgroups at most: two per CU of the 256-CU part,
 // each holding 80 KB of LDS.
 constexpr int VSA_EXTRA_WGS = 512;
+// Candidate entries kept per sparse row by the two-pass extra-token select; a row with more
+// takes the streaming fallback.
+constexpr int VSA_EXTRA_CAND = 1024;
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
   size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
   size_t xpart, xpcnt;        // extra tokens: per-segment best E of each row, and counts
+  size_t xtm1, xtm4, xthr, xmask, xccnt, xcand;  // two-pass select: maxima, thresholds, candidates
+  size_t xqsplit;                                // two-pass select: qbar as three bf16 terms
   size_t cpart;               // coarse partials per (row, slice): max, sum, 2 pad, O[128]
   // Spark-Reblock: key-moment partials and M (fp32, bf16 hi/lo), video-token norms, token
   // lists (ping-pong; `tiles` is the final one), projections, pass partials, node states,

@@ -34,9 +34,19 @@ void vsa_launch_select(const VsaGeom& g, const float* scores, const float* thr, 
 
 // Extra tokens per sparse row (best pooled-query scores outside the listed tiles): ids
 // ascending and counts, and their K / V rows staged [batch, Qs, 64, heads, 128].
+struct VsaExtraBuffers {
+  float *tm1, *tm4, *thr;      // per (row, tile) maxima; per row threshold
+  unsigned* mask;              // candidate tiles, [bh][tile / 32][row]
+  int* ccnt;                   // candidate counts
+  unsigned long long* cand;    // candidate entries, VSA_EXTRA_CAND per row
+  void* qsplit;                // per row: qbar as three bf16 terms in MFMA operand order
+  unsigned long long* part;    // fallback: per-segment best E of each row
+  int* pcnt;
+  int *xtok, *xcnt;            // the extra tokens and their count per row
+  void *kx, *vx;               // staged K and V rows
+};
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
-                      const int* counts, int* xtok, int* xcnt, void* kx, void* vx, void* xpart, int* xpcnt,
-                      hipStream_t st);
+                      const int* counts, const VsaExtraBuffers& x, hipStream_t st);
 
 // Spark-Reblock mapper: M, norms and the tree levels; returns the final token list
 // ([batch, heads, Vt, 64] packed token ids, leaf j = video tile j).

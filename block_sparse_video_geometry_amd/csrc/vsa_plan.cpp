@@ -157,10 +157,16 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     delete p;
     return VSA_ERR_UNSUPPORTED;
   }
+  // the extra-token threshold kernel holds a row's per-tile keys in registers: 8192 tiles at most
+  if (g.extra > 0 && g.Tq > 64 * 128) {
+    delete p;
+    return VSA_ERR_UNSUPPORTED;
+  }
   // Extra-token select: the (64-row block, tile) steps split evenly over xg workgroups (at
   // least 64 steps each); xms is the most workgroups whose ranges meet one row block.
   g.xg = 0;
   g.xms = 0;
+  g.xs1 = 0;
   if (g.extra > 0 && g.Qs > 0) {
     const int64_t nrb = (g.Qs + 63) / 64;
     const int64_t NRB = nrb * heads * batch;
@@ -171,6 +177,8 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     for (int64_t r = 0; r < NRB; ++r) ms = std::max(ms, wg_of((r + 1) * g.Tq - 1) - wg_of(r * g.Tq) + 1);
     g.xg = (int32_t)G;
     g.xms = (int32_t)ms;
+    // about three rounds of three workgroups per CU, chunks of at least 32 tiles
+    g.xs1 = (int32_t)std::max<int64_t>(1, std::min<int64_t>((g.Tq + 31) / 32, (9 * VSA_EXTRA_WGS / 2 + NRB - 1) / NRB));
   }
   g.sink = o.sink;
   g.select = o.select;
@@ -222,6 +230,14 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     const size_t xrb = g.extra > 0 ? BH * (size_t)((g.Qs + 63) / 64) * g.xms * 64 : 0;  // segment rows
     L.xpart = take(xrb * VSA_MAX_EXTRA * 8);
     L.xpcnt = take(xrb * 4);
+    const size_t xr = g.extra > 0 ? BH * (size_t)g.Qs : 0;  // sparse rows
+    L.xtm1 = take(xr * g.Tq * 4);
+    L.xtm4 = take(xr * g.Tq * 4);
+    L.xthr = take(xr * 4);
+    L.xmask = take(xr * ((g.Tq + 31) / 32) * 4);
+    L.xccnt = take(xr * 4);
+    L.xcand = take(xr * VSA_EXTRA_CAND * 8);
+    L.xqsplit = take(xr * 3 * VSA_HEAD_DIM * 2);
   }
   L.cpart = take(g.csplit > 1 ? BH * (size_t)g.Qs * g.csplit * (VSA_HEAD_DIM + 4) * 4 : 0);
   {

@@ -207,6 +207,35 @@ def test_extra_tokens_exact_ties():
     print(f"[ties] extra tokens: rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
 
 
+def test_extra_tokens_overflow_fallback():
+    """Every video key is one and the same vector, so every row's scores all tie: the
+    two-pass select's candidate list then holds every eligible key (more than it keeps
+    per row), so each row takes the streaming fallback.  The extra tokens must be the E
+    lowest eligible token ids, as the oracle picks them, with no adoption."""
+    w = Workload("extra_overflow", 2, ((SEG_TEXT, 64),), (8, 16, 16), 25.0, SINK_EXACT_KV, seed=100,
+                 recipe="scaled", extra=64)
+    x = make_inputs(w)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    vid = np.concatenate([geom.tiles[t] for t in range(geom.n_prefix, geom.n_tiles)])
+    k = x["k"].copy()
+    k[:, vid] = x["k"][:, vid[:1]]
+    x = dict(x, k=k)
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    d = plan.desc
+    eligible = (geom.n_tiles - geom.n_prefix - d.k) * 64
+    assert eligible > 1024, "the case must overflow the per-row candidate list"
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, want_intermediates=True,
+                         extra_tokens=w.extra)
+    for (b, h), it in inter.items():
+        for i in it["sparse_rows"]:
+            xc = int(gpu["xcnt"][b, h, i])
+            gx = gpu["xtok"][b, h, i, :xc].astype(np.int64)
+            assert np.array_equal(gx, it["extras"][i]), f"(b{b},h{h}) row {i}: {gx[:8]} != {it['extras'][i][:8]}"
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[overflow] extra tokens: rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
+
+
 def test_parity_no_gate():
     w = scaled_down(WORKLOADS["full"], heads=2, grid=(8, 16, 16), name="nogate")
     x = make_inputs(w)
