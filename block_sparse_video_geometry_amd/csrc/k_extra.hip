@@ -8,35 +8,35 @@
 // z = s qbar_i . k_t (no tile bias); over the valid tokens of the tiles not in
 // i's list the E largest are kept, equal scores to the lower packed token index.
 //
-// The select runs in two passes over the keys, scored the same way in both:
-//   z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split exactly into
-//   three bf16 terms hi + mid + lo, so the products are exact and only the fp32
-//   accumulation rounds (a plain bf16 qbar would move logits by ~2^-9 of their size).
-//   Keys are ranked by these raw dot products; the positive scale s does not change the
-//   order.  A tile in the row's list, and the padding rows of a partial prefix tile, take
-//   no part.
-// vsa_extra_tmax_kernel (pass 1): every (sparse row, tile) pair once, keeping only M1, the
-//   row's best score in the tile, and M4, the least of the four lane maxima (four keys of the
-//   tile score at least that).  One workgroup per (head, tile chunk, 64-row block), key tiles
-//   staged by buffer-to-LDS loads two tiles ahead.
-// vsa_extra_thr_kernel: per row T = max(E-th largest M1, ceil(E/4)-th largest M4), read from
-//   the top 16 bits of the order keys: a lower bound of the row's E-th best score (E tiles
-//   hold a key >= the one, ceil(E/4) tiles four keys >= the other).  The row's E best keys
-//   then all lie in its candidate tiles, those with M1 >= T, which are recorded as bits.
-// vsa_extra_score_kernel (pass 2): per (tile, head), the rows with the tile among their
-//   candidates, 16 to an MFMA group; every key scoring >= its row's T is appended to the row's
-//   candidate list (an atomic count gives the slot).  About E + a few keys per row on the
-//   pages' workloads; the list keeps VSA_EXTRA_CAND.
+// The exact score: z^T (64 keys x 16 rows) = K qbar^T on the bf16 MFMAs, with qbar split
+// exactly into three bf16 terms hi + mid + lo, so the products are exact and only the fp32
+// accumulation rounds (a plain bf16 qbar would move logits by ~2^-9 of their size).  Keys are
+// ranked by these raw dot products; the positive scale s does not change the order.  A tile in
+// the row's list, and the padding rows of a partial prefix tile, take no part.  The select
+// runs in two passes over the keys:
+// vsa_extra_tmax_kernel (pass 1, a screen): every (sparse row, tile) pair once, scored with hi
+//   alone (a third of the MFMAs), keeping only M1, the row's best screening score in the tile,
+//   and M4, the least of the four lane maxima (four keys of the tile score at least that).
+//   One workgroup per (head, tile chunk, 128-row block), key tiles staged by buffer-to-LDS
+//   loads two tiles ahead; M1 / M4 stored [bh][tile][row], one coalesced store per wave and tile.
+// vsa_extra_thr_kernel: eps bounds the screen's error against the exact score per (row, tile)
+//   (from |qbar - hi| and the tile's largest key norm, written by the pool step).  Per row
+//   T = max(E-th largest M1 - eps, ceil(E/4)-th largest M4 - eps), read from the top 16 bits
+//   of the order keys: a lower bound of the row's E-th best exact score (E tiles hold a key
+//   >= the one, ceil(E/4) tiles four keys >= the other).  The row's E best keys then all lie
+//   in its candidate tiles, those with M1 + eps >= T, which are recorded as bits.
+// vsa_extra_score_kernel (pass 2): per (two tiles, head), the rows with a tile among their
+//   candidates, 16 to an MFMA group, scored exactly; every key scoring >= its row's T is
+//   appended to the row's candidate list (an atomic count gives the slot).  About E + a few
+//   keys per row on the pages' workloads; the list keeps VSA_EXTRA_CAND.
 // vsa_extra_select_kernel (fallback): a row whose list overflowed (heavy exact ties, say) is
 //   selected by streaming every key tile with a running threshold (described at the kernel);
 //   segments with no such row are skipped, so the kernel costs ~8 us when none overflowed.
 // vsa_extra_gather_kernel: the exact best E of the row's candidates (or of the fallback's
 //   partial lists) by (score, then lower token), ranked by token.
-// Measured on the 36,096-token, 32-head workload at E = 64: pass 1 0.49 ms, threshold 0.05,
-// pass 2 0.27, fallback 0.01 (1.69 ms before as one streaming pass).  Pass 1 runs its MFMAs
-// about half the time: every wave reads the whole 16 KB key tile from LDS for its 16 rows, so
-// the LDS reads come close to the MFMA time; pass 2 re-reads a row's split qbar for each of
-// its ~64 candidate tiles.
+// Measured on the 36,096-token, 32-head workload at E = 64: pass 1 0.25 ms, threshold 0.06,
+// pass 2 0.24, fallback 0.01 (1.69 ms as one streaming pass, 0.82 with an exact pass 1).
+// About 75 candidate tiles per row pass the screen (65 with exact maxima).
 //
 // vsa_extra_gather_kernel: copies each row's extra K and V rows into staging
 // buffers laid out [batch, Qs, 64, heads, 128] (padding rows zero), i.e. with
@@ -546,15 +546,21 @@ __global__ __launch_bounds__(256) void vsa_extra_select_kernel(VsaGeom g, const 
   }
 }
 
-// Pass 1 of the two-pass select.  Per (sparse row, tile): M1, the row's best score among
-// the tile's eligible keys, and M4, the least of the four lanes' best (each lane holds 16 of
-// the 64 keys, so at least four keys score >= M4); both -inf for a tile in the row's list.
-// One workgroup per (batch x head, tile chunk, 64-row block): the tiles are cut into xs1
-// chunks, and the row blocks of one chunk get consecutive logical ids, dealt to one XCD so
-// that they stream the same key tiles through its L2 together.  Key tiles come into a ring of three
-// LDS buffers by buffer-to-LDS loads issued two tiles ahead (each wave four 1 KB loads per
-// tile, padding rows of a partial prefix tile read out of range and so as zeros), with one
-// barrier per tile; 48 KB of LDS and no staging registers, so three workgroups fit a CU.
+// Pass 1 of the two-pass select, a screen.  Per (sparse row, tile): M1, the row's best
+// screening score among the tile's eligible keys, and M4, the least of the four lane maxima
+// (each lane holds 16 of the 64 keys, so at least four keys score >= M4); both -inf for a
+// tile in the row's list.  The screening score is the MFMA product with hi(qbar), the first
+// bf16 term of the row's split, alone: one third of the MFMAs of the exact score.  Its error
+// against the exact score is bounded per (row, tile) and the threshold kernel widens M1 and
+// M4 by that bound.
+// One workgroup of four waves per (batch x head, tile chunk, 128-row block): the tiles are
+// cut into xs1 chunks, and the row blocks of one chunk get consecutive logical ids, dealt to
+// one XCD so that they stream the same key tiles through its L2 together.  A wave scores 32
+// rows, two MFMA row groups sharing every key operand it reads from LDS.  Key tiles come into
+// a ring of three LDS buffers by buffer-to-LDS loads issued two tiles ahead (each wave four
+// 1 KB loads per tile; padding rows of a partial prefix tile read out of range, so as zeros),
+// one barrier per tile; 52 KB of LDS, three workgroups per CU.
+constexpr int X1ROWS = 128;
 constexpr int XNB = 3;
 // 16 bytes per lane from buffer offset voff into LDS at lds + 16 lane (M0 holds the LDS base).
 // Written as asm so that the compiler neither waits for it before unrelated LDS reads nor
@@ -567,151 +573,168 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned vo
 }
 template <int N>
 using IC = std::integral_constant<int, N>;
-__global__ __launch_bounds__(256) void vsa_extra_tmax_kernel(VsaGeom g, const char* __restrict__ kp,
+__global__ __launch_bounds__(256, 3) void vsa_extra_tmax_kernel(VsaGeom g, const char* __restrict__ kp,
                                                              const float* __restrict__ qbar,
                                                              const int* __restrict__ lists,
                                                              const int* __restrict__ counts,
                                                              float* __restrict__ tm1, float* __restrict__ tm4,
                                                              int* __restrict__ ccnt, u32x4* __restrict__ qsplit) {
   __shared__ __attribute__((aligned(16))) char kring[XNB][64 * 256];
-  __shared__ unsigned xbits[XROWS][8];  // listed tiles of each row among the current 256
+  __shared__ unsigned xbits[X1ROWS][8];  // listed tiles of each row among the current 256
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
-  const int nrb = (g.Qs + XROWS - 1) / XROWS;
+  const int nrb = (g.Qs + X1ROWS - 1) / X1ROWS;
   const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
   const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
-  const int rl = 16 * wave + ql;
   const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
   const unsigned nrec = (unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2;
+  const int rb = w % nrb;
+  const int tch = (w / nrb) % g.xs1;  // the tile chunk
+  const int bhl = w / nrb / g.xs1;
+  const int h = bhl % g.heads, b = bhl / g.heads;
+  const size_t bh = (size_t)b * g.heads + h;
+  const int t0 = (int)((long long)tch * g.Tq / g.xs1);
+  const int t1 = (int)((long long)(tch + 1) * g.Tq / g.xs1);
+  // row group u of this wave: rows 32 wave + 16 u .. + 15 of the block, this lane's is + ql
+  const int wr0 = rb * X1ROWS + 32 * wave;
+  const int Qsp = (g.Qs + 31) & ~31;  // rows of the M1 / M4 arrays
+  int r[2];
+  bool live[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    r[u] = wr0 + 16 * u + ql;
+    live[u] = r[u] < g.Qs;
+  }
+  // live row groups of the wave (wave-uniform): a group with a live row has its first row live
+  const int nl = (wr0 < g.Qs) + (wr0 + 16 < g.Qs);
+  bf16x8 qh[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live[u] ? r[u] : 0)) * VSA_HEAD_DIM);
+    bf16x8 qs[3][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x4 a = live[u] ? qp[8 * ks + 2 * grp] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 c = live[u] ? qp[8 * ks + 2 * grp + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hi3, mid3, lo3;
+        split3(x[e], hi3, mid3, lo3);
+        qs[0][ks][e] = hi3;
+        qs[1][ks][e] = mid3;
+        qs[2][ks][e] = lo3;
+      }
+      qh[u][ks] = qs[0][ks];
+    }
+    // the row's three bf16 terms of qbar, in the lane order of the MFMA operands, for pass 2
+    // (layout per row: (term, ks, grp) at 16 term + 4 ks + grp, 16 bytes each)
+    if (tch == 0 && live[u]) {
+      u32x4* qo = qsplit + (bh * g.Qs + r[u]) * 48 + grp;
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qo[16 * pp + 4 * ks] = __builtin_bit_cast(u32x4, qs[pp][ks]);
+    }
+  }
+  // the listed tiles: lane (ql, grp < 2) keeps the list cursor of row group grp's row ql
+  const bool lister = grp < 2 && live[grp & 1];
+  const int lrow = r[grp & 1];
+  const int* lst = lists + (bh * g.Qs + (lister ? lrow : 0)) * g.cap;
+  const int cnt_l = lister ? counts[bh * g.Qs + lrow] : 0;
+  int cur;
+  {
+    int a = 0, c = cnt_l;
+    while (a < c) {
+      const int m = (a + c) >> 1;
+      if (lst[m] < t0) a = m + 1;
+      else c = m;
+    }
+    cur = a;
+  }
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + ((size_t)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2)), 0, (int)nrec, 0x00020000);
   // this lane's share of a tile's loads: wave w moves rows 4 w + 16 m + (lane >> 4), m = 0..3,
   // i.e. (dt, dh, dw) = (m, w, lane >> 4) of a video tile; its 16 bytes land at position
   // lane & 15 of the row, which holds chunk (lane & 15) ^ (row & 15)
   const unsigned chunk = (unsigned)((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 16u;
   const unsigned vrow = (unsigned)(wave * g.W + (lane >> 4));  // (dh, dw) offset in tokens
   const unsigned plane = (unsigned)(g.H * g.W);
-
-  {
-    const int rb = w % nrb;
-    const int tch = (w / nrb) % g.xs1;  // the tile chunk
-    const int bhl = w / nrb / g.xs1;
-    const int h = bhl % g.heads, b = bhl / g.heads;
-    const size_t bh = (size_t)b * g.heads + h;
-    const int t0 = (int)((long long)tch * g.Tq / g.xs1);
-    const int t1 = (int)((long long)(tch + 1) * g.Tq / g.xs1);
-    const int r = rb * XROWS + rl;
-    const bool live = r < g.Qs;
-    const bool wlive = rb * XROWS + 16 * wave < g.Qs;
-    bf16x8 qs[3][4];
-    {
-      const f32x4* qp = reinterpret_cast<const f32x4*>(qbar + (bh * g.Tq + g.n_dense + (live ? r : 0)) * VSA_HEAD_DIM);
+  auto issue = [&](const TileWalk& tw, auto bic) {
+    constexpr int BI = decltype(bic)::value;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 4 * wave + 16 * m + (lane >> 4);
+      unsigned off;
+      if (tw.video) off = (unsigned)(tw.tok0 + m * (int)plane + (int)vrow) * rowbytes + chunk;
+      else off = row < tw.nv ? (unsigned)(tw.tok0 + row) * rowbytes + chunk : nrec;
+      lds_dma16(rs, off, (unsigned)(size_t)(kring[BI] + 1024 * (wave + 4 * m)));
+    }
+  };
+  // Every step issues the loads of one tile (past the chunk's end, its last tile again), so
+  // the loads issued after tile t's are always the next tile's four plus the stores since.
+  TileWalk wc, wf;
+  walk_seek(g, wc, t0);
+  wf = wc;
+  issue(wf, IC<0>{});
+  if (t0 + 1 < t1) walk_next(g, wf);
+  issue(wf, IC<1>{});
+  // one tile from ring buffer BI (a constant, so that the compiler can tell the buffer read
+  // from the ones being loaded and adds no wait for the loads in flight)
+  auto step = [&](int t, auto bic) {
+    constexpr int BI = decltype(bic)::value;
+    const int i = t - t0;
+    if ((i & 255) == 0) {
+      // the row's listed tiles among the next 256, as bits (by its lister lane; the wave's
+      // other lanes read them after this wave's LDS writes)
+      if (grp < 2) {
+        unsigned* xm = xbits[32 * wave + 16 * grp + ql];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) xm[jj] = 0u;
+        while (cur < cnt_l) {
+          const int x = lst[cur];
+          if (x >= t + 256) break;
+          atomicOr(&xm[(x - t) >> 5], 1u << ((x - t) & 31));
+          ++cur;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    }
+    // Wait for this wave's loads of tile t: issued after them are the next tile's four and,
+    // in a live wave, the one M1 / M4 store of each tile since (one tile at i = 1, two
+    // later).  A plain barrier would make the compiler wait for every load in flight first;
+    // the bare barrier between two compiler fences does not.
+    if (i == 0 || nl == 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (i == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // tile t is in LDS; every wave is done with tile t - 1
+    asm volatile("" ::: "memory");
+    if (t + 2 < t1) walk_next(g, wf);
+    issue(wf, IC<(BI + 2) % XNB>{});  // into the buffer tile t - 1 held
+    if (nl > 0) {
+      const char* kt = kring[BI];
+      f32x4 acc[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[u][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f32x4 a = live ? qp[8 * ks + 2 * grp] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 c = live ? qp[8 * ks + 2 * grp + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+        bf16x8 a[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __bf16 hi3, mid3, lo3;
-          split3(x[e], hi3, mid3, lo3);
-          qs[0][ks][e] = hi3;
-          qs[1][ks][e] = mid3;
-          qs[2][ks][e] = lo3;
-        }
-      }
-    }
-    // the row's three bf16 terms of qbar, in the lane order of the MFMA operands, for pass 2
-    if (tch == 0 && live) {
-      // layout per row: (term, ks, grp) at 16 term + 4 ks + grp, 16 bytes each
-      u32x4* qo = qsplit + (bh * g.Qs + r) * 48 + grp;
+        for (int kb = 0; kb < 4; ++kb)
+          a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
 #pragma unroll
-      for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qo[16 * pp + 4 * ks] = __builtin_bit_cast(u32x4, qs[pp][ks]);
-    }
-    const int* lst = lists + (bh * g.Qs + (live ? r : 0)) * g.cap;
-    const int cnt_l = live ? counts[bh * g.Qs + r] : 0;
-    int cur;
-    {
-      int a = 0, c = cnt_l;
-      while (a < c) {
-        const int m = (a + c) >> 1;
-        if (lst[m] < t0) a = m + 1;
-        else c = m;
-      }
-      cur = a;
-    }
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kp + ((size_t)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2)), 0, (int)nrec, 0x00020000);
-    // the loads of tile `tw` into ring buffer bi (four 1 KB loads of this wave)
-    auto issue = [&](const TileWalk& tw, auto bic) {
-      constexpr int BI = decltype(bic)::value;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 4 * wave + 16 * m + (lane >> 4);
-        unsigned off;
-        if (tw.video) off = (unsigned)(tw.tok0 + m * (int)plane + (int)vrow) * rowbytes + chunk;
-        else off = row < tw.nv ? (unsigned)(tw.tok0 + row) * rowbytes + chunk : nrec;
-        lds_dma16(rs, off, (unsigned)(size_t)(kring[BI] + 1024 * (wave + 4 * m)));
-      }
-    };
-    TileWalk wc, wf;
-    walk_seek(g, wc, t0);
-    wf = wc;
-    issue(wf, IC<0>{});
-    if (t0 + 1 < t1) walk_next(g, wf);
-    issue(wf, IC<1>{});
-    // one tile from ring buffer BI (a constant, so that the compiler can tell the buffer
-    // read from the one being loaded and adds no wait for the loads in flight)
-    auto step = [&](int t, auto bic) {
-      constexpr int BI = decltype(bic)::value;
-      const int i = t - t0;
-      if ((i & 255) == 0) {
-        // the row's listed tiles among the next 256, as bits (by the row's grp-0 lane; the
-        // wave's other lanes read them after this wave's LDS writes)
-        unsigned* xm = xbits[rl];
-        if (grp == 0) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xm[j] = 0u;
-          while (cur < cnt_l) {
-            const int x = lst[cur];
-            if (x >= t + 256) break;
-            atomicOr(&xm[(x - t) >> 5], 1u << ((x - t) & 31));
-            ++cur;
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      }
-      // Wait for this wave's loads of tile t: the loads issued after them are the next
-      // tile's four and, in a wave with live rows, the two stores of each tile since.  A
-      // plain barrier would make the compiler wait for every load in flight first; the bare
-      // barrier between two compiler fences does not.
-      if (i == 0 || !wlive) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if (i == 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      __builtin_amdgcn_s_barrier();  // tile t is in LDS; every wave is done with tile t - 1
-      asm volatile("" ::: "memory");
-      const bool excl = (xbits[rl][(i & 255) >> 5] >> (i & 31)) & 1u;
-      if (t + 2 < t1) walk_next(g, wf);
-      issue(wf, IC<(BI + 2) % XNB>{});  // into the buffer tile t - 1 held
-      if (wlive) {
-        const char* kt = kring[BI];
-        f32x4 acc[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8 a[4];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
-            a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
+            acc[u][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kb], qh[u][ks], acc[u][kb], 0, 0, 0);
+      }
+      float v1[2], v4[2];  // M1 and M4 of this lane's row in each row group
 #pragma unroll
-          for (int pp = 2; pp >= 0; --pp)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-              acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kb], qs[pp][ks], acc[kb], 0, 0, 0);
-        }
+      for (int u = 0; u < 2; ++u) {
         float z[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = acc[e >> 2][e & 3];
+        for (int e = 0; e < 16; ++e) z[e] = acc[u][e >> 2][e & 3];
         if (!wc.video) {  // padding keys of a partial prefix tile take no part
           const int nv = wc.nv;
 #pragma unroll
@@ -721,51 +744,125 @@ __global__ __launch_bounds__(256) void vsa_extra_tmax_kernel(VsaGeom g, const ch
         float mx = z[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, z[e]);
-        if (!live || excl) mx = -INFINITY;
+        const bool excl = (xbits[32 * wave + 16 * u + ql][(i & 255) >> 5] >> (i & 31)) & 1u;
+        if (!live[u] || excl) mx = -INFINITY;
         int rv[4];
         row_values4(__float_as_int(mx), rv);
         const float a0 = __int_as_float(rv[0]), a1 = __int_as_float(rv[1]);
         const float a2 = __int_as_float(rv[2]), a3 = __int_as_float(rv[3]);
-        if (grp == 0 && live) {
-          const size_t o = (bh * g.Qs + r) * (size_t)g.Tq + t;
-          tm1[o] = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
-          tm4[o] = fminf(fminf(a0, a1), fminf(a2, a3));
-          if (t == 0) ccnt[bh * g.Qs + r] = 0;  // the row's candidate count, for pass 2
-        }
+        v1[u] = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+        v4[u] = fminf(fminf(a0, a1), fminf(a2, a3));
+        if (t == 0 && grp == 0 && live[u]) ccnt[bh * g.Qs + r[u]] = 0;  // the row's candidate count
       }
-      walk_next(g, wc);
-    };
-    int t = t0;
-    for (; t + 2 < t1; t += 3) {
-      step(t, IC<0>{});
-      step(t + 1, IC<1>{});
-      step(t + 2, IC<2>{});
+      // One store for the wave's 32 rows: lane group grp writes M1 (grp even) or M4 (odd) of
+      // row group grp / 2, 16 consecutive floats of the tile's row of [bh][tile][padded row]
+      // (rows past Qs land in the padding).
+      const int uu = grp >> 1;
+      const float val = (grp & 1) ? (uu ? v4[1] : v4[0]) : (uu ? v1[1] : v1[0]);
+      float* dst = (grp & 1) ? tm4 : tm1;
+      dst[(bh * g.Tq + t) * (size_t)Qsp + wr0 + 16 * uu + ql] = val;
     }
-    if (t < t1) step(t, IC<0>{});
-    if (t + 1 < t1) step(t + 1, IC<1>{});
+    walk_next(g, wc);
+  };
+  int t = t0;
+  for (; t + 2 < t1; t += 3) {
+    step(t, IC<0>{});
+    step(t + 1, IC<1>{});
+    step(t + 2, IC<2>{});
   }
+  if (t < t1) step(t, IC<0>{});
+  if (t + 1 < t1) step(t + 1, IC<1>{});
+  // the loads issued past the chunk's end land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int NC>
-__global__ __launch_bounds__(64) void vsa_extra_thr_kernel(VsaGeom g, const float* __restrict__ tm1,
-                                                           const float* __restrict__ tm4,
-                                                           float* __restrict__ xthr,
-                                                           unsigned* __restrict__ xmask) {
-  const int s = blockIdx.x, lane = threadIdx.x;
-  const size_t bh = blockIdx.y;
+// The screen's error per (row, tile).  Pass 1 scores a key k with hi, the first bf16 term of
+// the row's qbar; pass 2 and the fallback with all three terms, whose sum is qbar exactly.
+// The products of bf16 values are exact in fp32, so the two scores differ by r . k, with
+// r = qbar - hi, plus the fp32 rounding of the sums: recursive summation of n terms errs by at
+// most about n 2^-24 of their absolute sum, here 3 x 128 and 128 terms (and the MFMA
+// accumulator adds), under 2^-14 |qbar| |k| together.  With |r . k| <= |r| |k|
+// (Cauchy-Schwarz) and |k| at most the tile's largest key norm:
+//   |exact - screen| <= eps = (|r| (1 + 2^-10) + |qbar| 2^-13) knorm(tile) + 1e-35,
+// the factor and the doubled 2^-13 covering the rounding of eps itself and of the sums below,
+// the constant any flushed denormal products.
+// Threshold kernel: with lo1 = M1 - eps and lo4 = M4 - eps (each tile then holds a key, or
+// four keys, whose exact score is >= these), T = max(E-th largest lo1, ceil(E/4)-th largest
+// lo4) bounds the row's E-th best exact score from below, and a tile can hold a key scoring
+// >= T only if M1 + eps >= T: those are the candidates.
+// One workgroup of R waves per R consecutive rows, a wave per row.  The workgroup stages
+// each chunk of 64 tiles of its rows' M1 and M4 ([bh][tile][padded row]: R consecutive floats
+// per tile) through LDS, so that the loads are coalesced; each wave then holds its row's keys,
+// one tile per lane and chunk, in registers (R shrinks as the tile count grows).
+template <int NC, int R>
+__global__ __launch_bounds__(64 * R) void vsa_extra_thr_kernel(VsaGeom g, const float* __restrict__ qbar,
+                                                               const float* __restrict__ knorm,
+                                                               const float* __restrict__ tm1,
+                                                               const float* __restrict__ tm4,
+                                                               float* __restrict__ xthr,
+                                                               unsigned* __restrict__ xmask) {
+  __shared__ float sm[2][64][R + 1];  // one chunk: [M1 / M4][tile][row], padded against bank conflicts
+  // row blocks in order within an XCD: the blocks that share a 128-byte line of M1 / M4 are
+  // read through one L2
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
+  const int nrb = (g.Qs + R - 1) / R;
+  const int s0 = (w % nrb) * R;
+  const size_t bh = w / nrb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int s = s0 + wave;  // this wave's row
+  const bool live = s < g.Qs;
   const int Tq = g.Tq, E = g.extra, E4 = (g.extra + 3) / 4;
   const int nc = (Tq + 63) / 64;
-  const float* m1 = tm1 + (bh * g.Qs + s) * (size_t)Tq;
-  const float* m4 = tm4 + (bh * g.Qs + s) * (size_t)Tq;
-  unsigned k1[NC], k4[NC];
+  const size_t Qsp = (g.Qs + 31) & ~31;
+  const float* m1b = tm1 + bh * Tq * Qsp + s0;  // tile t, row s0 + i at [t Qsp + i]
+  const float* m4b = tm4 + bh * Tq * Qsp + s0;
+  const float* kn = knorm + bh * (size_t)Tq;
+  // the row's error scale: eps(tile) = es knorm(tile) + 1e-35
+  float es = 0.f;
+  if (live) {
+    const float* qr = qbar + (bh * g.Tq + g.n_dense + s) * VSA_HEAD_DIM;
+    const float x0 = qr[lane], x1 = qr[lane + 64];
+    const float r0 = x0 - (float)(__bf16)x0, r1 = x1 - (float)(__bf16)x1;  // as split3 rounds
+    const float rn = sqrtf(wave_sum(r0 * r0 + r1 * r1)), qn = sqrtf(wave_sum(x0 * x0 + x1 * x1));
+    es = rn * 1.0009765625f + qn * 0x1p-13f;
+  }
+  // keys of lo1 = M1 - eps, lo4 = M4 - eps and hi1 = M1 + eps; 0: absent (every present key
+  // is above 0)
+  unsigned k1[NC], k4[NC], kh[NC];
+  const int tl = tid / R, rr = tid % R;  // this thread's element of a chunk
+  // every chunk's loads in flight at once (from clamped addresses, so that no lane branches)
+  const bool rin = s0 + rr < g.Qs;
+  const int rc = rin ? rr : 0;
+  float la[NC], lc[NC], lk[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+    if (j < nc) {
+      const size_t o = (size_t)min(64 * j + tl, Tq - 1) * Qsp + rc;
+      la[j] = m1b[o];
+      lc[j] = m4b[o];
+      lk[j] = kn[min(64 * j + lane, Tq - 1)];
+    }
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int t = 64 * j + lane;
-    const float a = j < nc && t < Tq ? m1[t] : -INFINITY;
-    const float c = j < nc && t < Tq ? m4[t] : -INFINITY;
-    k1[j] = a == -INFINITY ? 0u : order_key(a);  // 0: absent (every present key is above 0)
-    k4[j] = c == -INFINITY ? 0u : order_key(c);
+    k1[j] = k4[j] = kh[j] = 0u;
+    if (j < nc) {
+      const bool in = rin && 64 * j + tl < Tq;
+      __syncthreads();  // the last chunk has been read
+      sm[0][tl][rr] = in ? la[j] : -INFINITY;
+      sm[1][tl][rr] = in ? lc[j] : -INFINITY;
+      __syncthreads();
+      const int tt = 64 * j + lane;
+      const float m1 = sm[0][lane][wave], m4 = sm[1][lane][wave];
+      const float e = tt < Tq ? fmaf(es, lk[j], 1e-35f) : 0.f;
+      if (m1 != -INFINITY) {
+        k1[j] = order_key(m1 - e);
+        kh[j] = order_key(m1 + e);
+      }
+      if (m4 != -INFINITY) k4[j] = order_key(m4 - e);
+    }
   }
+  if (!live) return;
   auto counts = [&](unsigned c1, unsigned c4, int& n1, int& n4) {
     n1 = 0;
     n4 = 0;
@@ -795,7 +892,7 @@ __global__ __launch_bounds__(64) void vsa_extra_thr_kernel(VsaGeom g, const floa
 #pragma unroll
   for (int j = 0; j < NC; ++j)
     if (j < nc) {
-      const unsigned long long m = __ballot(k1[j] != 0u && k1[j] >= kt);
+      const unsigned long long m = __ballot(kh[j] != 0u && kh[j] >= kt);
       if (lane == 0) {
         xmask[(bh * nw + 2 * j) * g.Qs + s] = (unsigned)m;
         if (2 * j + 1 < nw) xmask[(bh * nw + 2 * j + 1) * g.Qs + s] = (unsigned)(m >> 32);
@@ -803,76 +900,98 @@ __global__ __launch_bounds__(64) void vsa_extra_thr_kernel(VsaGeom g, const floa
     }
 }
 
-// Pass 2: one workgroup per (tile, batch x head).  The rows that have the tile among their
-// candidates are gathered (in row order) from the masks; each wave scores groups of 16 of
-// them against the tile's keys on the MFMAs (the same three-term products as pass 1), and a
-// key scoring >= its row's T is appended to the row's candidate list (its slot from an atomic
-// count; past VSA_EXTRA_CAND the count keeps growing but nothing is written).
-__global__ __launch_bounds__(256, 3) void vsa_extra_score_kernel(VsaGeom g, const u32x4* __restrict__ k,
+// Pass 2: one workgroup of four waves per (TPW consecutive tiles, batch x head).  The tiles'
+// keys come into LDS by buffer-to-LDS loads (padding rows of a partial prefix tile read out of
+// range, so as zeros) while the rows that have each tile among their candidates are gathered
+// from the masks (in any order, through LDS counts); the waves then take the (tile, 16-row
+// group) items in turn and score them against the tile's keys on the MFMAs with the rows'
+// exact three-term split, and a key scoring >= its row's T is appended to the row's candidate
+// list (its slot from an atomic count; past VSA_EXTRA_CAND the count keeps growing but nothing
+// is written).
+template <int TPW>
+__global__ __launch_bounds__(256, 4) void vsa_extra_score_kernel(VsaGeom g, const char* __restrict__ kp,
                                                               const float* __restrict__ xthr,
                                                               const unsigned* __restrict__ xmask,
                                                               int* __restrict__ ccnt,
                                                               unsigned long long* __restrict__ xcand,
                                                               const u32x4* __restrict__ qsplit) {
-  __shared__ __attribute__((aligned(16))) char ktile[64 * 256];
-  __shared__ int nrows_s;
-  extern __shared__ int rowlist[];  // Qs entries
+  __shared__ __attribute__((aligned(16))) char ktile[TPW][64 * 256];
+  __shared__ int nrows_s[TPW];
+  extern __shared__ int rowlist[];  // TPW x Qs entries
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
-  const int t = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int b = (int)(bh / g.heads), h = (int)(bh % g.heads);
+  const int tb = blockIdx.x * TPW;      // the first tile
+  const int nt = min(TPW, g.Tq - tb);   // tiles of this workgroup
   const int nw = (g.Tq + 31) / 32;
-  // the tile's keys: loads first, so that they are in flight during the row scan
-  TileWalk tw;
-  walk_seek(g, tw, t);
-  u32x4 kreg[4];
-  unsigned kvalid = 0u;
-  {
-    const int hw = g.H * g.W;
-    const int fdhw = ((tid >> 6) & 3) * g.W + ((tid >> 4) & 3);
-    const u32x4* kbh = k + (((size_t)b * g.N) * g.heads + h) * (VSA_HEAD_DIM / 8) + (tid & 15);
-    const int tokstride = g.heads * (VSA_HEAD_DIM / 8);
+  const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
+  const unsigned nrec = (unsigned)(g.N - 1) * rowbytes + VSA_HEAD_DIM * 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + ((size_t)b * g.N * g.heads + h) * (VSA_HEAD_DIM * 2)), 0, (int)nrec, 0x00020000);
+  // the keys, as in pass 1: wave w moves rows 4 w + 16 m + (lane >> 4) of each tile
+  const unsigned chunk = (unsigned)((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 16u;
+  const unsigned vrow = (unsigned)(wave * g.W + (lane >> 4));
+  const unsigned plane = (unsigned)(g.H * g.W);
+  TileWalk tw[TPW];
+  walk_seek(g, tw[0], tb);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int rr = (tid >> 4) + 16 * m;
-      const bool valid = tw.video || rr < tw.nv;
-      const int tok = tw.tok0 + (tw.video ? m * hw + fdhw : (valid ? rr : 0));
-      kreg[m] = kbh[(size_t)tok * tokstride];
-      kvalid |= (unsigned)valid << m;
-    }
-  }
-  // the rows that have this tile among their candidates (any order: every wave appends its
-  // 64-row chunks through an LDS count)
-  if (tid == 0) nrows_s = 0;
-  __syncthreads();
-  {
-    const unsigned* mk = xmask + (bh * nw + (t >> 5)) * g.Qs;
-    for (int base = 64 * wave; base < g.Qs; base += 256) {
-      const int s = base + lane;
-      const bool in = s < g.Qs && ((mk[s] >> (t & 31)) & 1u);
-      const unsigned long long m = __ballot(in);
-      int at = 0;
-      if (m != 0ull && lane == 0) at = atomicAdd(&nrows_s, __popcll(m));
-      at = __shfl(at, 0);
-      if (in) rowlist[at + lanes_below(m)] = s;
-    }
+  for (int i = 1; i < TPW; ++i) {
+    tw[i] = tw[i - 1];
+    if (i < nt) walk_next(g, tw[i]);
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int rr = (tid >> 4) + 16 * m;
-    *reinterpret_cast<u32x4*>(ktile + 256 * rr + 16 * ((tid & 15) ^ (rr & 15))) =
-        ((kvalid >> m) & 1u) ? kreg[m] : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int i = 0; i < TPW; ++i)
+    if (i < nt) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 4 * wave + 16 * m + (lane >> 4);
+        unsigned off;
+        if (tw[i].video) off = (unsigned)(tw[i].tok0 + m * (int)plane + (int)vrow) * rowbytes + chunk;
+        else off = row < tw[i].nv ? (unsigned)(tw[i].tok0 + row) * rowbytes + chunk : nrec;
+        lds_dma16(rs, off, (unsigned)(size_t)(ktile[i] + 1024 * (wave + 4 * m)));
+      }
+    }
+  if (tid < TPW) nrows_s[tid] = 0;
   __syncthreads();
-  const int n = nrows_s;
-  if (n == 0) return;
-  const int tokl = tw.tok0 + (tw.video ? grp * g.W : 4 * grp);  // key e: tokl + (video ? kb hw + i : 16 kb + i)
-  const int kstep = tw.video ? g.H * g.W : 16;
-  const int ngroups = (n + 15) / 16;
-  for (int gi = wave; gi < ngroups; gi += 4) {
-    const int idx = 16 * gi + ql;
-    const bool live = idx < n;
-    const int s = rowlist[live ? idx : 0];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+    if (i < nt) {
+      const int t = tb + i;
+      const unsigned* mk = xmask + (bh * nw + (t >> 5)) * g.Qs;
+      for (int base = 64 * wave; base < g.Qs; base += 256) {
+        const int s = base + lane;
+        const bool in = s < g.Qs && ((mk[s] >> (t & 31)) & 1u);
+        const unsigned long long m = __ballot(in);
+        int at = 0;
+        if (m != 0ull && lane == 0) at = atomicAdd(&nrows_s[i], __popcll(m));
+        at = __shfl(at, 0);
+        if (in) rowlist[i * g.Qs + at + lanes_below(m)] = s;
+      }
+    }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's key loads
+  __syncthreads();
+  int n[TPW], ng = 0;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    n[i] = nrows_s[i];
+    ng += (n[i] + 15) / 16;
+  }
+  for (int gi = wave; gi < ng; gi += 4) {
+    // the item's tile i and row group gg (per-tile values picked by selects, not by index)
+    int i = 0, gg = gi, cnt = n[0], tok0 = tw[0].tok0, nv = tw[0].nv, video = tw[0].video;
+#pragma unroll
+    for (int ii = 1; ii < TPW; ++ii)
+      if (i == ii - 1 && gg >= (cnt + 15) / 16) {
+        gg -= (cnt + 15) / 16;
+        i = ii;
+        cnt = n[ii];
+        tok0 = tw[ii].tok0;
+        nv = tw[ii].nv;
+        video = tw[ii].video;
+      }
+    const int idx = 16 * gg + ql;
+    const bool live = idx < cnt;
+    const int s = rowlist[i * g.Qs + (live ? idx : 0)];
     bf16x8 qs[3][4];
     {
       const u32x4* qi = qsplit + (bh * g.Qs + s) * 48 + grp;
@@ -882,6 +1001,7 @@ __global__ __launch_bounds__(256, 3) void vsa_extra_score_kernel(VsaGeom g, cons
         for (int ks = 0; ks < 4; ++ks) qs[pp][ks] = as_bf16x8(qi[16 * pp + 4 * ks]);
     }
     const float T = live ? xthr[bh * g.Qs + s] : INFINITY;
+    const char* kt = ktile[0] + i * (64 * 256);
     f32x4 acc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -890,7 +1010,7 @@ __global__ __launch_bounds__(256, 3) void vsa_extra_score_kernel(VsaGeom g, cons
       bf16x8 a[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(ktile + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
+        a[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + 256 * (16 * kb + ql) + 16 * ((4 * ks + grp) ^ ql)));
 #pragma unroll
       for (int p = 2; p >= 0; --p)
 #pragma unroll
@@ -900,11 +1020,15 @@ __global__ __launch_bounds__(256, 3) void vsa_extra_score_kernel(VsaGeom g, cons
     float z[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) z[e] = acc[e >> 2][e & 3];
-    if (!tw.video) {  // padding keys get a NaN, which never passes
+    if (!video) {  // padding keys get a NaN, which never passes
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (16 * (e >> 2) + 4 * grp + (e & 3) >= tw.nv) z[e] = __builtin_nanf("");
+        if (16 * (e >> 2) + 4 * grp + (e & 3) >= nv) z[e] = __builtin_nanf("");
     }
+    // key e of this lane: row 16 (e >> 2) + 4 grp + (e & 3) of the tile, whose token is
+    // tokl + (e >> 2) kstep + (e & 3)
+    const int tokl = tok0 + (video ? grp * g.W : 4 * grp);
+    const int kstep = video ? g.H * g.W : 16;
     unsigned ge = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ge |= (unsigned)(z[e] >= T) << e;
@@ -1080,17 +1204,22 @@ void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const floa
                       const int* counts, const VsaExtraBuffers& x, hipStream_t st) {
   if (g.Qs == 0 || g.extra == 0) return;
   const int BH = g.heads * g.batch;
-  hipLaunchKernelGGL(vsa_extra_tmax_kernel, dim3((g.Qs + XROWS - 1) / XROWS * BH * g.xs1), dim3(256), 0, st, g,
+  hipLaunchKernelGGL(vsa_extra_tmax_kernel, dim3((g.Qs + X1ROWS - 1) / X1ROWS * BH * g.xs1), dim3(256), 0, st, g,
                      (const char*)k, qbar, lists, counts, x.tm1, x.tm4, x.ccnt, (u32x4*)x.qsplit);
   {
     const int nc = (g.Tq + 63) / 64;
-    auto thr = nc <= 16 ? vsa_extra_thr_kernel<16> : nc <= 32 ? vsa_extra_thr_kernel<32>
-             : nc <= 64 ? vsa_extra_thr_kernel<64> : vsa_extra_thr_kernel<128>;
-    hipLaunchKernelGGL(thr, dim3(g.Qs, BH), dim3(64), 0, st, g, (const float*)x.tm1, (const float*)x.tm4, x.thr,
-                       x.mask);
+    auto thr = nc <= 16 ? vsa_extra_thr_kernel<16, 8> : nc <= 32 ? vsa_extra_thr_kernel<32, 8>
+             : nc <= 64 ? vsa_extra_thr_kernel<64, 4> : vsa_extra_thr_kernel<128, 2>;
+    const int R = nc <= 16 ? 8 : nc <= 32 ? 8 : nc <= 64 ? 4 : 2;
+    hipLaunchKernelGGL(thr, dim3((g.Qs + R - 1) / R * BH), dim3(64 * R), 0, st, g, qbar, x.knorm,
+                       (const float*)x.tm1, (const float*)x.tm4, x.thr, x.mask);
   }
-  hipLaunchKernelGGL(vsa_extra_score_kernel, dim3(g.Tq, BH), dim3(256), 4 * g.Qs, st, g, (const u32x4*)k,
-                     (const float*)x.thr, (const unsigned*)x.mask, x.ccnt, x.cand, (const u32x4*)x.qsplit);
+  {
+    constexpr int TPW = 2;
+    hipLaunchKernelGGL(vsa_extra_score_kernel<TPW>, dim3((g.Tq + TPW - 1) / TPW, BH), dim3(256),
+                       4 * TPW * g.Qs, st, g, (const char*)k, (const float*)x.thr, (const unsigned*)x.mask,
+                       x.ccnt, x.cand, (const u32x4*)x.qsplit);
+  }
   hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(g.xg), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
                      (const int*)x.ccnt, x.part, x.pcnt);
   hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(256), 0, st, g,

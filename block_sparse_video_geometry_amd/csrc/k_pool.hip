@@ -13,6 +13,10 @@
 // Native VSA (recipe)", "The inputs that matter"); a partial prefix tile is
 // summarised over its valid tokens.
 //
+// With extra tokens the step also writes every tile's largest key L2 norm, from the
+// key rows it holds (loading K for a prefix tile that is no key candidate): the
+// extra-token screen's error bound scales with it.
+//
 // HBM-bound: each (tile, head) slice of Q, K, V is read once; one wave per
 // (tile, head), 16 lanes per token (16 x 16 B = one 256-byte head row), four
 // tokens per load instruction; a candidate tile's 48 loads (Q, K, V) are all in flight at once.
@@ -57,19 +61,50 @@ __device__ __forceinline__ void tile_sum(const u32x4 buf[16], float acc[8]) {
   for (int i = 0; i < 8; ++i) acc[i] = group_sum(acc[i]);
 }
 
+// The largest L2 norm among the tile's 64 rows in buf (laid out as tile_load leaves them;
+// padding rows are zero), in every lane.  Each lane first sums the squares of its 8 dims of
+// its 16 rows; the 16 lanes of a row then add their sums in four exchange steps, each lane
+// keeping half of the rows it still holds (after the steps lane c holds row 4c + grp whole),
+// and a max over the wave ends it.  Used to bound the extra-token screen's error.
+__device__ __forceinline__ float tile_max_norm(const u32x4 buf[16], int lane) {
+  float s16[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = bf16lo(buf[p][w]), hi = bf16hi(buf[p][w]);
+      a = fmaf(lo, lo, a);
+      a = fmaf(hi, hi, a);
+    }
+    s16[p] = a;
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+  float s8[8], s4[4], s2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = (b3 ? s16[i + 8] : s16[i]) + __shfl_xor(b3 ? s16[i] : s16[i + 8], 8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = (b2 ? s8[i + 4] : s8[i]) + __shfl_xor(b2 ? s8[i] : s8[i + 4], 4);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) s2[i] = (b1 ? s4[i + 2] : s4[i]) + __shfl_xor(b1 ? s4[i] : s4[i + 2], 2);
+  const float m = (b0 ? s2[1] : s2[0]) + __shfl_xor(b0 ? s2[0] : s2[1], 1);
+  return sqrtf(wave_max(m));
+}
+
 __device__ __forceinline__ void store8(float* dst, const float v[8], float mul) {
   f32x4* d4 = reinterpret_cast<f32x4*>(dst);
   d4[0] = f32x4{v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul};
   d4[1] = f32x4{v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul};
 }
 
-// Q-bar of tile t, and K-bar / V-bar when KV (t is a candidate key tile).
-template <bool VIDEO, bool KV>
+// Q-bar of tile t, and K-bar / V-bar when KV (t is a candidate key tile); with KN also the
+// tile's largest key norm (every tile).
+template <bool VIDEO, bool KV, bool KN>
 __device__ __forceinline__ void pool_tile(const VsaGeom& g, const u32x4* __restrict__ q,
                                           const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                                           float* __restrict__ qbar, float* __restrict__ kbar,
-                                          float* __restrict__ vbar, float* __restrict__ bias, int b,
-                                          int h, int t, int lane) {
+                                          float* __restrict__ vbar, float* __restrict__ bias,
+                                          float* __restrict__ knorm, int b, int h, int t, int lane) {
   const int grp = lane >> 4, c = lane & 15;
   const size_t bh = (size_t)b * g.heads + h;
   const float inv = VIDEO ? 1.0f / VSA_TILE_TOKENS : 1.0f / (float)tile_valid(g, t);
@@ -79,6 +114,12 @@ __device__ __forceinline__ void pool_tile(const VsaGeom& g, const u32x4* __restr
   if (!KV) {
     tile_sum(bq, acc);
     if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+    if (KN) {
+      u32x4 bk[16];
+      tile_load<VIDEO>(g, k, b, h, t, grp, c, bk);
+      const float n = tile_max_norm(bk, lane);
+      if (lane == 0) knorm[bh * g.Tq + t] = n;
+    }
     return;
   }
   // candidate key tile: all 48 loads in flight before the first sum
@@ -88,6 +129,10 @@ __device__ __forceinline__ void pool_tile(const VsaGeom& g, const u32x4* __restr
   const int j = t - g.kc0;
   tile_sum(bq, acc);
   if (grp == 0) store8(qbar + (bh * g.Tq + t) * VSA_HEAD_DIM + 8 * c, acc, inv);
+  if (KN) {
+    const float n = tile_max_norm(bk, lane);
+    if (lane == 0) knorm[bh * g.Tq + t] = n;
+  }
   tile_sum(bk, acc);
   if (grp == 0) store8(kbar + (bh * g.Kc + j) * VSA_HEAD_DIM + 8 * c, acc, inv);
   tile_sum(bv, acc);
@@ -95,13 +140,15 @@ __device__ __forceinline__ void pool_tile(const VsaGeom& g, const u32x4* __restr
   if (g.coarse == VSA_COARSE_MEAN && lane == 0) bias[bh * g.Kc + j] = 0.0f;
 }
 
+template <bool KN>
 __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* __restrict__ q,
                                                        const u32x4* __restrict__ k,
                                                        const u32x4* __restrict__ v,
                                                        float* __restrict__ qbar,
                                                        float* __restrict__ kbar,
                                                        float* __restrict__ vbar,
-                                                       float* __restrict__ bias) {
+                                                       float* __restrict__ bias,
+                                                       float* __restrict__ knorm) {
   // head groups fastest: consecutive workgroups read neighbouring 1 KB pieces of the same
   // token rows, which keeps HBM page locality
   const int t = blockIdx.y;
@@ -110,11 +157,11 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaGeom g, const u32x4* _
   const int b = blockIdx.z;
   if (h >= g.heads) return;
   if (t >= g.P)  // video tiles are always candidates
-    pool_tile<true, true>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
+    pool_tile<true, true, KN>(g, q, k, v, qbar, kbar, vbar, bias, knorm, b, h, t, lane);
   else if (t >= g.kc0)  // prefix candidate (sink off)
-    pool_tile<false, true>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
+    pool_tile<false, true, KN>(g, q, k, v, qbar, kbar, vbar, bias, knorm, b, h, t, lane);
   else
-    pool_tile<false, false>(g, q, k, v, qbar, kbar, vbar, bias, b, h, t, lane);
+    pool_tile<false, false, KN>(g, q, k, v, qbar, kbar, vbar, bias, knorm, b, h, t, lane);
 }
 
 // q_a = mean of the video tiles' qbar (every video tile holds 64 tokens, so
@@ -260,10 +307,14 @@ __global__ __launch_bounds__(256) void vsa_logmass_kernel(VsaGeom g, int t_first
 }  // namespace
 
 void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void* v, float* qbar,
-                     float* kbar, float* vbar, float* bias, hipStream_t st) {
+                     float* kbar, float* vbar, float* bias, float* knorm, hipStream_t st) {
   dim3 grid((g.heads + 3) / 4, g.Tq, g.batch);
-  hipLaunchKernelGGL(vsa_pool_kernel, grid, dim3(256), 0, st, g, (const u32x4*)q, (const u32x4*)k,
-                     (const u32x4*)v, qbar, kbar, vbar, bias);
+  if (knorm != nullptr)
+    hipLaunchKernelGGL(vsa_pool_kernel<true>, grid, dim3(256), 0, st, g, (const u32x4*)q, (const u32x4*)k,
+                       (const u32x4*)v, qbar, kbar, vbar, bias, knorm);
+  else
+    hipLaunchKernelGGL(vsa_pool_kernel<false>, grid, dim3(256), 0, st, g, (const u32x4*)q, (const u32x4*)k,
+                       (const u32x4*)v, qbar, kbar, vbar, bias, knorm);
 }
 
 void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipStream_t st) {

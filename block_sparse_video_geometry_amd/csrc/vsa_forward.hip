@@ -142,6 +142,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   xb.ccnt = reinterpret_cast<int*>(ws + L.xccnt);
   xb.cand = reinterpret_cast<unsigned long long*>(ws + L.xcand);
   xb.qsplit = ws + L.xqsplit;
+  xb.knorm = reinterpret_cast<const float*>(ws + L.xknorm);
   xb.part = reinterpret_cast<unsigned long long*>(ws + L.xpart);
   xb.pcnt = reinterpret_cast<int*>(ws + L.xpcnt);
   xb.xtok = xtok;
@@ -182,7 +183,8 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   }
   // with no sparse row (the dense mode) nothing is pooled, scored or selected
   if (G.Qs > 0) {
-    VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias, st));
+    VSA_STEP("pool", vsa_launch_pool(G, q, k, v, qbar, kbar, vbar, bias,
+                                    G.extra > 0 ? reinterpret_cast<float*>(ws + L.xknorm) : nullptr, st));
     if (G.coarse == VSA_COARSE_MEAN_LOGMASS || G.coarse == VSA_COARSE_WEIGHTED_LOGMASS) {
       VSA_STEP("anchor", vsa_launch_anchor(G, qbar, anchor, st));
       VSA_STEP("logmass", vsa_launch_logmass(G, k, v, kbar, vbar, anchor, bias, st));

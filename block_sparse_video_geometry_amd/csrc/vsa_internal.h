@@ -61,6 +61,7 @@ struct VsaLayout {        // byte offsets into the workspace
   size_t xpart, xpcnt;        // extra tokens: per-segment best E of each row, and counts
   size_t xtm1, xtm4, xthr, xmask, xccnt, xcand;  // two-pass select: maxima, thresholds, candidates
   size_t xqsplit;                                // two-pass select: qbar as three bf16 terms
+  size_t xknorm;                                 // two-pass select: largest key norm per tile
   size_t cpart;               // coarse partials per (row, slice): max, sum, 2 pad, O[128]
   // Spark-Reblock: key-moment partials and M (fp32, bf16 hi/lo), video-token norms, token
   // lists (ping-pong; `tiles` is the final one), projections, pass partials, node states,

@@ -6,9 +6,10 @@
 #include "vsa_internal.h"
 
 // Geometry gather + mean pooling: qbar for every tile, kbar/vbar for video
-// tiles; writes bias = 0 when the coarse mode has no log-mass bias.
+// tiles; writes bias = 0 when the coarse mode has no log-mass bias.  With knorm
+// (extra tokens), also every tile's largest key L2 norm, [batch x head][tile].
 void vsa_launch_pool(const VsaGeom& g, const void* q, const void* k, const void* v, float* qbar,
-                     float* kbar, float* vbar, float* bias, hipStream_t st);
+                     float* kbar, float* vbar, float* bias, float* knorm, hipStream_t st);
 
 // Mean video query per (batch, head) (log-mass anchor).
 void vsa_launch_anchor(const VsaGeom& g, const float* qbar, float* anchor, hipStream_t st);
@@ -40,6 +41,7 @@ struct VsaExtraBuffers {
   int* ccnt;                   // candidate counts
   unsigned long long* cand;    // candidate entries, VSA_EXTRA_CAND per row
   void* qsplit;                // per row: qbar as three bf16 terms in MFMA operand order
+  const float* knorm;          // per tile: largest key L2 norm (written by the pool step)
   unsigned long long* part;    // fallback: per-segment best E of each row
   int* pcnt;
   int *xtok, *xcnt;            // the extra tokens and their count per row

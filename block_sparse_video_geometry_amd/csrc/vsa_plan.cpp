@@ -177,8 +177,10 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     for (int64_t r = 0; r < NRB; ++r) ms = std::max(ms, wg_of((r + 1) * g.Tq - 1) - wg_of(r * g.Tq) + 1);
     g.xg = (int32_t)G;
     g.xms = (int32_t)ms;
-    // about three rounds of three workgroups per CU, chunks of at least 32 tiles
-    g.xs1 = (int32_t)std::max<int64_t>(1, std::min<int64_t>((g.Tq + 31) / 32, (9 * VSA_EXTRA_WGS / 2 + NRB - 1) / NRB));
+    // pass 1: 128-row blocks; about four rounds of three workgroups per CU (3,072 items),
+    // chunks of about 32 tiles or more
+    const int64_t NRB1 = (g.Qs + 127) / 128 * heads * batch;
+    g.xs1 = (int32_t)std::max<int64_t>(1, std::min<int64_t>((g.Tq + 31) / 32, (6 * VSA_EXTRA_WGS + NRB1 - 1) / NRB1));
   }
   g.sink = o.sink;
   g.select = o.select;
@@ -231,13 +233,16 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
     L.xpart = take(xrb * VSA_MAX_EXTRA * 8);
     L.xpcnt = take(xrb * 4);
     const size_t xr = g.extra > 0 ? BH * (size_t)g.Qs : 0;  // sparse rows
-    L.xtm1 = take(xr * g.Tq * 4);
-    L.xtm4 = take(xr * g.Tq * 4);
+    // per (tile, row): [bh][tile][row], rows padded to a multiple of 32
+    const size_t xrp = g.extra > 0 ? BH * (size_t)((g.Qs + 31) & ~31) : 0;
+    L.xtm1 = take(xrp * g.Tq * 4);
+    L.xtm4 = take(xrp * g.Tq * 4);
     L.xthr = take(xr * 4);
     L.xmask = take(xr * ((g.Tq + 31) / 32) * 4);
     L.xccnt = take(xr * 4);
     L.xcand = take(xr * VSA_EXTRA_CAND * 8);
     L.xqsplit = take(xr * 3 * VSA_HEAD_DIM * 2);
+    L.xknorm = take(g.extra > 0 ? BH * (size_t)g.Tq * 4 : 0);
   }
   L.cpart = take(g.csplit > 1 ? BH * (size_t)g.Qs * g.csplit * (VSA_HEAD_DIM + 4) * 4 : 0);
   {
