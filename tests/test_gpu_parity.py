@@ -372,6 +372,12 @@ LIMIT_CASES = [
     # the same shape with 64 extra tokens: each row's scoring streams all 4,097 key tiles
     Workload("max_video_tiles_extra", 1, ((SEG_TEXT, 64),), (64, 64, 64), 1.0, SINK_EXACT_KV_AND_ROWS,
              seed=95, recipe="scaled", extra=64),
+    # 1,025 and 2,049 tiles with 64 extra tokens: the extra-token threshold kernel's shapes for
+    # up to 2,048 and up to 4,096 tiles per row (8 and 4 rows per workgroup)
+    Workload("long_video_extra_1k", 1, ((SEG_TEXT, 64),), (32, 32, 64), 2.0, SINK_EXACT_KV, seed=101,
+             recipe="scaled", extra=64),
+    Workload("long_video_extra_2k", 1, ((SEG_TEXT, 64),), (32, 64, 64), 1.0, SINK_EXACT_KV, seed=102,
+             recipe="scaled", extra=64),
 ]
 
 
