@@ -236,6 +236,56 @@ def test_extra_tokens_overflow_fallback():
     print(f"[overflow] extra tokens: rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
 
 
+def test_extra_tokens_screen_bound():
+    """The first pass screens (row, tile) pairs with hi(qbar), the first bf16 term of the
+    pooled query, and widens its maxima by a bound on the difference to the exact score.
+    Built so that the screen ranks the wrong key first: every query alternates 2 and
+    2 + 2^-6 in dim 0 (qbar = 2 + 2^-7, exactly halfway, so hi = 2 and the residual is 2^-7)
+    and is 1 in dim 1.  Key A = (1, 255/256) screens at 2.99609375 but scores 3.00390625
+    exactly; key B = (0, 3) scores 3 either way; every other video tile holds keys
+    (0.5, 0.5), which win the coarse selection (so A's and B's tiles stay unlisted) and
+    score 1.50390625.  With one extra token every sparse row must take A, as the oracle
+    does: a missing or too small bound would leave A's tile out of the candidates."""
+    from workloads.synth import f32_to_bf16_bits
+    w = Workload("extra_screen", 1, ((SEG_TEXT, 64),), (8, 8, 16), 25.0, SINK_EXACT_KV, seed=103,
+                 recipe="scaled", extra=1)
+    x = make_inputs(w)
+    geom = O.map_geometry(w.segments(), *w.grid)
+    P = geom.n_prefix
+    q = np.zeros((1, w.n_tokens, 1, 128), np.float32)
+    q[0, 0::2, 0, 0] = 2.0
+    q[0, 1::2, 0, 0] = 2.0 + 2.0 ** -6
+    q[0, :, 0, 1] = 1.0
+    k = np.zeros_like(q)
+    ta, tb = P + 1, P + 6  # two of the 16 video tiles
+    for t in range(P, geom.n_tiles):
+        if t not in (ta, tb):
+            k[0, geom.tiles[t], 0, 0] = 0.5
+            k[0, geom.tiles[t], 0, 1] = 0.5
+    tok_a, tok_b = int(geom.tiles[ta][5]), int(geom.tiles[tb][7])
+    k[0, tok_a, 0, :2] = (1.0, 255.0 / 256.0)
+    k[0, tok_b, 0, :2] = (0.0, 3.0)
+    x = dict(x, q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k))
+    # the case is what it claims: hi(qbar) ranks B above A, the exact score A above B
+    qbar = np.float32(2.0 + 2.0 ** -7)
+    hi = np.float32(2.0)
+    assert hi * 1.0 + 255.0 / 256.0 < 3.0 < float(qbar) * 1.0 + 255.0 / 256.0
+    plan, ws, o, _ = run_gpu(w, x)
+    gpu = PAR.gpu_results_to_numpy(plan, ws, o)
+    _, inter = O.forward(x, w.segments(), w.grid, w.keep, w.sink, want_intermediates=True, extra_tokens=w.extra)
+    it = inter[(0, 0)]
+    rows = it["sparse_rows"]
+    assert len(rows) > 0
+    for i in rows:
+        assert ta not in it["lists"][i] and tb not in it["lists"][i], f"row {i} lists A's or B's tile"
+        xc = int(gpu["xcnt"][0, 0, i])
+        gx = gpu["xtok"][0, 0, i, :xc].astype(np.int64)
+        assert it["extras"][i].tolist() == [tok_a], f"row {i}: oracle extras {it['extras'][i]}"
+        assert gx.tolist() == [tok_a], f"row {i}: GPU extras {gx.tolist()} (A = {tok_a}, B = {tok_b})"
+    rep = PAR.check_parity(w, x, gpu)
+    print(f"[screen] extra tokens: rows={rep['rows']} max_abs={rep['max_abs']:.3e}", flush=True)
+
+
 def test_parity_no_gate():
     w = scaled_down(WORKLOADS["full"], heads=2, grid=(8, 16, 16), name="nogate")
     x = make_inputs(w)
