@@ -1208,9 +1208,9 @@ void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const floa
                      (const char*)k, qbar, lists, counts, x.tm1, x.tm4, x.ccnt, (u32x4*)x.qsplit);
   {
     const int nc = (g.Tq + 63) / 64;
-    auto thr = nc <= 16 ? vsa_extra_thr_kernel<16, 8> : nc <= 32 ? vsa_extra_thr_kernel<32, 8>
+    auto thr = nc <= 16 ? vsa_extra_thr_kernel<16, 4> : nc <= 32 ? vsa_extra_thr_kernel<32, 8>
              : nc <= 64 ? vsa_extra_thr_kernel<64, 4> : vsa_extra_thr_kernel<128, 2>;
-    const int R = nc <= 16 ? 8 : nc <= 32 ? 8 : nc <= 64 ? 4 : 2;
+    const int R = nc <= 16 ? 4 : nc <= 32 ? 8 : nc <= 64 ? 4 : 2;
     hipLaunchKernelGGL(thr, dim3((g.Qs + R - 1) / R * BH), dim3(64 * R), 0, st, g, qbar, x.knorm,
                        (const float*)x.tm1, (const float*)x.tm4, x.thr, x.mask);
   }
