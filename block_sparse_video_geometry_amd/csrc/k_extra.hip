@@ -49,7 +49,7 @@
 
 namespace {
 
-constexpr int XROWS = 64;   // sparse rows per workgroup, 16 per wave
+constexpr int XROWS = 64;   // streaming fallback: sparse rows per workgroup, 16 per wave
 constexpr int XCAP = 128;   // candidate buffer entries per row (a tile adds at most 64)
 constexpr int XSLACK = 16;  // a cut inside the stream may keep up to E + XSLACK entries
 
@@ -564,7 +564,8 @@ constexpr int X1ROWS = 128;
 constexpr int XNB = 3;
 // 16 bytes per lane from buffer offset voff into LDS at lds + 16 lane (M0 holds the LDS base).
 // Written as asm so that the compiler neither waits for it before unrelated LDS reads nor
-// counts it: the kernel waits for these loads itself.  Nothing else in the kernel uses M0.
+// counts it: the kernels that use it wait for these loads themselves, and nothing else in
+// them uses M0.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
