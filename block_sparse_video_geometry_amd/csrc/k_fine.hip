@@ -141,12 +141,14 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // the lane address is base_v[db] + 256 * (32c + 4h).
 // The DMA lane offsets below follow the same two swizzles.
 
+// XT: the plan has extra tokens (a sparse row may then run its extra tokens' tile first).
+template <bool XT>
 __global__ __launch_bounds__(64) void vsa_fine_kernel(
     VsaGeom g, const char* __restrict__ kptr, const char* __restrict__ vptr,
     const u32x4* __restrict__ q, const unsigned short* __restrict__ gate,
     const float* __restrict__ ocoarse, const int* __restrict__ lists,
     const int* __restrict__ counts, unsigned short* __restrict__ o, int per_xcd,
-    const char* __restrict__ kxptr, const char* __restrict__ vxptr, const int* __restrict__ xcnt) {
+    const int* __restrict__ xtok, const char* __restrict__ vxptr, const int* __restrict__ xcnt) {
   // a K tile and a V tile; separate arrays so LDS reads of one are never taken as aliasing
   // DMA writes in flight to the other.  About 33 KB in all, so four workgroups share a CU.
   __shared__ __attribute__((aligned(16))) char klds[TILE_BYTES];
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   for (int m = 0; m < 2; ++m) voff[m] = gi * rowbytes + ((pos ^ ((2 * gi + 8 * m) & 15)) << 4);
   // a sparse row's staged extra tokens (nx of them, none when the option is off) run first
   int nx = 0;
-  if (!dense && g.extra > 0) nx = __builtin_amdgcn_readfirstlane(xcnt[(size_t)bh * g.Qs + srow]);
+  if (XT && !dense) nx = __builtin_amdgcn_readfirstlane(xcnt[(size_t)bh * g.Qs + srow]);
   const int hx = nx > 0 ? 1 : 0;
   const unsigned plane = (unsigned)g.H * g.W * rowbytes;  // token stride dt -> bytes
   const unsigned line = (unsigned)g.W * rowbytes;         // token stride dh -> bytes
@@ -225,12 +227,14 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(kptr + bh_off), 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(vptr + bh_off), 0, nrec, 0x00020000);
-  // the first tile's resources: the staging buffers ([batch, Qs, 64, heads, 128]) when the
-  // row has extra tokens
-  const long long bhx_off = ((long long)b * g.Qs * VSA_MAX_EXTRA * g.heads + h) * (VSA_HEAD_DIM * 2);
-  const int nrec_x = (int)((unsigned)(g.Qs * VSA_MAX_EXTRA - 1) * rowbytes + VSA_HEAD_DIM * 2);
-  const __amdgpu_buffer_rsrc_t krs0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)uniform_ptr(hx ? kxptr + bhx_off : kptr + bh_off), 0, hx ? nrec_x : nrec, 0x00020000);
+  // The extra tokens' tile (a row with extra tokens runs it first): its K rows and V rows
+  // 0-31 are loaded in the prologue straight from K and V by token id; its V rows 32-63,
+  // which the loop loads during the tile's first phase like any tile's, come from the
+  // staging buffer [batch, Qs, 32, heads, 128].  Their resource starts 32 rows before the
+  // row's staging block, so that row r of the tile sits at the tile offset + r row bytes.
+  const long long bhx_off =
+      ((long long)b * g.Qs * VSA_XSTAGE * g.heads + h) * (VSA_HEAD_DIM * 2) - (long long)VSA_XSTAGE * rowbytes;
+  const int nrec_x = (int)((unsigned)(g.Qs * VSA_XSTAGE + VSA_XSTAGE - 1) * rowbytes + VSA_HEAD_DIM * 2);
   const __amdgpu_buffer_rsrc_t vrs0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(hx ? vxptr + bhx_off : vptr + bh_off), 0, hx ? nrec_x : nrec, 0x00020000);
 
@@ -283,8 +287,8 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     }
     d_off = (unsigned)tok0 * rowbytes;
     d_flags = (unsigned)video | ((unsigned)nvalid << 1);
-    if (j < hx) {  // the staged extra tokens: nx consecutive rows of the row's staging tile
-      d_off = (unsigned)srow * VSA_MAX_EXTRA * rowbytes;
+    if (j < hx) {  // the extra tokens' tile: nx valid rows; V rows 32-63 from the staging
+      d_off = (unsigned)srow * VSA_XSTAGE * rowbytes;
       d_flags = (unsigned)nx << 1;
     }
   };
@@ -377,6 +381,22 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   // the tile's (O and l rescaled) and P(j) is taken again.
   unsigned c_off = NO_TILE, c_flags = 0, n_off = NO_TILE, n_flags = 0;
   f32x4 scur[4][4];
+  // the extra tokens' tile: byte offset of the token row of this lane's row 4 n + gi in copy
+  // n (out of range past the nx tokens, so that row reads zero)
+  unsigned xo[16];
+  if (hx) {
+    const int* xt = xtok + ((size_t)bh * g.Qs + srow) * VSA_MAX_EXTRA;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int r = 4 * n + gi;
+      xo[n] = r < nx ? (unsigned)xt[r] * rowbytes : NO_TILE;
+    }
+  }
+  // copy n of the extra tokens' K or V rows 0-31: the token rows' 16-byte chunks, swizzled as
+  // the lane offsets koff / voff place them (their gi row term replaced by the token's row)
+  auto xdma = [&](__amdgpu_buffer_rsrc_t rs, unsigned vo, int n, unsigned buf) {
+    bdma16<0, true>(rs, xo[n] + (vo - (unsigned)gi * rowbytes), 0u, buf + 1024u * (unsigned)n);
+  };
   if (my_n > 0) {
     describe(0);
     c_off = __builtin_amdgcn_readlane(d_off, 0);
@@ -387,8 +407,13 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     }
     unsigned stp, stl;
     steps(c_flags, stp, stl);
+    if (hx) {
 #pragma unroll
-    for (int n = 0; n < 16; ++n) kdma_r(krs0, n, c_off, stp, stl);
+      for (int n = 0; n < 16; ++n) xdma(krs, koff[(n >> 1) & 3], n, kbuf_u);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) kdma_r(krs, n, c_off, stp, stl);
+    }
   }
   // Q, the epilogue's copies and K(0) landed.  A wait the compiler sees, on every path to
   // the loop, so it does not wait (whole queue) for the Q loads again inside the loop.
@@ -429,8 +454,13 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     steps(n_flags, n_stp, n_stl);
 #pragma unroll
     for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
+    if (hx) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) vdma_r(vrs0, n, c_off, stp, stl);
+      for (int n = 0; n < 8; ++n) xdma(vrs, voff[(n >> 1) & 1], n, vbuf_u);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) vdma_r(vrs0, n, c_off, stp, stl);
+    }
     if ((int)(c_flags >> 1) < VSA_TILE_TOKENS) mask(scur, (int)(c_flags >> 1));
     // the first tile sets the running max
 #pragma unroll
@@ -724,10 +754,11 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
                      const float* ocoarse, const int* lists, const int* counts, void* o,
-                     const void* kx, const void* vx, const int* xcnt, hipStream_t st) {
+                     const int* xtok, const void* vx, const int* xcnt, hipStream_t st) {
   const int total = g.batch * g.heads * g.Tq;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(vsa_fine_kernel, dim3(8 * per_xcd), dim3(64), (size_t)g.cap * sizeof(int), st, g, (const char*)k,
+  auto kern = g.extra > 0 ? vsa_fine_kernel<true> : vsa_fine_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(64), (size_t)g.cap * sizeof(int), st, g, (const char*)k,
                      (const char*)v, (const u32x4*)q, (const unsigned short*)gate, ocoarse, lists,
-                     counts, (unsigned short*)o, per_xcd, (const char*)kx, (const char*)vx, xcnt);
+                     counts, (unsigned short*)o, per_xcd, xtok, (const char*)vx, xcnt);
 }

@@ -132,7 +132,6 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   float* cpart = reinterpret_cast<float*>(ws + L.cpart);
   int* xtok = reinterpret_cast<int*>(ws + L.xtok);
   int* xcnt = reinterpret_cast<int*>(ws + L.xcnt);
-  void* kx = ws + L.kx;
   void* vx = ws + L.vx;
   VsaExtraBuffers xb;
   xb.tm1 = reinterpret_cast<float*>(ws + L.xtm1);
@@ -147,7 +146,6 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
   xb.pcnt = reinterpret_cast<int*>(ws + L.xpcnt);
   xb.xtok = xtok;
   xb.xcnt = xcnt;
-  xb.kx = kx;
   xb.vx = vx;
   void* o_user = o;
 
@@ -194,7 +192,7 @@ int vsa_launch_forward(const vsa_plan* plan, const void* q, const void* k, const
     VSA_STEP("select", vsa_launch_select(G, scores, thr, lists, counts, st));
     if (G.extra > 0) VSA_STEP("extra", vsa_launch_extra(G, k, v, qbar, lists, counts, xb, st));
   }
-  VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, kx, vx, xcnt, st));
+  VSA_STEP("fine", vsa_launch_fine(G, q, k, v, g, ocoarse, lists, counts, o, xtok, vx, xcnt, st));
   if (G.reblock) VSA_STEP("unpermute", vsa_launch_rb_unpermute(G, rb_tiles, o, o_user, st));
 #undef VSA_STEP
   return VSA_OK;

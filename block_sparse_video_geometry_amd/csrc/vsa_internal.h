@@ -12,7 +12,8 @@
 #define VSA_HEAD_DIM 128
 #define VSA_TILE_TOKENS 64
 #define VSA_COARSE_ROWS 64   // sparse rows per workgroup of the coarse kernel
-#define VSA_MAX_EXTRA 64     // extra tokens per sparse row (one staged tile)
+#define VSA_MAX_EXTRA 64     // extra tokens per sparse row (one tile)
+#define VSA_XSTAGE 32        // of their V rows, those past the first 32 are staged
 
 // Geometry and options of one plan, passed to every kernel by value.  Tile ids:
 // prefix tiles [0, P) in packed order, video tiles [P, P + Vt) raster (tt, th, tw).
@@ -57,7 +58,7 @@ constexpr int VSA_EXTRA_CAND = 1024;
 
 struct VsaLayout {        // byte offsets into the workspace
   size_t qbar, kbar, vbar, bias, anchor, scores, ocoarse, thr, lists, counts, statp;
-  size_t xtok, xcnt, kx, vx;  // extra tokens: ids, counts, staged K and V rows
+  size_t xtok, xcnt, vx;      // extra tokens: ids, counts, staged V rows 32-63 of their tile
   size_t xpart, xpcnt;        // extra tokens: per-segment best E of each row, and counts
   size_t xtm1, xtm4, xthr, xmask, xccnt, xcand;  // two-pass select: maxima, thresholds, candidates
   size_t xqsplit;                                // two-pass select: qbar as three bf16 terms

@@ -45,7 +45,7 @@ struct VsaExtraBuffers {
   unsigned long long* part;    // fallback: per-segment best E of each row
   int* pcnt;
   int *xtok, *xcnt;            // the extra tokens and their count per row
-  void *kx, *vx;               // staged K and V rows
+  void* vx;                    // staged V rows 32-63 of the extra tokens' tile
 };
 void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const float* qbar, const int* lists,
                       const int* counts, const VsaExtraBuffers& x, hipStream_t st);
@@ -61,7 +61,8 @@ void vsa_launch_rb_permute(const VsaGeom& g, const int* tiles, const void* q, co
 void vsa_launch_rb_unpermute(const VsaGeom& g, const int* tiles, const void* o2, void* o, hipStream_t st);
 
 // Block-sparse fine attention + gated combine, output in packed order; a sparse row's
-// staged extra tokens (kx, vx, xcnt; unused when the option is off) run as its first tile.
+// extra tokens (xtok, xcnt, and their staged V rows 32-63 in vx; unused when the option is
+// off) run as its first tile.
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
                      const float* ocoarse, const int* lists, const int* counts, void* o,
-                     const void* kx, const void* vx, const int* xcnt, hipStream_t st);
+                     const int* xtok, const void* vx, const int* xcnt, hipStream_t st);

@@ -226,8 +226,7 @@ extern "C" int vsa_plan_geometry(const vsa_segment* segs, int n_segs, int batch,
   const size_t xrows = g.extra > 0 ? (size_t)batch * g.Qs * VSA_MAX_EXTRA : 0;
   L.xtok = take(g.extra > 0 ? BH * (size_t)g.Qs * VSA_MAX_EXTRA * 4 : 0);
   L.xcnt = take(g.extra > 0 ? BH * (size_t)g.Qs * 4 : 0);
-  L.kx = take(xrows * heads * VSA_HEAD_DIM * 2);
-  L.vx = take(xrows * heads * VSA_HEAD_DIM * 2);
+  L.vx = take(xrows / VSA_MAX_EXTRA * VSA_XSTAGE * heads * VSA_HEAD_DIM * 2);
   {
     const size_t xrb = g.extra > 0 ? BH * (size_t)((g.Qs + 63) / 64) * g.xms * 64 : 0;  // segment rows
     L.xpart = take(xrb * VSA_MAX_EXTRA * 8);
