@@ -38,10 +38,11 @@
 // pass 2 0.24, fallback 0.01 (1.69 ms as one streaming pass, 0.82 with an exact pass 1).
 // About 75 candidate tiles per row pass the screen (65 with exact maxima).
 //
-// vsa_extra_gather_kernel: copies each row's extra K and V rows into staging
-// buffers laid out [batch, Qs, 64, heads, 128] (padding rows zero), i.e. with
-// the token stride of K and V themselves, so the fine kernel reads a row's
-// extra tokens as one more 64-row tile of consecutive rows.
+// vsa_extra_gather_kernel also copies the V rows of each row's extra tokens 32..63 into a
+// staging buffer [batch, Qs, 32, heads, 128] (padding rows zero), with the token stride of V
+// itself: the fine kernel runs the extra tokens as its first tile, reading their K rows and
+// V rows 0-31 by token id in its prologue, and these 32 V rows in its main loop like any
+// tile's, by base-plus-stride addressing.
 #include <type_traits>
 
 #include "vsa_device.h"

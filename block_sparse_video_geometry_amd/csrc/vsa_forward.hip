@@ -317,7 +317,7 @@ extern "C" int vsa_read_stats(const vsa_plan* plan, const void* workspace, void*
     kept += cnt[i] - G.npin;
   }
   for (size_t i = 0; i < xc.size(); ++i) {
-    pairs += xc[i] > 0 ? 1 : 0;  // the staged extra-token tile
+    pairs += xc[i] > 0 ? 1 : 0;  // the extra tokens' tile
     extra += xc[i];
   }
   out->executed_pairs = pairs;

@@ -191,7 +191,7 @@ typedef struct {
   int32_t k;                /* as in vsa_plan_desc */
   int32_t reserved;
   int64_t extra_tokens;     /* extra tokens attended over all sparse rows (executed_pairs
-                               counts each row's staged extra tile as one pair) */
+                               counts each row's extra-token tile as one pair) */
 } vsa_stats;
 
 /* Byte offsets into the workspace of the intermediates of the last forward
