@@ -38,9 +38,9 @@
 // location of the wave's tiles is computed 64 tiles at a time (one per lane)
 // and read back with readlane.
 //
-// Rows are ordered head-major, dense rows first, and mapped XCD-aware: the
-// hardware deals workgroup i to XCD i % 8, so XCD x receives a contiguous
-// range of heads and its L2 sees few heads' K/V at a time.
+// Rows are mapped XCD-aware: the hardware deals workgroup i to XCD i % 8, so XCD x
+// receives a contiguous head-major range of rows and its L2 sees few heads' K/V at a time;
+// within the range its dense rows run first, so that none of these long rows starts late.
 //
 // Extra tokens ("ComfyUI Agrega Nodo Central de Atencion Dispersa...", schedule
 // paragraph): a sparse row's extra key tokens, staged by the extra-token kernels
@@ -158,10 +158,26 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   extern __shared__ int lst_lds[];                     // a sparse row's list (cap entries)
 
   const int lane = threadIdx.x;
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= g.batch * g.heads * g.Tq) return;
-  const int bh = item / g.Tq;
-  const int qt = item - bh * g.Tq;
+  // XCD x takes the head-major item range [a, e); within it, its dense rows (the long ones)
+  // first, then its sparse rows, each in head-major order.  D(p) and S(p): dense and sparse
+  // items before head-major position p.
+  const int total = g.batch * g.heads * g.Tq;
+  const int a = (int)(blockIdx.x & 7) * per_xcd, k = (int)(blockIdx.x >> 3);
+  const int e = min(a + per_xcd, total);
+  if (a + k >= e) return;
+  const int nd = g.n_dense, ns = g.Tq - g.n_dense;
+  auto D = [&](int p) { return (p / g.Tq) * nd + min(p % g.Tq, nd); };
+  const int da = D(a), ndr = D(e) - da;
+  int bh, qt;
+  if (k < ndr) {
+    const int jd = da + k;
+    bh = jd / nd;
+    qt = jd - bh * nd;
+  } else {
+    const int js = (a / g.Tq) * ns + max(a % g.Tq - nd, 0) + (k - ndr);
+    bh = js / ns;
+    qt = nd + (js - bh * ns);
+  }
   const int b = bh / g.heads, h = bh - b * g.heads;
   const bool dense = qt < g.n_dense;
   const int srow = qt - g.n_dense;
