@@ -921,9 +921,14 @@ __global__ __launch_bounds__(256, 4) void vsa_extra_score_kernel(VsaGeom g, cons
   __shared__ int nrows_s[TPW];
   extern __shared__ int rowlist[];  // TPW x Qs entries
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
-  const size_t bh = blockIdx.y;
+  // XCD-aware: each XCD takes a contiguous range of (head, tile pair) items, head-major, so
+  // a head's split qbar rows are read through few L2s
+  const int ntp = (g.Tq + TPW - 1) / TPW;
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
+  const size_t bh = w / ntp;
   const int b = (int)(bh / g.heads), h = (int)(bh % g.heads);
-  const int tb = blockIdx.x * TPW;      // the first tile
+  const int tb = (w % ntp) * TPW;       // the first tile
   const int nt = min(TPW, g.Tq - tb);   // tiles of this workgroup
   const int nw = (g.Tq + 31) / 32;
   const unsigned rowbytes = (unsigned)g.heads * VSA_HEAD_DIM * 2;
@@ -1208,7 +1213,7 @@ void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const floa
   }
   {
     constexpr int TPW = 2;
-    hipLaunchKernelGGL(vsa_extra_score_kernel<TPW>, dim3((g.Tq + TPW - 1) / TPW, BH), dim3(256),
+    hipLaunchKernelGGL(vsa_extra_score_kernel<TPW>, dim3((g.Tq + TPW - 1) / TPW * BH), dim3(256),
                        4 * TPW * g.Qs, st, g, (const char*)k, (const float*)x.thr, (const unsigned*)x.mask,
                        x.ccnt, x.cand, (const u32x4*)x.qsplit);
   }
