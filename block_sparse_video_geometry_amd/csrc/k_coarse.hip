@@ -53,8 +53,13 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
   __shared__ float bs[CCH];
   __shared__ double red[4][2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  const size_t bh = (size_t)blockIdx.z * g.heads + blockIdx.y;
-  const int rb = (int)blockIdx.x / g.csplit, slice = (int)blockIdx.x % g.csplit;
+  // XCD-aware: each XCD takes a contiguous range of (batch x head, block) items, head-major,
+  // so a head's K-bar and V-bar are read through few L2s
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7;
+  const int w = xcd * (G >> 3) + min(xcd, G & 7) + (L >> 3);
+  const int blk = w % g.coarse_blocks;
+  const size_t bh = (size_t)(w / g.coarse_blocks);
+  const int rb = blk / g.csplit, slice = blk % g.csplit;
   const int c_begin = slice * g.cchunks * CCH;                  // this slice's candidate tiles:
   const int c_end = min(g.Kc, c_begin + g.cchunks * CCH);       // [c_begin, c_end)
   const int row = rb * CROWS + 16 * wave + lr;  // the sparse row of this lane's values
@@ -220,8 +225,8 @@ __global__ __launch_bounds__(256) void vsa_coarse_kernel(VsaGeom g, const float*
       a += red[w][0];
       q += red[w][1];
     }
-    statp[(bh * g.coarse_blocks + blockIdx.x) * 2 + 0] = a;
-    statp[(bh * g.coarse_blocks + blockIdx.x) * 2 + 1] = q;
+    statp[(bh * g.coarse_blocks + blk) * 2 + 0] = a;
+    statp[(bh * g.coarse_blocks + blk) * 2 + 1] = q;
   }
 }
 
@@ -266,7 +271,7 @@ void vsa_launch_coarse(const VsaGeom& g, const float* qbar, const float* kbar, c
                        const float* bias, float* scores, float* ocoarse, double* statp, float* cpart,
                        hipStream_t st) {
   if (g.Qs == 0) return;
-  dim3 grid(g.coarse_blocks, g.heads, g.batch);
+  dim3 grid(g.coarse_blocks * g.heads * g.batch);
   hipLaunchKernelGGL(vsa_coarse_kernel, grid, dim3(256), 0, st, g, qbar, kbar, vbar, bias, scores, ocoarse,
                      statp, cpart);
   if (g.csplit > 1)
