@@ -1092,7 +1092,7 @@ __device__ unsigned long long kth_key(const unsigned long long* keys, int n, int
 // for a row whose list overflowed, of the union of the fallback's segment lists.  It ranks them
 // by token and writes the row's extra tokens and count.  Then thread tid copies 64 bytes of
 // extra row tid >> 2 (zeros past the count) of K and of V.
-__global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const u32x4* __restrict__ v,
+__global__ __launch_bounds__(128) void vsa_extra_gather_kernel(VsaGeom g, const u32x4* __restrict__ v,
                                                                const int* __restrict__ ccnt,
                                                                const unsigned long long* __restrict__ xcand,
                                                                const unsigned long long* __restrict__ xpart,
@@ -1179,20 +1179,22 @@ __global__ __launch_bounds__(256) void vsa_extra_gather_kernel(VsaGeom g, const 
   __syncthreads();
   // the V rows of tokens 32..63 (the fine kernel reads the rest straight from K and V):
   // row 32 + e of the tile to row e of the [batch, Qs, 32, heads, 128] staging, head h
-  const int e = threadIdx.x >> 3, part = threadIdx.x & 7;
+  const int e = threadIdx.x >> 2, part = threadIdx.x & 3;
   const int n = mcnt;
-  const size_t dst = ((((size_t)b * g.Qs + s) * VSA_XSTAGE + e) * g.heads + h) * 16 + 2 * part;
-  u32x4 va[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  const size_t dst = ((((size_t)b * g.Qs + s) * VSA_XSTAGE + e) * g.heads + h) * 16 + 4 * part;
+  u32x4 va[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) va[i] = u32x4{0u, 0u, 0u, 0u};
   if (VSA_MAX_EXTRA - VSA_XSTAGE + e < n) {
     // (a token id outside the sequence cannot come from the select kernel; clamped all the
     // same, so that a read never leaves the (b, h) plane)
     const int tok = min(max(stok[VSA_MAX_EXTRA - VSA_XSTAGE + e], 0), g.N - 1);
-    const long long src = row_offset(g, b, tok, h) / 8 + 2 * part;
-    va[0] = v[src];
-    va[1] = v[src + 1];
+    const long long src = row_offset(g, b, tok, h) / 8 + 4 * part;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) va[i] = v[src + i];
   }
-  vx[dst] = va[0];
-  vx[dst + 1] = va[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vx[dst + i] = va[i];
 }
 
 }  // namespace
@@ -1219,7 +1221,7 @@ void vsa_launch_extra(const VsaGeom& g, const void* k, const void* v, const floa
   }
   hipLaunchKernelGGL(vsa_extra_select_kernel, dim3(g.xg), dim3(256), 0, st, g, (const u32x4*)k, qbar, lists, counts,
                      (const int*)x.ccnt, x.part, x.pcnt);
-  hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(256), 0, st, g,
+  hipLaunchKernelGGL(vsa_extra_gather_kernel, dim3(g.Qs, g.heads, g.batch), dim3(128), 0, st, g,
                      (const u32x4*)v, (const int*)x.ccnt, (const unsigned long long*)x.cand,
                      (const unsigned long long*)x.part, (const int*)x.pcnt, x.xtok, x.xcnt, (u32x4*)x.vx);
 }
