@@ -1,7 +1,7 @@
 """Benchmark of the two-branch video sparse attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload full]
-                    [--no-cpu-baseline] [--cpu-workers 16] [--cpu-heads H]
+                    [--no-cpu-baseline] [--cpu-workers 16] [--cpu-heads H] [--ceiling]
 
 One step = one whole vsa_forward (pool, [log-mass], coarse logits + softmax +
 O_coarse, [tau], selection, fine attention + gated combine) on the full clip
@@ -11,6 +11,9 @@ exact_kv_and_rows.  Inputs are seeded synthetic bf16 tensors, resident in HBM
 before timing starts.  Prints one JSON line: the headline times plain forwards;
 per-kernel times come from a second pass with HIP events between the kernels, and
 ms_per_step_graph from replays of the same forward captured into a HIP graph.
+With --ceiling the line also carries, for context, what two library kernels reach on
+the same device: a plain bf16 GEMM (torch.matmul, 8192^3) and torch's flash SDPA on
+the dense shape of the workload (every token against every token, all heads).
 """
 from __future__ import annotations
 
@@ -52,7 +55,49 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, copy this many MiB device-to-device (a kernel of known "
                          "traffic that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a plain bf16 GEMM and torch's flash SDPA on the workload's "
+                         "dense shape (library kernels, for context)")
     return ap.parse_args()
+
+
+def ceiling(torch, q, reps=3):
+    """TFLOP/s of two library kernels on the current device, HIP events on the current
+    stream: torch.matmul on 8192^3 bf16, and torch's flash SDPA (no other backend) with
+    every query against every key of q's shape [batch, N, heads, 128] (random values)."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    def timeit(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    gen = torch.Generator(device=q.device).manual_seed(0)
+    m = 8192
+    x = torch.randn(m, m, device=q.device, dtype=torch.bfloat16, generator=gen)
+    y = torch.randn(m, m, device=q.device, dtype=torch.bfloat16, generator=gen)
+    gms = timeit(lambda: torch.matmul(x, y), 20)
+    out["gemm_bf16_8192"] = {"ms": round(gms, 4), "tflops": round(2 * m ** 3 / (gms * 1e-3) / 1e12, 1)}
+    del x, y
+    B, N, H, D = q.shape
+    qs = torch.randn(B, H, N, D, device=q.device, dtype=torch.bfloat16, generator=gen)
+    ks, vs = torch.randn_like(qs), torch.randn_like(qs)
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            sms = timeit(lambda: F.scaled_dot_product_attention(qs, ks, vs), reps)
+        out["sdpa_flash_dense"] = {"ms": round(sms, 3), "n_tokens": N, "heads": H,
+                                   "tflops": round(4.0 * B * H * N * N * D / (sms * 1e-3) / 1e12, 1)}
+    except RuntimeError as ex:
+        out["sdpa_flash_dense"] = {"unavailable": str(ex)[:160]}
+    return out
 
 
 # inputs of the CPU baseline, read by forked workers (set before the pool starts)
@@ -281,6 +326,8 @@ def main():
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu
+    if a.ceiling:
+        line["ceiling"] = ceiling(torch, q)
     print(json.dumps(line), flush=True)
 
 
