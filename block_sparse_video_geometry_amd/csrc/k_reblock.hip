@@ -274,6 +274,7 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
 // 16 tokens per step, eight steps' loads in flight.
 constexpr int RB_CH = 2048;
 constexpr int RB_PART = 2 * VSA_HEAD_DIM;  // floats per chunk partial
+constexpr int RB_FNB = 8;                   // nodes per finish workgroup
 
 template <int MODE>
 __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsigned short* __restrict__ q,
@@ -374,78 +375,116 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
   }
 }
 
-// One node per workgroup (128 threads, one per dim).  The chunk sums added in chunk order and
-// divided by n; after the first pass mu = sum psi / n and z = C a0 = sum (psi.a0) psi / n -
-// mu (mu.a0); after a later pass z = sum / n.  Then a = M z / |z|_M (0 if |z|_M = 0; M rows
-// read from L2) and mu . a go to the node state.
+// Per node (128 threads, one per dim; RB_FNB nodes of one (batch, head) per workgroup, so
+// that each thread's row of M is read once for all of them).  The chunk sums added in chunk
+// order and divided by n; after the first pass mu = sum psi / n and z = C a0 = sum (psi.a0)
+// psi / n - mu (mu.a0); after a later pass z = sum / n.  Then a = M z / |z|_M (0 if
+// |z|_M = 0) and mu . a go to the node state.  A node's arithmetic, and its order, does not
+// depend on the other nodes of its workgroup.
 __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, const float* __restrict__ M,
                                                                      const float* __restrict__ a0,
                                                                      const float* __restrict__ part,
                                                                      float* __restrict__ state, int level,
                                                                      int cpn, int first) {
-  __shared__ float zs[VSA_HEAD_DIM];
-  __shared__ float red[3][2];
-  const int bh = blockIdx.y, node = blockIdx.x;
-  int t0, m;
-  node_range(g.Vt, level, node, t0, m);
-  if (m < 2) return;
+  __shared__ float zs[RB_FNB][VSA_HEAD_DIM];
+  __shared__ float red[RB_FNB][3][2];
+  const int bh = blockIdx.y;
   const int d = threadIdx.x, wave = d >> 6;
   const int nodes = 1 << level;
-  const float inv_n = 1.0f / (float)(VSA_TILE_TOKENS * m);
-  const float* pp = part + ((size_t)bh * nodes * cpn + (size_t)node * cpn) * RB_PART;
-  float* st = state + ((size_t)bh * nodes + node) * RB_STATE;
-  float v = 0.f, v2 = 0.f;
-  for (int c = 0; c < cpn; ++c) {
-    v += pp[(size_t)c * RB_PART + d];
-    if (first) v2 += pp[(size_t)c * RB_PART + VSA_HEAD_DIM + d];
+  const int n0 = blockIdx.x * RB_FNB;
+  const float a0d = first ? a0[(size_t)bh * VSA_HEAD_DIM + d] : 0.f;
+  float mu[RB_FNB], z[RB_FNB], v2s[RB_FNB], inv_n[RB_FNB];
+  bool live[RB_FNB];
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) {
+    const int node = n0 + i;
+    int t0 = 0, m = 0;
+    if (node < nodes) node_range(g.Vt, level, node, t0, m);
+    live[i] = m >= 2;
+    mu[i] = z[i] = v2s[i] = 0.f;
+    inv_n[i] = live[i] ? 1.0f / (float)(VSA_TILE_TOKENS * m) : 0.f;
+    if (!live[i]) continue;
+    const float* pp = part + ((size_t)bh * nodes * cpn + (size_t)node * cpn) * RB_PART;
+    float v = 0.f, v2 = 0.f;
+    for (int c = 0; c < cpn; ++c) {
+      v += pp[(size_t)c * RB_PART + d];
+      if (first) v2 += pp[(size_t)c * RB_PART + VSA_HEAD_DIM + d];
+    }
+    if (first) {
+      mu[i] = v * inv_n[i];
+      v2s[i] = v2;
+    } else {
+      mu[i] = state[((size_t)bh * nodes + node) * RB_STATE + d];
+      z[i] = v * inv_n[i];
+    }
   }
-  float mu, z;
   if (first) {
-    mu = v * inv_n;
-    const float ma0 = wave_sum(mu * a0[(size_t)bh * VSA_HEAD_DIM + d]);
-    if ((d & 63) == 0) red[0][wave] = ma0;
+#pragma unroll
+    for (int i = 0; i < RB_FNB; ++i) {
+      const float ma0 = wave_sum(mu[i] * a0d);
+      if ((d & 63) == 0) red[i][0][wave] = ma0;
+    }
     __syncthreads();
-    z = v2 * inv_n - mu * (red[0][0] + red[0][1]);
-    st[d] = mu;
-  } else {
-    mu = st[d];
-    z = v * inv_n;
+#pragma unroll
+    for (int i = 0; i < RB_FNB; ++i) {
+      if (!live[i]) continue;
+      z[i] = v2s[i] * inv_n[i] - mu[i] * (red[i][0][0] + red[i][0][1]);
+      state[((size_t)bh * nodes + n0 + i) * RB_STATE + d] = mu[i];
+    }
   }
-  zs[d] = z;
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) zs[i][d] = z[i];
   __syncthreads();
   const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
-  float av = 0.f;
-#pragma unroll 8
+  float av[RB_FNB];
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) av[i] = 0.f;
+#pragma unroll 4
   for (int e = 0; e < VSA_HEAD_DIM; e += 4) {
     const f32x4 mr = *reinterpret_cast<const f32x4*>(Mr + e);
-    av = fmaf(mr[0], zs[e], av);
-    av = fmaf(mr[1], zs[e + 1], av);
-    av = fmaf(mr[2], zs[e + 2], av);
-    av = fmaf(mr[3], zs[e + 3], av);
+#pragma unroll
+    for (int i = 0; i < RB_FNB; ++i) {
+      av[i] = fmaf(mr[0], zs[i][e], av[i]);
+      av[i] = fmaf(mr[1], zs[i][e + 1], av[i]);
+      av[i] = fmaf(mr[2], zs[i][e + 2], av[i]);
+      av[i] = fmaf(mr[3], zs[i][e + 3], av[i]);
+    }
   }
-  const float za = wave_sum(z * av);
-  if ((d & 63) == 0) red[1][wave] = za;
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) {
+    const float za = wave_sum(z[i] * av[i]);
+    if ((d & 63) == 0) red[i][1][wave] = za;
+  }
   __syncthreads();
-  const float zat = red[1][0] + red[1][1];
-  const float sc = zat > 0.f ? 1.0f / sqrtf(zat) : 0.f;
-  av *= sc;
-  const float ma = wave_sum(mu * av);
-  if ((d & 63) == 0) red[2][wave] = ma;
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) {
+    const float zat = red[i][1][0] + red[i][1][1];
+    const float sc = zat > 0.f ? 1.0f / sqrtf(zat) : 0.f;
+    av[i] *= sc;
+    const float ma = wave_sum(mu[i] * av[i]);
+    if ((d & 63) == 0) red[i][2][wave] = ma;
+  }
   __syncthreads();
-  st[VSA_HEAD_DIM + d] = av;
-  if (d == 0) st[2 * VSA_HEAD_DIM] = red[2][0] + red[2][1];
+#pragma unroll
+  for (int i = 0; i < RB_FNB; ++i) {
+    if (!live[i]) continue;
+    float* st = state + ((size_t)bh * nodes + n0 + i) * RB_STATE;
+    st[VSA_HEAD_DIM + d] = av[i];
+    if (d == 0) st[2 * VSA_HEAD_DIM] = red[i][2][0] + red[i][2][1];
+  }
 }
 
 // Per node: the split.  k = 64 floor(m/2); the k-th smallest key T by a four-round 8-bit MSB
 // radix search, need = the number of keys equal to T among the k smallest; then a stable
 // partition in position order (positions are ascending tokens): left = keys below T and the
 // first `need` keys equal to T.
-__global__ __launch_bounds__(1024) void vsa_rb_split_kernel(VsaGeom g, const float* __restrict__ pbuf,
+template <int BS>
+__global__ __launch_bounds__(BS) void vsa_rb_split_kernel(VsaGeom g, const float* __restrict__ pbuf,
                                                             const int* __restrict__ src, int* __restrict__ dst,
                                                             int level) {
   __shared__ unsigned hist[256];
   __shared__ unsigned s_sel[2];
-  __shared__ unsigned wsum[2][16];
+  __shared__ unsigned wsum[2][BS / 64];
   const int bh = blockIdx.y, node = blockIdx.x;
   int t0, m;
   node_range(g.Vt, level, node, t0, m);
@@ -463,9 +502,9 @@ __global__ __launch_bounds__(1024) void vsa_rb_split_kernel(VsaGeom g, const flo
   unsigned prefix = 0u, mask = 0u, kk = k;
   for (int round = 0; round < 4; ++round) {
     const int shift = 24 - 8 * round;
-    for (int i = tid; i < 256; i += 1024) hist[i] = 0u;
+    for (int i = tid; i < 256; i += BS) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) {
+    for (int i = tid; i < n; i += BS) {
       const unsigned key = fkey(pb[i]);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
@@ -511,9 +550,9 @@ __global__ __launch_bounds__(1024) void vsa_rb_split_kernel(VsaGeom g, const flo
   }
   const unsigned T = prefix;
   const unsigned need = kk;  // keys equal to T that go left (the first ones in position order)
-  // stable partition, 1024 positions per step
+  // stable partition, BS positions per step
   unsigned eq_before = 0u, left_before = 0u;
-  for (int i0 = 0; i0 < n; i0 += 1024) {
+  for (int i0 = 0; i0 < n; i0 += BS) {
     const int i = i0 + tid;
     const bool valid = i < n;
     const unsigned key = valid ? fkey(pb[i]) : 0xFFFFFFFFu;
@@ -524,7 +563,7 @@ __global__ __launch_bounds__(1024) void vsa_rb_split_kernel(VsaGeom g, const flo
     __syncthreads();
     unsigned eq_rank = eq_before + eq_in_wave;
     unsigned eq_tot = 0u;
-    for (int w2 = 0; w2 < 16; ++w2) {
+    for (int w2 = 0; w2 < BS / 64; ++w2) {
       const unsigned cnt = wsum[0][w2];
       if (w2 < wave) eq_rank += cnt;
       eq_tot += cnt;
@@ -536,7 +575,7 @@ __global__ __launch_bounds__(1024) void vsa_rb_split_kernel(VsaGeom g, const flo
     __syncthreads();
     unsigned lrank = left_before + l_in_wave;
     unsigned l_tot = 0u;
-    for (int w2 = 0; w2 < 16; ++w2) {
+    for (int w2 = 0; w2 < BS / 64; ++w2) {
       const unsigned cnt = wsum[1][w2];
       if (w2 < wave) lrank += cnt;
       l_tot += cnt;
@@ -636,19 +675,27 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
   const int levels = vsa_reblock_levels(g.Vt);
   for (int L = 0; L < levels; ++L) {
     const int cpn = vsa_reblock_chunks(g.Vt, L);
-    const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH);
+    const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH), fgrid(((1 << L) + RB_FNB - 1) / RB_FNB, BH);
     // power step 1 (z from 1: the direction a0 is the head's), steps 2 .. RB_STEPS
     hipLaunchKernelGGL(vsa_rb_pass_kernel<0>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                        cpn);
-    hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 1);
+    hipLaunchKernelGGL(vsa_rb_finish_kernel, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 1);
     for (int s = 1; s < RB_STEPS; ++s) {
       hipLaunchKernelGGL(vsa_rb_pass_kernel<1>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                          cpn);
-      hipLaunchKernelGGL(vsa_rb_finish_kernel, ngrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 0);
+      hipLaunchKernelGGL(vsa_rb_finish_kernel, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 0);
     }
     hipLaunchKernelGGL(vsa_rb_pass_kernel<2>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                        cpn);
-    hipLaunchKernelGGL(vsa_rb_split_kernel, ngrid, dim3(1024), 0, st, g, pbuf, src, dst, L);
+    // the split's workgroup size: the level's largest node, rounded up to 256, 512 or 1024
+    // tokens (the result does not depend on it)
+    const int nmax = VSA_TILE_TOKENS * ((g.Vt + (1 << L) - 1) >> L);
+    if (nmax <= 256)
+      hipLaunchKernelGGL(vsa_rb_split_kernel<256>, ngrid, dim3(256), 0, st, g, pbuf, src, dst, L);
+    else if (nmax <= 512)
+      hipLaunchKernelGGL(vsa_rb_split_kernel<512>, ngrid, dim3(512), 0, st, g, pbuf, src, dst, L);
+    else
+      hipLaunchKernelGGL(vsa_rb_split_kernel<1024>, ngrid, dim3(1024), 0, st, g, pbuf, src, dst, L);
     int* t = src;
     src = dst;
     dst = t;
