@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
 // 16 tokens per step, eight steps' loads in flight.
 constexpr int RB_CH = 2048;
 constexpr int RB_PART = 2 * VSA_HEAD_DIM;  // floats per chunk partial
-constexpr int RB_FNB = 8;                   // nodes per finish workgroup
+constexpr int RB_FNB = 8;                   // most nodes per finish workgroup
 
 template <int MODE>
 __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsigned short* __restrict__ q,
@@ -375,28 +375,29 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
   }
 }
 
-// Per node (128 threads, one per dim; RB_FNB nodes of one (batch, head) per workgroup, so
-// that each thread's row of M is read once for all of them).  The chunk sums added in chunk
+// Per node (128 threads, one per dim; NB nodes of one (batch, head) per workgroup, so that
+// each thread's row of M is read once for all of them).  The chunk sums added in chunk
 // order and divided by n; after the first pass mu = sum psi / n and z = C a0 = sum (psi.a0)
 // psi / n - mu (mu.a0); after a later pass z = sum / n.  Then a = M z / |z|_M (0 if
 // |z|_M = 0) and mu . a go to the node state.  A node's arithmetic, and its order, does not
 // depend on the other nodes of its workgroup.
+template <int NB>
 __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, const float* __restrict__ M,
                                                                      const float* __restrict__ a0,
                                                                      const float* __restrict__ part,
                                                                      float* __restrict__ state, int level,
                                                                      int cpn, int first) {
-  __shared__ float zs[RB_FNB][VSA_HEAD_DIM];
-  __shared__ float red[RB_FNB][3][2];
+  __shared__ float zs[NB][VSA_HEAD_DIM];
+  __shared__ float red[NB][3][2];
   const int bh = blockIdx.y;
   const int d = threadIdx.x, wave = d >> 6;
   const int nodes = 1 << level;
-  const int n0 = blockIdx.x * RB_FNB;
+  const int n0 = blockIdx.x * NB;
   const float a0d = first ? a0[(size_t)bh * VSA_HEAD_DIM + d] : 0.f;
-  float mu[RB_FNB], z[RB_FNB], v2s[RB_FNB], inv_n[RB_FNB];
-  bool live[RB_FNB];
+  float mu[NB], z[NB], v2s[NB], inv_n[NB];
+  bool live[NB];
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const int node = n0 + i;
     int t0 = 0, m = 0;
     if (node < nodes) node_range(g.Vt, level, node, t0, m);
@@ -420,30 +421,30 @@ __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, 
   }
   if (first) {
 #pragma unroll
-    for (int i = 0; i < RB_FNB; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const float ma0 = wave_sum(mu[i] * a0d);
       if ((d & 63) == 0) red[i][0][wave] = ma0;
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < RB_FNB; ++i) {
+    for (int i = 0; i < NB; ++i) {
       if (!live[i]) continue;
       z[i] = v2s[i] * inv_n[i] - mu[i] * (red[i][0][0] + red[i][0][1]);
       state[((size_t)bh * nodes + n0 + i) * RB_STATE + d] = mu[i];
     }
   }
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) zs[i][d] = z[i];
+  for (int i = 0; i < NB; ++i) zs[i][d] = z[i];
   __syncthreads();
   const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
-  float av[RB_FNB];
+  float av[NB];
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) av[i] = 0.f;
+  for (int i = 0; i < NB; ++i) av[i] = 0.f;
 #pragma unroll 4
   for (int e = 0; e < VSA_HEAD_DIM; e += 4) {
     const f32x4 mr = *reinterpret_cast<const f32x4*>(Mr + e);
 #pragma unroll
-    for (int i = 0; i < RB_FNB; ++i) {
+    for (int i = 0; i < NB; ++i) {
       av[i] = fmaf(mr[0], zs[i][e], av[i]);
       av[i] = fmaf(mr[1], zs[i][e + 1], av[i]);
       av[i] = fmaf(mr[2], zs[i][e + 2], av[i]);
@@ -451,13 +452,13 @@ __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, 
     }
   }
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const float za = wave_sum(z[i] * av[i]);
     if ((d & 63) == 0) red[i][1][wave] = za;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const float zat = red[i][1][0] + red[i][1][1];
     const float sc = zat > 0.f ? 1.0f / sqrtf(zat) : 0.f;
     av[i] *= sc;
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, 
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < RB_FNB; ++i) {
+  for (int i = 0; i < NB; ++i) {
     if (!live[i]) continue;
     float* st = state + ((size_t)bh * nodes + n0 + i) * RB_STATE;
     st[VSA_HEAD_DIM + d] = av[i];
@@ -676,14 +677,29 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
   for (int L = 0; L < levels; ++L) {
     const int cpn = vsa_reblock_chunks(g.Vt, L);
     const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH), fgrid(((1 << L) + RB_FNB - 1) / RB_FNB, BH);
+    // finish: min(RB_FNB, nodes) nodes per workgroup
+    auto finish = [&](int first) {
+      if (L == 0)
+        hipLaunchKernelGGL(vsa_rb_finish_kernel<1>, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn,
+                           first);
+      else if (L == 1)
+        hipLaunchKernelGGL(vsa_rb_finish_kernel<2>, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn,
+                           first);
+      else if (L == 2)
+        hipLaunchKernelGGL(vsa_rb_finish_kernel<4>, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn,
+                           first);
+      else
+        hipLaunchKernelGGL(vsa_rb_finish_kernel<RB_FNB>, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L,
+                           cpn, first);
+    };
     // power step 1 (z from 1: the direction a0 is the head's), steps 2 .. RB_STEPS
     hipLaunchKernelGGL(vsa_rb_pass_kernel<0>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                        cpn);
-    hipLaunchKernelGGL(vsa_rb_finish_kernel, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 1);
+    finish(1);
     for (int s = 1; s < RB_STEPS; ++s) {
       hipLaunchKernelGGL(vsa_rb_pass_kernel<1>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                          cpn);
-      hipLaunchKernelGGL(vsa_rb_finish_kernel, fgrid, dim3(VSA_HEAD_DIM), 0, st, g, M, a0, part, state, L, cpn, 0);
+      finish(0);
     }
     hipLaunchKernelGGL(vsa_rb_pass_kernel<2>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
                        cpn);
