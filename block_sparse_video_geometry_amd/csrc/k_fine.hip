@@ -42,6 +42,13 @@
 // receives a contiguous head-major range of rows and its L2 sees few heads' K/V at a time;
 // within the range its dense rows run first, so that none of these long rows starts late.
 //
+// The dense call (every row dense, every row the same list of all tiles) runs the same
+// pipeline four query tiles at a time: a workgroup of four waves, one per SIMD, of one
+// (batch, head), moving through the tiles in step.  Each wave copies a quarter of every K
+// and V half-tile into the buffers the four share, waits for its own copies and meets the
+// others at a barrier before the half is read, and before it is refilled once all four
+// have read it.  Per wave the arithmetic, and its order, is unchanged.
+//
 // Extra tokens ("ComfyUI Agrega Nodo Central de Atencion Dispersa...", schedule
 // paragraph): a sparse row's extra key tokens, staged by the extra-token kernels
 // as 64 consecutive rows (padding zero) with the token stride of K and V, run as
@@ -142,8 +149,11 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // The DMA lane offsets below follow the same two swizzles.
 
 // XT: the plan has extra tokens (a sparse row may then run its extra tokens' tile first).
-template <bool XT>
-__global__ __launch_bounds__(64) void vsa_fine_kernel(
+// SH: every row is dense (the dense call): a workgroup of four waves, one per SIMD, runs four
+// query tiles of one (batch, head) in step over the same key tiles, each wave copying a
+// quarter of every K and V tile into LDS buffers the four share.
+template <bool XT, bool SH>
+__global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
     VsaGeom g, const char* __restrict__ kptr, const char* __restrict__ vptr,
     const u32x4* __restrict__ q, const unsigned short* __restrict__ gate,
     const float* __restrict__ ocoarse, const int* __restrict__ lists,
@@ -153,33 +163,47 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   // DMA writes in flight to the other.  About 33 KB in all, so four workgroups share a CU.
   __shared__ __attribute__((aligned(16))) char klds[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char vlds[TILE_BYTES];
-  __shared__ float lbuf[64];
+  __shared__ float lbuf[SH ? 256 : 64];
   __shared__ int seg_lds[3][VSA_MAX_PREFIX_SEGS + 1];  // prefix segment table (start, len, tile0)
   extern __shared__ int lst_lds[];                     // a sparse row's list (cap entries)
+  // (SH: no lists; the dynamic area holds the O^T staging of waves 1-3 instead, wave 0
+  // staging in the K and V buffers)
 
-  const int lane = threadIdx.x;
+  const int lane = SH ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+  const int wv = SH ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   // XCD x takes the head-major item range [a, e); within it, its dense rows (the long ones)
   // first, then its sparse rows, each in head-major order.  D(p) and S(p): dense and sparse
   // items before head-major position p.
-  const int total = g.batch * g.heads * g.Tq;
-  const int a = (int)(blockIdx.x & 7) * per_xcd, k = (int)(blockIdx.x >> 3);
-  const int e = min(a + per_xcd, total);
-  if (a + k >= e) return;
-  const int nd = g.n_dense, ns = g.Tq - g.n_dense;
-  auto D = [&](int p) { return (p / g.Tq) * nd + min(p % g.Tq, nd); };
-  const int da = D(a), ndr = D(e) - da;
   int bh, qt;
-  if (k < ndr) {
-    const int jd = da + k;
-    bh = jd / nd;
-    qt = jd - bh * nd;
+  if (SH) {
+    // XCD x takes the head-major range of groups of four query tiles [a, a + per_xcd)
+    const int ng = (g.Tq + 3) >> 2;
+    const int total = g.batch * g.heads * ng;
+    const int a = (int)(blockIdx.x & 7) * per_xcd, k = (int)(blockIdx.x >> 3);
+    if (a + k >= min(a + per_xcd, total)) return;  // the whole workgroup
+    bh = (a + k) / ng;
+    qt = 4 * (a + k - bh * ng) + wv;  // past the last tile: a wave that only keeps step
   } else {
-    const int js = (a / g.Tq) * ns + max(a % g.Tq - nd, 0) + (k - ndr);
-    bh = js / ns;
-    qt = nd + (js - bh * ns);
+    const int total = g.batch * g.heads * g.Tq;
+    const int a = (int)(blockIdx.x & 7) * per_xcd, k = (int)(blockIdx.x >> 3);
+    const int e = min(a + per_xcd, total);
+    if (a + k >= e) return;
+    const int nd = g.n_dense, ns = g.Tq - g.n_dense;
+    auto D = [&](int p) { return (p / g.Tq) * nd + min(p % g.Tq, nd); };
+    const int da = D(a), ndr = D(e) - da;
+    if (k < ndr) {
+      const int jd = da + k;
+      bh = jd / nd;
+      qt = jd - bh * nd;
+    } else {
+      const int js = (a / g.Tq) * ns + max(a % g.Tq - nd, 0) + (k - ndr);
+      bh = js / ns;
+      qt = nd + (js - bh * ns);
+    }
   }
   const int b = bh / g.heads, h = bh - b * g.heads;
-  const bool dense = qt < g.n_dense;
+  const bool qvalid = !SH || qt < g.Tq;
+  const bool dense = SH || qt < g.n_dense;
   const int srow = qt - g.n_dense;
   const int grp = lane >> 4, ql = lane & 15;
   // Q^T operands: lane holds queries 16 qb + ql, dims 32 ks + 8 grp .. +7.  Issued first,
@@ -187,7 +211,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   bf16x8 qv[4][4];
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    const int tok = tile_token(g, qt, 16 * qb + ql);
+    const int tok = qvalid ? tile_token(g, qt, 16 * qb + ql) : -1;
     if (tok >= 0) {
       const u32x4* qp = q + row_offset(g, b, tok, h) / 8;
 #pragma unroll
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     for (int i = lane; i < g.cap; i += 64) lst_lds[i] = lst[i];
     nlist = min(cnt, g.cap);
   }
-  if (lane <= VSA_MAX_PREFIX_SEGS) {
+  if (wv == 0 && lane <= VSA_MAX_PREFIX_SEGS) {
     seg_lds[0][lane] = lane < VSA_MAX_PREFIX_SEGS ? g.pre_start[lane] : 0;
     seg_lds[1][lane] = lane < VSA_MAX_PREFIX_SEGS ? g.pre_len[lane] : 0;
     seg_lds[2][lane] = g.pre_tile0[lane];
@@ -338,6 +362,27 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   };
   auto kdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { kdma_r(krs, n, off, stp, stl); };
   auto vdma = [&](int n, unsigned off, unsigned stp, unsigned stl) { vdma_r(vrs, n, off, stp, stl); };
+  // SH: this wave's quarter of a 32-row half (hf = 0: rows 0-31, 1: rows 32-63) of a shared
+  // tile: copies n = 8 hf + 2 wv and n + 1, one M0 write for the pair.  M0 takes the LDS
+  // address of copy n itself, so the pair's immediates are 0 and 1024 (copy n + 1's source
+  // offset takes the 1024 off again).  Their lane offsets are those of koff / voff for this n.
+  const unsigned kofw = gi * rowbytes + ((pos ^ (gi | ((wv & 3) << 2))) << 4);
+  const unsigned vofw = gi * rowbytes + ((pos ^ ((2 * gi + 8 * (wv & 1)) & 15)) << 4);
+  auto dma_q = [&](__amdgpu_buffer_rsrc_t rs, unsigned vo, int hf, unsigned off, unsigned stp, unsigned stl,
+                   unsigned buf) {
+    const unsigned n = 8u * (unsigned)hf + 2u * (unsigned)wv, r = n & 3u;
+    const unsigned so = off + (n >> 2) * stp + r * stl;
+    const unsigned lds = __builtin_amdgcn_readfirstlane(buf + 4096u * (n >> 2) + 1024u * r);
+    bdma16<0, true>(rs, vo, so, lds);
+    bdma16<1024, false>(rs, vo, so + stl - 1024u, lds);
+  };
+  auto kdma_q = [&](int hf, unsigned off, unsigned stp, unsigned stl) { dma_q(krs, kofw, hf, off, stp, stl, kbuf_u); };
+  auto vdma_q = [&](int hf, unsigned off, unsigned stp, unsigned stl) { dma_q(vrs, vofw, hf, off, stp, stl, vbuf_u); };
+  // SH: the four waves meet (no memory wait of its own: each wave waits for its own copies
+  // and LDS reads just before)
+  auto meet = [&]() {
+    if (SH) __builtin_amdgcn_s_barrier();
+  };
 
   f32x4 oacc[8][4];
 #pragma unroll
@@ -423,7 +468,10 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     }
     unsigned stp, stl;
     steps(c_flags, stp, stl);
-    if (hx) {
+    if (SH) {
+      kdma_q(0, c_off, stp, stl);
+      kdma_q(1, c_off, stp, stl);
+    } else if (hx) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) xdma(krs, koff[(n >> 1) & 3], n, kbuf_u);
     } else {
@@ -434,6 +482,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   // Q, the epilogue's copies and K(0) landed.  A wait the compiler sees, on every path to
   // the loop, so it does not wait (whole queue) for the Q loads again inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
+  meet();  // SH: every wave's quarter of K(0) landed
   if (my_n > 0) {
     unsigned stp, stl;
     steps(c_flags, stp, stl);
@@ -466,11 +515,19 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     // K buffer is free once its reads returned: K(1) (zeros past the end of the list), then
     // V(0) rows 0-31, as iteration 0 expects them in flight
     wait_lgkm0();
+    meet();  // SH: every wave has read K(0)
     unsigned n_stp, n_stl;
     steps(n_flags, n_stp, n_stl);
+    if (SH) {
+      kdma_q(0, n_off, n_stp, n_stl);
+      kdma_q(1, n_off, n_stp, n_stl);
+      vdma_q(0, c_off, stp, stl);
+    } else {
 #pragma unroll
-    for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
-    if (hx) {
+      for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
+    }
+    if (SH) {
+    } else if (hx) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) xdma(vrs, voff[(n >> 1) & 1], n, vbuf_u);
     } else {
@@ -532,7 +589,12 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     // ---- R1.  On the last tile the K buffer holds the zeros loaded for the tile past the
     // end; that product is not used, and costs nothing next to the softmax beside it.
     // K(j+1) rows 0-31 landed (in flight after them: K(j+1) rows 32-63, V(j) rows 0-31).
-    wait_vm<16>();
+    if (SH) {
+      wait_vm<4>();  // own K(j+1) rows 0-31 (after them: K(j+1) rows 32-63, V(j) rows 0-31)
+      meet();
+    } else {
+      wait_vm<16>();
+    }
     f32x4 snext[4][4];
     {
       bf16x8 ka[2];
@@ -541,7 +603,17 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
       for (int s = 0; s < 16; ++s) {
         // K(j+1) rows 32-63 landed before their first read (in flight after them: V(j)
         // rows 0-31 and the 7 loads of V(j) rows 32-63 issued so far)
-        if (s == 7) wait_vm<15>();
+        if (s == 7) {
+          if (SH) {
+            // own K(j+1) rows 32-63 (after them: V(j) rows 0-31, V(j) rows 32-63), and this
+            // wave's reads of rows 0-31 done before any wave refills them
+            wait_lgkm0();
+            wait_vm<4>();
+            meet();
+          } else {
+            wait_vm<15>();
+          }
+        }
         if (s < 15) ka[(s + 1) & 1] = kread(s + 1);
         const int kb = s >> 2, ks = s & 3;
 #pragma unroll
@@ -556,10 +628,14 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
           __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (s < 8)
+        if (SH) {
+          if (s == 0) vdma_q(1, c_off, c_stp, c_stl);    // V(j) rows 32-63
+          if (s == 8) kdma_q(0, nn_off, nn_stp, nn_stl);  // K(j+2) rows 0-31
+        } else if (s < 8) {
           vdma_r(vrs_c, 8 + s, c_off, c_stp, c_stl);  // V(j) rows 32-63
-        else
+        } else {
           kdma(s - 8, nn_off, nn_stp, nn_stl);  // K(j+2) rows 0-31 (read by steps 0-7)
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -649,7 +725,12 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
     // ---- R2.  K(j+1) reads returned (the K buffer may be refilled); V(j) rows 0-31 landed
     // (in flight after them: V(j) rows 32-63, K(j+2) rows 0-31).
     wait_lgkm0();
-    wait_vm<16>();
+    if (SH) {
+      wait_vm<4>();  // own V(j) rows 0-31 (after them: V(j) rows 32-63, K(j+2) rows 0-31)
+      meet();
+    } else {
+      wait_vm<16>();
+    }
     // S(j+1) is read out of the accumulator registers below: cover the MFMA-result latency
     // (the barrier keeps the QK MFMAs above the NOPs)
     __builtin_amdgcn_sched_barrier(0);
@@ -662,7 +743,17 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
       for (int u = 0; u < 16; ++u) {
         // V(j) rows 32-63 landed before their first read (in flight after them: K(j+2)
         // rows 0-31 and the 7 loads of K(j+2) rows 32-63 issued so far)
-        if (u == 7) wait_vm<15>();
+        if (u == 7) {
+          if (SH) {
+            // own V(j) rows 32-63 (after them: K(j+2) rows 0-31, K(j+2) rows 32-63), and this
+            // wave's reads of rows 0-31 done before any wave refills them
+            wait_lgkm0();
+            wait_vm<4>();
+            meet();
+          } else {
+            wait_vm<15>();
+          }
+        }
         if (u < 15) va[(u + 1) & 1] = vread(u + 1);
         const int c = u >> 3, db = u & 7;
 #pragma unroll
@@ -672,10 +763,14 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
           scur[u >> 2][u & 3][qb] = acc_read(snext[u >> 2][u & 3][qb]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (u < 8)
+        if (SH) {
+          if (u == 0) kdma_q(1, nn_off, nn_stp, nn_stl);  // K(j+2) rows 32-63
+          if (u == 8) vdma_q(0, n_off, n_stp, n_stl);     // V(j+1) rows 0-31
+        } else if (u < 8) {
           kdma(8 + u, nn_off, nn_stp, nn_stl);  // K(j+2) rows 32-63 (read by R1 steps 8-15)
-        else
+        } else {
           vdma(u - 8, n_off, n_stp, n_stl);  // V(j+1) rows 0-31 (read by steps 0-7)
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -691,6 +786,10 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   // the loads issued past the end of the list (out of range, writing zeros) must land
   // before the K buffer is reused below
   wait_vm<0>();
+  if (SH) {
+    wait_lgkm0();
+    meet();  // every wave is done with the shared K and V buffers
+  }
   // ---- O and l to LDS.  Softmax statistics are per lane for queries 16 qb + ql; O is
   // held as oacc[db][qb][i] = O[16 qb + 4 grp + i][16 db + ql].  O^T goes to the K/V
   // buffers: dims 0..63 in the K area, 64..127 in the V area, each dim a 256-byte row of
@@ -698,9 +797,11 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     lsum[qb] = group_sum(lsum[qb]);
-    if (grp == 0) lbuf[16 * qb + ql] = lsum[qb];
+    if (grp == 0) lbuf[64 * wv + 16 * qb + ql] = lsum[qb];
   }
   auto part = [&](int d) -> lds_u32x4* {
+    if (SH && wv > 0)
+      return (lds_u32x4*)((char*)lst_lds + (2 * (wv - 1) + (d < 64 ? 0 : 1)) * TILE_BYTES) + (d & 63) * 16;
     return (lds_u32x4*)(d < 64 ? klds : vlds) + (d & 63) * 16;
   };
 #pragma unroll
@@ -720,7 +821,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      qtok[w][i] = tile_token(g, qt, 16 * w + 4 * qg + i);
+      qtok[w][i] = qvalid ? tile_token(g, qt, 16 * w + 4 * qg + i) : -1;
       gv[w][i] = u32x4{0u, 0u, 0u, 0u};
       if (gated && qtok[w][i] >= 0)
         gv[w][i] = *reinterpret_cast<const u32x4*>(gate + row_offset(g, b, qtok[w][i], h) + 8 * dg);
@@ -744,7 +845,7 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (qtok[w][i] < 0) continue;
-      const float ltot = lbuf[q0 + i];
+      const float ltot = lbuf[64 * wv + q0 + i];
       const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty list gives O_fine = 0
       float y[8];
 #pragma unroll
@@ -771,9 +872,19 @@ __global__ __launch_bounds__(64) void vsa_fine_kernel(
 void vsa_launch_fine(const VsaGeom& g, const void* q, const void* k, const void* v, const void* gate,
                      const float* ocoarse, const int* lists, const int* counts, void* o,
                      const int* xtok, const void* vx, const int* xcnt, hipStream_t st) {
+  if (g.n_dense == g.Tq) {
+    // every row dense (the dense call): four query tiles of a (batch, head) per workgroup
+    const int groups = g.batch * g.heads * ((g.Tq + 3) / 4);
+    const int per_xcd = (groups + 7) / 8;
+    hipLaunchKernelGGL((vsa_fine_kernel<false, true>), dim3(8 * per_xcd), dim3(256), (size_t)6 * TILE_BYTES, st, g,
+                       (const char*)k,
+                       (const char*)v, (const u32x4*)q, (const unsigned short*)gate, ocoarse, lists, counts,
+                       (unsigned short*)o, per_xcd, xtok, (const char*)vx, xcnt);
+    return;
+  }
   const int total = g.batch * g.heads * g.Tq;
   const int per_xcd = (total + 7) / 8;
-  auto kern = g.extra > 0 ? vsa_fine_kernel<true> : vsa_fine_kernel<false>;
+  auto kern = g.extra > 0 ? vsa_fine_kernel<true, false> : vsa_fine_kernel<false, false>;
   hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(64), (size_t)g.cap * sizeof(int), st, g, (const char*)k,
                      (const char*)v, (const u32x4*)q, (const unsigned short*)gate, ocoarse, lists,
                      counts, (unsigned short*)o, per_xcd, xtok, (const char*)vx, xcnt);
