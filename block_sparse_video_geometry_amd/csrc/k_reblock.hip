@@ -25,7 +25,7 @@
 //   norm        |q|_M per video token with bf16 MFMAs against the hi/lo split of M (staged
 //               in LDS, 512 tokens per workgroup); the level-0 token list (tokens ascending)
 //   per level:  pass(first) finish  2 x [pass(power) finish]  pass(projection)  split
-//     pass      chunks of up to 2048 tokens of one node.  first: the sums of psi and of
+//     pass      chunks of up to 512 tokens of one node.  first: the sums of psi and of
 //               (psi.a0) psi (then C a0 = those / n - mu (mu.a0), since the centred psi sum
 //               to zero); power: the sums of (psi.a - mu.a)(psi - mu); projection: psi.a
 //     finish    per node: the chunk sums added in chunk order, then z, a = M z / |z|_M
@@ -270,9 +270,9 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
 // ---------------------------------------------------------------- per-level passes
 // MODE 0 (first power step): sums of psi and of (psi.a0) psi; 1 (later power steps): sums of
 // (psi.a - mu.a)(psi - mu); 2: projections psi.a to pbuf.  Workgroup (x, bh): node x / cpn,
-// positions [2048 c, 2048 c + 2048) of it (c = x % cpn).  16 lanes per token (8 dims each),
+// positions [512 c, 512 c + 512) of it (c = x % cpn).  16 lanes per token (8 dims each),
 // 16 tokens per step, eight steps' loads in flight.
-constexpr int RB_CH = 2048;
+constexpr int RB_CH = 512;
 constexpr int RB_PART = 2 * VSA_HEAD_DIM;  // floats per chunk partial
 constexpr int RB_FNB = 8;                   // most nodes per finish workgroup
 
