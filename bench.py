@@ -162,7 +162,7 @@ def cpu_baseline(w, x, max_workers, heads=None):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
