@@ -5,7 +5,8 @@
   Every replay must equal the eager forward on the same inputs, bit for bit (the kernels
   are deterministic).
 - The dense fallback (the plan's dense mode) must match the fp64 oracle's dense
-  attention (keep 100%, no gate), and so must a direct dense-mode forward.
+  attention (keep 100%, no gate), and so must a direct dense-mode forward, also at full size
+  on sampled query tiles.
 """
 import dataclasses
 
@@ -100,6 +101,48 @@ def test_dense_mode_matches_oracle(name):
     assert st["executed_pairs"] == st["dense_pairs"] == w.batch * w.heads * d.n_tiles ** 2
     assert st["sparse_rows"] == 0
     _check_dense(w, x, o)
+
+
+def test_dense_mode_full_size_sampled():
+    """The dense call at full size, in the launch configuration bench.py times (four query
+    tiles of a head per workgroup sharing each K/V tile): sampled query tiles of two heads,
+    prefix and video, against the oracle's dense attention over all 36,096 tokens."""
+    import zlib
+    import block_sparse_video_geometry_amd as V
+    from oracle import vsa_oracle as O
+    w = WORKLOADS["full"]
+    print(f"[gpu] dense mode on {w.name} (sampled rows)", flush=True)
+    x = make_inputs(w)
+    plan = V.vsa_plan_geometry(w.segments(), w.batch, *w.grid, w.heads, 128, 100.0,
+                               select=V.VSA_SELECT_DENSE)
+    q, k, v, g = (_dev(x[n]) for n in "qkvg")
+    o = torch.empty_like(q)
+    ws = V.alloc_workspace(plan)
+    V.vsa_forward(plan, q, k, v, g, o, ws)
+    torch.cuda.synchronize()
+    got_all = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    del q, k, v, g, o, ws
+    geom = O.map_geometry(w.segments(), *w.grid)
+    rng = np.random.default_rng(zlib.crc32(b"dense_full_sampled"))
+    heads = [0, int(rng.integers(1, w.heads))]
+    rows = sorted(set([0, geom.n_prefix - 1, geom.n_prefix, geom.n_tiles - 1] +
+                      [int(r) for r in rng.integers(0, geom.n_tiles, size=4)]))
+    max_abs, err2, ref2 = 0.0, 0.0, 0.0
+    for h in heads:
+        Q, K, Vh = (PAR.bits_to_f64(x[n][0, :, h]) for n in "qkv")
+        # keep 100% without a gate: every row attends to every valid token, no coarse term
+        ref, _ = O.forward_head(Q, K, Vh, None, geom, 100.0, w.sink, O.SELECT_TOPK, O.COARSE_MEAN, 0.0,
+                                rows=rows)
+        got = PAR.bits_to_f64(got_all[0, :, h])
+        for r in rows:
+            toks = np.asarray(geom.tiles[r])
+            d = got[toks] - ref[toks]
+            max_abs = max(max_abs, float(np.abs(d).max()))
+            err2 += float((d ** 2).sum())
+            ref2 += float((ref[toks] ** 2).sum())
+    rel = float(np.sqrt(err2 / ref2))
+    print(f"[dense-full] heads={heads} rows={rows}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= PAR.TOL_ABS and rel <= PAR.TOL_REL
 
 
 def test_driver_sparse_call_matches_forward():
