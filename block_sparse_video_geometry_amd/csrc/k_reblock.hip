@@ -270,7 +270,8 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
 // ---------------------------------------------------------------- per-level passes
 // MODE 0 (first power step): sums of psi and of (psi.a0) psi; 1 (later power steps): sums of
 // (psi.a - mu.a)(psi - mu); 2: projections psi.a to pbuf.  Workgroup (x, bh): node x / cpn,
-// positions [512 c, 512 c + 512) of it (c = x % cpn).  16 lanes per token (8 dims each),
+// positions [chunk c, chunk (c + 1)) of it (c = x % cpn; chunk = the level's largest node
+// split evenly into cpn whole tiles, at most RB_CH tokens).  16 lanes per token (8 dims each),
 // 16 tokens per step, eight steps' loads in flight.
 constexpr int RB_CH = 512;
 constexpr int RB_PART = 2 * VSA_HEAD_DIM;  // floats per chunk partial
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
                                                           const float* __restrict__ state,
                                                           const float* __restrict__ a0,
                                                           float* __restrict__ part, float* __restrict__ pbuf,
-                                                          int level, int cpn) {
+                                                          int level, int cpn, int chunk) {
   __shared__ float red[16][RB_PART];
   const int bh = blockIdx.y;
   const int b = bh / g.heads, h = bh - b * g.heads;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
   node_range(g.Vt, level, node, t0, m);
   const int Nv = VSA_TILE_TOKENS * g.Vt;
   const int n = VSA_TILE_TOKENS * m;
-  const int lo = c * RB_CH, hi = min(n, lo + RB_CH);
+  const int lo = c * chunk, hi = min(n, lo + chunk);
   const int tid = threadIdx.x, l16 = tid & 15, slot = tid >> 4;
   float* pp = part + ((size_t)bh * gridDim.x + blockIdx.x) * RB_PART;
   if (m < 2 || lo >= hi) {
@@ -652,6 +653,14 @@ int vsa_reblock_levels(int Vt) {
   return d;
 }
 
+// Tokens per pass workgroup at a level: the largest node's tiles split evenly over the
+// level's cpn chunks (at most RB_CH tokens each), so that no chunk is a small remainder.
+int vsa_reblock_chunk_tokens(int Vt, int level) {
+  const int maxm = (Vt + (1 << level) - 1) >> level;
+  const int cpn = vsa_reblock_chunks(Vt, level);
+  return VSA_TILE_TOKENS * ((maxm + cpn - 1) / cpn);
+}
+
 int vsa_reblock_chunks(int Vt, int level) {
   const int maxm = (Vt + (1 << level) - 1) >> level;
   return std::max(1, (VSA_TILE_TOKENS * maxm + RB_CH - 1) / RB_CH);
@@ -676,6 +685,7 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
   const int levels = vsa_reblock_levels(g.Vt);
   for (int L = 0; L < levels; ++L) {
     const int cpn = vsa_reblock_chunks(g.Vt, L);
+    const int chunk = vsa_reblock_chunk_tokens(g.Vt, L);
     const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH), fgrid(((1 << L) + RB_FNB - 1) / RB_FNB, BH);
     // finish: min(RB_FNB, nodes) nodes per workgroup
     auto finish = [&](int first) {
@@ -694,15 +704,15 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
     };
     // power step 1 (z from 1: the direction a0 is the head's), steps 2 .. RB_STEPS
     hipLaunchKernelGGL(vsa_rb_pass_kernel<0>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
-                       cpn);
+                       cpn, chunk);
     finish(1);
     for (int s = 1; s < RB_STEPS; ++s) {
       hipLaunchKernelGGL(vsa_rb_pass_kernel<1>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
-                         cpn);
+                         cpn, chunk);
       finish(0);
     }
     hipLaunchKernelGGL(vsa_rb_pass_kernel<2>, pgrid, dim3(256), 0, st, g, qs, norms, src, state, a0, part, pbuf, L,
-                       cpn);
+                       cpn, chunk);
     // the split's workgroup size: the level's largest node, rounded up to 256, 512 or 1024
     // tokens (the result does not depend on it)
     const int nmax = VSA_TILE_TOKENS * ((g.Vt + (1 << L) - 1) >> L);
