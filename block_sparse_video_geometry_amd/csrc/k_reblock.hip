@@ -93,7 +93,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 __global__ __launch_bounds__(256) void vsa_rb_moment_kernel(VsaGeom g, const unsigned short* __restrict__ k,
                                                             float* __restrict__ mpart, int nsplit) {
   __shared__ __attribute__((aligned(16))) unsigned short kt[128][40];  // 32 tokens + pad per dim
-  const int bh = blockIdx.y, s = blockIdx.x;
+  const int bh = blockIdx.x, s = blockIdx.y;  // (batch, head) fastest, as in the pass kernel
   const int b = bh / g.heads, h = bh - b * g.heads;
   const int j0 = (int)((long long)g.Vt * s / nsplit), j1 = (int)((long long)g.Vt * (s + 1) / nsplit);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
                                                           float* __restrict__ norms, int* __restrict__ list0) {
   __shared__ __attribute__((aligned(16))) unsigned short ms[2][VSA_HEAD_DIM][VSA_HEAD_DIM + 8];
   __shared__ __attribute__((aligned(16))) unsigned short qs[4][16][VSA_HEAD_DIM + 8];
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.x;  // (batch, head) fastest, as in the pass kernel
   const int b = bh / g.heads, h = bh - b * g.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, ql = lane & 15;
   const int Nv = VSA_TILE_TOKENS * g.Vt;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void vsa_rb_norm_kernel(VsaGeom g, const unsig
     *reinterpret_cast<u32x4*>(&ms[part][row][8 * c]) =
         *reinterpret_cast<const u32x4*>(Mh + (size_t)part * VSA_HEAD_DIM * VSA_HEAD_DIM + row * VSA_HEAD_DIM + 8 * c);
   }
-  const int base = RB_NORM_TOKENS * blockIdx.x;
+  const int base = RB_NORM_TOKENS * blockIdx.y;
   for (int i = tid; i < RB_NORM_TOKENS; i += 256)
     if (base + i < Nv) list0[(size_t)bh * Nv + base + i] = g.vstart + base + i;
   __syncthreads();
@@ -286,17 +286,21 @@ __global__ __launch_bounds__(256) void vsa_rb_pass_kernel(VsaGeom g, const unsig
                                                           float* __restrict__ part, float* __restrict__ pbuf,
                                                           int level, int cpn, int chunk) {
   __shared__ float red[16][RB_PART];
-  const int bh = blockIdx.y;
+  // (batch, head) runs fastest in the grid, so the workgroups in flight read the rows of one
+  // token range for every head (neighbouring 256-byte pieces of the same token rows) rather
+  // than one head's rows, 8 KB apart
+  const int bh = blockIdx.x, item = blockIdx.y;
   const int b = bh / g.heads, h = bh - b * g.heads;
-  const int node = blockIdx.x / cpn, c = blockIdx.x - node * cpn;
+  const int node = item / cpn, c = item - node * cpn;
   int t0, m;
   node_range(g.Vt, level, node, t0, m);
   const int Nv = VSA_TILE_TOKENS * g.Vt;
   const int n = VSA_TILE_TOKENS * m;
   const int lo = c * chunk, hi = min(n, lo + chunk);
   const int tid = threadIdx.x, l16 = tid & 15, slot = tid >> 4;
-  float* pp = part + ((size_t)bh * gridDim.x + blockIdx.x) * RB_PART;
-  if (m < 2 || lo >= hi) {
+  float* pp = part + ((size_t)bh * gridDim.y + item) * RB_PART;
+  if (m < 2) return;  // no split there: the finish kernel reads no partial of such a node
+  if (lo >= hi) {       // an empty chunk of a node that splits: its partial sums are zero
     if (MODE != 2)
       for (int i = tid; i < RB_PART; i += 256) pp[i] = 0.f;
     return;
@@ -437,10 +441,10 @@ __global__ __launch_bounds__(VSA_HEAD_DIM) void vsa_rb_finish_kernel(VsaGeom g, 
 #pragma unroll
   for (int i = 0; i < NB; ++i) zs[i][d] = z[i];
   __syncthreads();
-  const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
   float av[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) av[i] = 0.f;
+  const float* Mr = M + (size_t)bh * VSA_HEAD_DIM * VSA_HEAD_DIM + (size_t)d * VSA_HEAD_DIM;
 #pragma unroll 4
   for (int e = 0; e < VSA_HEAD_DIM; e += 4) {
     const f32x4 mr = *reinterpret_cast<const f32x4*>(Mr + e);
@@ -673,12 +677,12 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
   const int nsplit = g.rb_nsplit;
   const int Nv = VSA_TILE_TOKENS * g.Vt;
   const unsigned short* qs = (const unsigned short*)q;
-  hipLaunchKernelGGL(vsa_rb_moment_kernel, dim3(nsplit, BH), dim3(256), 0, st, g, (const unsigned short*)k, mpart,
+  hipLaunchKernelGGL(vsa_rb_moment_kernel, dim3(BH, nsplit), dim3(256), 0, st, g, (const unsigned short*)k, mpart,
                      nsplit);
   hipLaunchKernelGGL(vsa_rb_moment_reduce_kernel, dim3(VSA_HEAD_DIM * VSA_HEAD_DIM / 1024, BH), dim3(256), 0, st, g,
                      mpart, nsplit, M, mhl);
   hipLaunchKernelGGL(vsa_rb_a0_kernel, dim3(BH), dim3(VSA_HEAD_DIM), 0, st, (const float*)M, a0);
-  hipLaunchKernelGGL(vsa_rb_norm_kernel, dim3((Nv + RB_NORM_TOKENS - 1) / RB_NORM_TOKENS, BH), dim3(256), 0, st, g,
+  hipLaunchKernelGGL(vsa_rb_norm_kernel, dim3(BH, (Nv + RB_NORM_TOKENS - 1) / RB_NORM_TOKENS), dim3(256), 0, st, g,
                      qs, mhl, norms, list_a);
   int* src = list_a;
   int* dst = list_b;
@@ -686,7 +690,7 @@ const int* vsa_launch_reblock(const VsaGeom& g, const void* q, const void* k, fl
   for (int L = 0; L < levels; ++L) {
     const int cpn = vsa_reblock_chunks(g.Vt, L);
     const int chunk = vsa_reblock_chunk_tokens(g.Vt, L);
-    const dim3 pgrid((1 << L) * cpn, BH), ngrid(1 << L, BH), fgrid(((1 << L) + RB_FNB - 1) / RB_FNB, BH);
+    const dim3 pgrid(BH, (1 << L) * cpn), ngrid(1 << L, BH), fgrid(((1 << L) + RB_FNB - 1) / RB_FNB, BH);
     // finish: min(RB_FNB, nodes) nodes per workgroup
     auto finish = [&](int first) {
       if (L == 0)
