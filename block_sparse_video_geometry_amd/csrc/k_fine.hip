@@ -475,24 +475,37 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
 #pragma unroll
       for (int n = 0; n < 16; ++n) xdma(krs, koff[(n >> 1) & 3], n, kbuf_u);
     } else {
+      // K(0) into the (still idle) V buffer and K(1) into the K buffer, both in flight
+      // together: the first tile's product then reads the V buffer, and the loop finds K(1)
+      // in place without a second round trip
 #pragma unroll
-      for (int n = 0; n < 16; ++n) kdma_r(krs, n, c_off, stp, stl);
+      for (int n = 0; n < 16; ++n) dma(krs, koff[(n >> 1) & 3], n, c_off, stp, stl, vbuf_u);
+      unsigned n_stp, n_stl;
+      steps(n_flags, n_stp, n_stl);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
     }
   }
-  // Q, the epilogue's copies and K(0) landed.  A wait the compiler sees, on every path to
-  // the loop, so it does not wait (whole queue) for the Q loads again inside the loop.
+  // the plain path's K(0) sits in the V buffer (same layout): its reads are offset by this
+  const unsigned k0_shift = (!SH && !hx) ? vbuf_u - kbuf_u : 0u;
+  // Q, the epilogue's copies and K(0) (on the plain path K(1) too) landed.  A wait the compiler
+  // sees, on every path to the loop, so it does not wait (whole queue) for the Q loads again.
   __builtin_amdgcn_s_waitcnt(0);
   meet();  // SH: every wave's quarter of K(0) landed
   if (my_n > 0) {
     unsigned stp, stl;
     steps(c_flags, stp, stl);
     {
+      auto kread0 = [&](int s) -> bf16x8 {
+        const int kb = s >> 2;
+        return as_bf16x8(*(const lds_u32x4*)(size_t)(kbase[s & 3] + k0_shift + 256 * (32 * (kb >> 1) + 4 * (kb & 1))));
+      };
       f32x4 s0[4][4];
       bf16x8 ka[2];
-      ka[0] = kread(0);
+      ka[0] = kread0(0);
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        if (s < 15) ka[(s + 1) & 1] = kread(s + 1);
+        if (s < 15) ka[(s + 1) & 1] = kread0(s + 1);
         const int kb = s >> 2, ks = s & 3;
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb)
@@ -512,8 +525,9 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) scur[kb][qb][i] = acc_read(s0[kb][qb][i]);
     }
-    // K buffer is free once its reads returned: K(1) (zeros past the end of the list), then
-    // V(0) rows 0-31, as iteration 0 expects them in flight
+    // The buffer K(0) was read from is free once its reads returned: K(1) (zeros past the
+    // end of the list; on the plain path already in place), then V(0) rows 0-31, as
+    // iteration 0 expects them in flight
     wait_lgkm0();
     meet();  // SH: every wave has read K(0)
     unsigned n_stp, n_stl;
@@ -522,7 +536,7 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
       kdma_q(0, n_off, n_stp, n_stl);
       kdma_q(1, n_off, n_stp, n_stl);
       vdma_q(0, c_off, stp, stl);
-    } else {
+    } else if (hx) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
     }
