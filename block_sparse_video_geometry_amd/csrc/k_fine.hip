@@ -472,8 +472,13 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
       kdma_q(0, c_off, stp, stl);
       kdma_q(1, c_off, stp, stl);
     } else if (hx) {
+      // the extra tokens' K rows into the V buffer and K(1) into the K buffer, as below
 #pragma unroll
-      for (int n = 0; n < 16; ++n) xdma(krs, koff[(n >> 1) & 3], n, kbuf_u);
+      for (int n = 0; n < 16; ++n) xdma(krs, koff[(n >> 1) & 3], n, vbuf_u);
+      unsigned n_stp, n_stl;
+      steps(n_flags, n_stp, n_stl);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
     } else {
       // K(0) into the (still idle) V buffer and K(1) into the K buffer, both in flight
       // together: the first tile's product then reads the V buffer, and the loop finds K(1)
@@ -486,9 +491,9 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
       for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
     }
   }
-  // the plain path's K(0) sits in the V buffer (same layout): its reads are offset by this
-  const unsigned k0_shift = (!SH && !hx) ? vbuf_u - kbuf_u : 0u;
-  // Q, the epilogue's copies and K(0) (on the plain path K(1) too) landed.  A wait the compiler
+  // K(0) sits in the V buffer (same layout) except in the dense call: its reads are offset by this
+  const unsigned k0_shift = !SH ? vbuf_u - kbuf_u : 0u;
+  // Q, the epilogue's copies and K(0) (outside the dense call K(1) too) landed.  A wait the compiler
   // sees, on every path to the loop, so it does not wait (whole queue) for the Q loads again.
   __builtin_amdgcn_s_waitcnt(0);
   meet();  // SH: every wave's quarter of K(0) landed
@@ -526,7 +531,7 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
           for (int i = 0; i < 4; ++i) scur[kb][qb][i] = acc_read(s0[kb][qb][i]);
     }
     // The buffer K(0) was read from is free once its reads returned: K(1) (zeros past the
-    // end of the list; on the plain path already in place), then V(0) rows 0-31, as
+    // end of the list; outside the dense call already in place), then V(0) rows 0-31, as
     // iteration 0 expects them in flight
     wait_lgkm0();
     meet();  // SH: every wave has read K(0)
@@ -536,9 +541,6 @@ __global__ __launch_bounds__(SH ? 256 : 64) void vsa_fine_kernel(
       kdma_q(0, n_off, n_stp, n_stl);
       kdma_q(1, n_off, n_stp, n_stl);
       vdma_q(0, c_off, stp, stl);
-    } else if (hx) {
-#pragma unroll
-      for (int n = 0; n < 16; ++n) kdma(n, n_off, n_stp, n_stl);
     }
     if (SH) {
     } else if (hx) {
